@@ -1,0 +1,434 @@
+"""Plain CPU oracle for UltraEP's per-layer exact-load rebalancing path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code, table or helper with
+the HIP library; the two meet only through the seeded inputs of ``workload``.
+
+Every function is the slow, obvious definition of one step, written with
+NumPy primitives (bincount, stable argsort, fancy indexing, fp64 sums) and
+pure-Python loops over the small per-expert / per-rank state.
+
+Sources (web pages on UltraEP; cited by title and section):
+  [README]  "UltraEP" project README (mirror kd.iw.mk/studio-dots-ai/UltraEP)
+  [NEWS]    "Xiaohongshu's UltraEP Balances MoE Experts in 300 µs, Reaching
+            94.3% of Ideal" (news.hamidun.com, English)
+  [WEEKLY]  "UltraEP: Real-Time Load Balancing for Large-Scale MoE Training
+            and Inference" (aikit weekly article)
+
+Shapes and notation (readings where the pages are silent are marked R#; the
+full list is kept with the design notes):
+  R logical EP ranks, T tokens per rank (R1), token g = r*T + t, top-k
+  routing ``idx[R*T, k]``; pair n = g*k + j; N = R*T*k.
+  E experts, M = E/R masters per rank, expert e homed on rank e // M (R2).
+  S redundant slots per rank ([README] Interface / Initialization: the same
+  number of redundant-expert slots on every rank).  Domain size D: rank r is
+  in domain r // D (R3); replicas stay inside the domain ([README] principles,
+  "Topology-aware replication").
+  Load = number of (token, k) pairs (R4).
+  Physical experts P = R*(M+S), rank-major: p = r*(M+S) + j; j < M is the
+  master of expert r*M + j, j >= M is redundant slot j-M of rank r (R12).
+  Redundant slot id s = r*S + j-M.
+
+Parity: count, reroute, layout, permute and fold are pinned by closed forms
+and brute force in the tests.  The plan is pinned by invariants, special
+cases with closed-form answers, hand-worked examples, the pages' 1.01-1.04
+post-balance band and a brute-force optimum on tiny shapes; its tie-break
+rules are this build's own reading (the pages give no algorithm), so the
+exact choice among equally valid plans is parity unpinned by the pages.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# count
+# ---------------------------------------------------------------------------
+def count(topk_idx: np.ndarray, E: int) -> Tuple[np.ndarray, int]:
+    """Exact number of (token, k) pairs routed to each expert.
+
+    [WEEKLY] "Technical Details": each expert's load is computed from the
+    exact routing before the forward pass; [README] intro and Interface /
+    "Forward and backward": ``update_placement`` plans from the exact
+    post-gating routing map.  Ids outside [0, E) are dropped pairs (R13).
+    """
+    ids = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    valid = (ids >= 0) & (ids < E)
+    c = np.bincount(ids[valid], minlength=E).astype(np.int64)
+    return c, int(ids.size - valid.sum())
+
+
+# ---------------------------------------------------------------------------
+# plan
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass
+class Plan:
+    E: int
+    R: int
+    S: int
+    D: int
+    M: int
+    P: int
+    c: np.ndarray                 # [E] pairs per expert
+    total: int                    # valid pairs
+    dropped: int
+    rank_before: np.ndarray       # [R] home load H[r]
+    Q_lb: int
+    Q_max: int
+    tol: int
+    floor: int                    # max over domains of ceil(domain load / D)
+    grid_index: int
+    Q_star: int
+    slot_expert: np.ndarray       # [R*S] expert hosted in redundant slot, -1 empty
+    slot_quota: np.ndarray        # [R*S] pairs served by that slot
+    master_quota: np.ndarray      # [E]
+    phys_load: np.ndarray         # [P]
+    phys_off: np.ndarray          # [P+1] exclusive prefix of phys_load
+    inst_ptr: np.ndarray          # [E+1] CSR of each expert's instances
+    inst_phys: np.ndarray         # [E + R*S] physical id of each instance (ascending per expert)
+    inst_end: np.ndarray          # [E + R*S] cumulative ordinal end of each instance
+    rank_after: np.ndarray        # [R]
+
+    @property
+    def n_replicas(self) -> int:
+        return int((self.slot_expert >= 0).sum())
+
+    def instances(self, e: int) -> List[Tuple[int, int, int]]:
+        """(phys, start, end) ordinal ranges of expert e, in instance order."""
+        out, start = [], 0
+        for i in range(self.inst_ptr[e], self.inst_ptr[e + 1]):
+            out.append((int(self.inst_phys[i]), start, int(self.inst_end[i])))
+            start = int(self.inst_end[i])
+        return out
+
+    def imbalance_before(self) -> float:
+        return 1.0 if self.total == 0 else float(self.rank_before.max() * self.R / self.total)
+
+    def imbalance_after(self) -> float:
+        return 1.0 if self.total == 0 else float(self.rank_after.max() * self.R / self.total)
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def quota_grid(total: int, H: List[int], R: int, D: int, eps_num: int, eps_den: int):
+    """The quota values a plan may settle on, in the order they are tried.
+
+    [README] "Performance Tuning / Replication planning": the balancing ratio
+    is searched with an early-stop target of 1.0 and a numerical tolerance
+    eps (default 0.01).  Read as an integer grid (R6): start at the lowest
+    quota any placement could reach -- the mean rank load, or the mean rank
+    load of the most loaded domain, since replicas cannot leave their domain
+    ([README] principles, "Topology-aware replication"; R7) -- and step by
+    eps * mean until the no-replication load max H is reached; that last
+    quota is always feasible.  (The domain term is never below the global
+    mean, so it alone sets the start; the mean is kept for readability.)
+    """
+    Q_mean = _ceil_div(total, R)
+    floor = max(_ceil_div(sum(H[d * D:(d + 1) * D]), D) for d in range(R // D))
+    Q_lb = max(Q_mean, floor)
+    Q_max = max(H)
+    tol = max(1, (total * eps_num) // (R * eps_den))
+    grid = []
+    q = Q_lb
+    while q < Q_max:
+        grid.append(q)
+        q += tol
+    grid.append(Q_max)
+    return grid, Q_lb, Q_max, tol, floor
+
+
+def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
+             allow_zero_master: bool = False) -> Optional[Dict[int, List[Tuple[int, int]]]]:
+    """Try to bring every rank's load to at most Q with <= S replicas per rank.
+
+    Returns, per rank, the replicas it hosts as (expert, quota) in arrival
+    order (arrival index = redundant slot index), or None if this greedy
+    cannot reach Q.  The pages name a quota-driven scheduler ([NEWS] "How
+    balancing in 300 microseconds works") that replicates hot experts onto
+    idle devices and merges cold ones ([WEEKLY] "Technical Details") but give
+    no procedure; this greedy is this build's reading (R8-R10):
+
+    1. Shedding.  A rank above Q gives up its excess from its hottest experts
+       first (pairs desc, id asc).  A master keeps at least one pair unless
+       zero-quota masters are allowed ([README] "Replication planning").
+       Each shed amount is a queued piece; ``room[e]`` is how much more of e
+       its master could still give up.
+    2. Placement, per domain.  Receivers have ``spare = Q - load`` and S free
+       slots.  Repeatedly take the largest piece (ties: lower expert id):
+       a. if a receiver can take it whole, the tightest one does (smallest
+          spare, then lowest rank);
+       b. else, if some other shedding rank could host it, pick the largest
+          queued piece q whose home could (ties: lower id): first fill the
+          roomiest receiver, then swap the rest onto q's home rank, which
+          sheds that much more of q's expert (its load is unchanged);
+       c. else fill the roomiest receiver and queue the remainder;
+       d. else fail.
+       Every step fills one slot, so a domain takes at most D*S steps.
+    """
+    M = E // R
+    H = [sum(c[r * M:(r + 1) * M]) for r in range(R)]
+
+    def keep(e: int) -> int:
+        return 1 if (c[e] > 0 and not allow_zero_master) else 0
+
+    hosted: Dict[int, List[Tuple[int, int]]] = {r: [] for r in range(R)}
+    for d in range(R // D):
+        ranks = list(range(d * D, (d + 1) * D))
+        piece: Dict[int, int] = {}
+        room: Dict[int, int] = {}
+        for r in ranks:
+            X = H[r] - Q
+            if X <= 0:
+                continue
+            for e in sorted(range(r * M, (r + 1) * M), key=lambda f: (-c[f], f)):
+                t = min(X, c[e] - keep(e))
+                if t > 0:
+                    piece[e] = t
+                    room[e] = c[e] - keep(e) - t
+                    X -= t
+            if X > 0:
+                return None
+        spare = {r: max(0, Q - H[r]) for r in ranks}
+        free = {r: S for r in ranks}
+
+        def place(e: int, r: int, x: int) -> None:
+            assert x > 0 and free[r] > 0
+            hosted[r].append((e, x))
+            free[r] -= 1
+
+        while piece:
+            e = max(piece, key=lambda f: (piece[f], -f))
+            a = piece.pop(e)
+            home = e // M
+
+            def elig(r: int) -> bool:
+                return r != home and free[r] > 0 and all(x != e for x, _ in hosted[r])
+
+            rec = [r for r in ranks if elig(r) and spare[r] > 0]
+            fit = [r for r in rec if spare[r] >= a]
+            if fit:
+                r = min(fit, key=lambda q: (spare[q], q))
+                place(e, r, a)
+                spare[r] -= a
+                continue
+            don = [f for f in piece if elig(f // M) and room[f] > 0]
+            if don:
+                f = max(don, key=lambda g: (piece[g], -g))
+                if rec:
+                    r2 = max(rec, key=lambda q: (spare[q], -q))
+                    assert r2 != f // M
+                    x = spare[r2]
+                    place(e, r2, x)
+                    spare[r2] = 0
+                    a -= x
+                x = min(a, room[f])
+                place(e, f // M, x)
+                piece[f] += x
+                room[f] -= x
+                a -= x
+                if a > 0:
+                    piece[e] = a
+            elif rec:
+                r = max(rec, key=lambda q: (spare[q], -q))
+                x = spare[r]
+                place(e, r, x)
+                spare[r] = 0
+                piece[e] = a - x
+            else:
+                return None
+    return hosted
+
+
+def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
+         eps_num: int = 1, eps_den: int = 100, allow_zero_master: bool = False) -> Plan:
+    """Replication plan from the exact per-expert load ([README] Interface /
+    "Forward and backward": ``update_placement``).
+
+    Q* is the first grid quota (see ``quota_grid``) that ``feasible`` reaches.
+    Each expert's instances are its master and its replicas, ordered by
+    ascending physical id (R10); instance i serves the ordinals
+    [start_i, start_i + quota_i) of that expert's pairs, cumulatively.
+    """
+    if E % R or R % D or S < 0:
+        raise ValueError("bad shape")
+    M = E // R
+    P = R * (M + S)
+    c = [int(x) for x in c]
+    total = sum(c)
+    H = [sum(c[r * M:(r + 1) * M]) for r in range(R)]
+    grid, Q_lb, Q_max, tol, floor = quota_grid(total, H, R, D, eps_num, eps_den)
+    for gi, Q in enumerate(grid):
+        hosted = feasible(c, Q, E, R, S, D, allow_zero_master)
+        if hosted is not None:
+            break
+    assert hosted is not None, "no replication at Q_max must always be feasible"
+
+    slot_expert = np.full(R * S, -1, dtype=np.int64)
+    slot_quota = np.zeros(R * S, dtype=np.int64)
+    for r in range(R):
+        for s, (e, x) in enumerate(hosted[r]):
+            slot_expert[r * S + s] = e
+            slot_quota[r * S + s] = x
+    master_quota = np.array(c, dtype=np.int64)
+    for s in range(R * S):
+        if slot_expert[s] >= 0:
+            master_quota[slot_expert[s]] -= slot_quota[s]
+
+    phys_load = np.zeros(P, dtype=np.int64)
+    for r in range(R):
+        for j in range(M):
+            phys_load[r * (M + S) + j] = master_quota[r * M + j]
+        for j in range(S):
+            phys_load[r * (M + S) + M + j] = slot_quota[r * S + j]
+    phys_off = np.zeros(P + 1, dtype=np.int64)
+    phys_off[1:] = np.cumsum(phys_load)
+
+    inst_ptr = [0]
+    inst_phys: List[int] = []
+    inst_end: List[int] = []
+    for e in range(E):
+        home = e // M
+        phys = [home * (M + S) + (e % M)]
+        for s in range(R * S):
+            if slot_expert[s] == e:
+                r, j = divmod(s, S)
+                phys.append(r * (M + S) + M + j)
+        end = 0
+        for p in sorted(phys):
+            end += int(phys_load[p])
+            inst_phys.append(p)
+            inst_end.append(end)
+        assert end == c[e]
+        inst_ptr.append(len(inst_phys))
+
+    rank_after = phys_load.reshape(R, M + S).sum(axis=1)
+    return Plan(E=E, R=R, S=S, D=D, M=M, P=P, c=np.array(c, dtype=np.int64), total=total,
+                dropped=int(dropped), rank_before=np.array(H, dtype=np.int64), Q_lb=Q_lb,
+                Q_max=Q_max, tol=tol, floor=floor, grid_index=gi, Q_star=grid[gi],
+                slot_expert=slot_expert, slot_quota=slot_quota, master_quota=master_quota,
+                phys_load=phys_load, phys_off=phys_off,
+                inst_ptr=np.array(inst_ptr, dtype=np.int64),
+                inst_phys=np.array(inst_phys, dtype=np.int64),
+                inst_end=np.array(inst_end, dtype=np.int64), rank_after=rank_after)
+
+
+# ---------------------------------------------------------------------------
+# reroute + dispatch layout
+# ---------------------------------------------------------------------------
+def ordinals(topk_idx: np.ndarray, E: int) -> np.ndarray:
+    """o[n] = number of pairs n' < n routed to the same expert (-1 if dropped).
+
+    Read off a stable sort by expert id: within one expert's run the pairs
+    keep their order, so a pair's place in the run is its ordinal.
+    """
+    ids = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    valid = (ids >= 0) & (ids < E)
+    key = np.where(valid, ids, E)
+    order = np.argsort(key, kind="stable")
+    run_start = np.searchsorted(key[order], key[order], side="left")
+    o = np.empty(ids.size, dtype=np.int64)
+    o[order] = np.arange(ids.size) - run_start
+    o[~valid] = -1
+    return o
+
+
+def reroute(topk_idx: np.ndarray, pl: Plan) -> Tuple[np.ndarray, np.ndarray]:
+    """Physical expert and dispatch row of every pair.
+
+    [README] Interface / "Forward and backward": ``reroute`` expands the
+    logical routing to physical replicas.  Pair n of expert e with ordinal o
+    goes to the instance whose range holds o (R11); its row in the
+    replica-contiguous layout is ``phys_off[p] + o - start``.  Dropped pairs
+    get -1 in both.
+    """
+    ids = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    o = ordinals(ids, pl.E)
+    valid = o >= 0
+    # Lay every expert's ordinal range end to end (experts ascending, each
+    # expert's instances in instance order); the instance holding a pair is
+    # then the first whose cumulative end lies beyond the pair's place.
+    expert_base = np.concatenate([[0], np.cumsum(pl.c)])
+    inst_expert = np.repeat(np.arange(pl.E), np.diff(pl.inst_ptr))
+    inst_gend = expert_base[inst_expert] + pl.inst_end
+    inst_start = pl.inst_end - pl.phys_load[pl.inst_phys]
+    e = ids[valid]
+    i = np.searchsorted(inst_gend, expert_base[e] + o[valid], side="right")
+    phys = np.full(ids.size, -1, dtype=np.int64)
+    pos = np.full(ids.size, -1, dtype=np.int64)
+    phys[valid] = pl.inst_phys[i]
+    pos[valid] = pl.phys_off[pl.inst_phys[i]] + o[valid] - inst_start[i]
+    return phys, pos
+
+
+def layout(pos: np.ndarray, topk_w: np.ndarray, total: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Inverse index and permuted weights of the dispatch layout.
+
+    inv[pos[n]] = n and w_perm[pos[n]] = w[n] for every valid pair; the
+    layout holds ``total`` rows.
+    """
+    pos = np.asarray(pos).reshape(-1)
+    w = np.asarray(topk_w, dtype=np.float32).reshape(-1)
+    inv = np.full(total, -1, dtype=np.int64)
+    w_perm = np.zeros(total, dtype=np.float32)
+    n = np.nonzero(pos >= 0)[0]
+    inv[pos[n]] = n
+    w_perm[pos[n]] = w[n]
+    return inv, w_perm
+
+
+# ---------------------------------------------------------------------------
+# permute
+# ---------------------------------------------------------------------------
+def permute(hidden_bits: np.ndarray, inv: np.ndarray, k: int, pl: Plan,
+            p_begin: int, p_end: int) -> np.ndarray:
+    """bf16 rows of the physical experts [p_begin, p_end), in layout order.
+
+    Row i of the segment is the hidden row of the token that owns pair
+    inv[phys_off[p_begin] + i].  Rows are moved as raw 16-bit patterns.
+    """
+    lo, hi = int(pl.phys_off[p_begin]), int(pl.phys_off[p_end])
+    return np.asarray(hidden_bits)[np.asarray(inv)[lo:hi] // k]
+
+
+# ---------------------------------------------------------------------------
+# fold
+# ---------------------------------------------------------------------------
+def fold(master: Dict[int, np.ndarray], replica_grads: np.ndarray, pl: Plan,
+         slot_begin: int, slot_end: int) -> Dict[int, np.ndarray]:
+    """Fold replica gradients back into their masters.
+
+    [README] Interface / "Forward and backward": ``grad_reduce`` reduces
+    replica weight gradients into the master experts' gradients;
+    "Performance Tuning / Expert communication": deterministic, non-atomic
+    reduction by default.  For each expert with a replica among the slots
+    [slot_begin, slot_end): master + the sum of those replicas, in fp64,
+    rounded once to fp32.  ``replica_grads[s - slot_begin]`` is slot s.
+    Returns the new master buffers of the touched experts.
+    """
+    out: Dict[int, np.ndarray] = {}
+    for e in range(pl.E):
+        slots = [s for s in range(slot_begin, slot_end) if pl.slot_expert[s] == e]
+        if not slots:
+            continue
+        acc = np.asarray(master[e], dtype=np.float64).copy()
+        for s in slots:
+            acc += np.asarray(replica_grads[s - slot_begin], dtype=np.float64)
+        out[e] = acc.astype(np.float32)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# the whole path for one layer
+# ---------------------------------------------------------------------------
+def balance(topk_idx: np.ndarray, E: int, R: int, S: int, D: int, **opts):
+    """count -> plan -> reroute for one layer; returns (plan, phys, pos)."""
+    c, dropped = count(topk_idx, E)
+    pl = plan(c, E, R, S, D, dropped=dropped, **opts)
+    phys, pos = reroute(topk_idx, pl)
+    return pl, phys, pos

@@ -1,0 +1,103 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case edits one line of a copy of the oracle's source (a dropped term, a
+flipped tie-break, an off-by-one, a wrong operand), loads the copy as a
+module, swaps it in for ``oracle`` and runs a fast subset of the pins.  The
+test passes only if at least one pin fails on the broken copy.
+"""
+import inspect
+import sys
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.ultraep_oracle as base
+import test_oracle_pins as P
+
+MUTATIONS = [
+    ("count keeps id E", "valid = (ids >= 0) & (ids < E)\n    c = np.bincount",
+     "valid = (ids >= 0) & (ids <= E)\n    c = np.bincount"),
+    ("ordinal off by one", 'run_start = np.searchsorted(key[order], key[order], side="left")',
+     'run_start = np.searchsorted(key[order], key[order], side="right")'),
+    ("no domain floor", "Q_lb = max(Q_mean, floor)", "Q_lb = Q_mean"),
+    ("tolerance not per rank", "tol = max(1, (total * eps_num) // (R * eps_den))",
+     "tol = max(1, (total * eps_num) // eps_den)"),
+    ("shed coldest first", "key=lambda f: (-c[f], f)", "key=lambda f: (c[f], f)"),
+    ("keep nothing", "return 1 if (c[e] > 0 and not allow_zero_master) else 0",
+     "return 0 if (c[e] > 0 and not allow_zero_master) else 0"),
+    ("piece tie by higher id", "e = max(piece, key=lambda f: (piece[f], -f))",
+     "e = max(piece, key=lambda f: (piece[f], f))"),
+    ("loosest fit", "r = min(fit, key=lambda q: (spare[q], q))", "r = min(fit, key=lambda q: (-spare[q], q))"),
+    ("roomiest tie by higher rank", "r = max(rec, key=lambda q: (spare[q], -q))",
+     "r = max(rec, key=lambda q: (spare[q], q))"),
+    ("chain does not grow the donor piece", "piece[f] += x", "piece[f] += 0"),
+    ("no chain branch", "if don:", "if False:"),
+    ("replica may sit on its home", "return r != home and free[r] > 0", "return free[r] > 0"),
+    ("instances in creation order", "for p in sorted(phys):", "for p in phys:"),
+    ("offset not prefix", "phys_off[1:] = np.cumsum(phys_load)", "phys_off[1:] = phys_load"),
+    ("instance lookup left", 'i = np.searchsorted(inst_gend, expert_base[e] + o[valid], side="right")',
+     'i = np.searchsorted(inst_gend, expert_base[e] + o[valid], side="left")'),
+    ("layout weight of row", "    w_perm[pos[n]] = w[n]\n    return inv, w_perm",
+     "    w_perm[pos[n]] = w[pos[n]]\n    return inv, w_perm"),
+    ("permute token from slot", "[np.asarray(inv)[lo:hi] // k]", "[np.asarray(inv)[lo:hi] % k]"),
+    ("permute segment shifted", "lo, hi = int(pl.phys_off[p_begin]), int(pl.phys_off[p_end])",
+     "lo, hi = int(pl.phys_off[p_begin]), int(pl.phys_off[p_end - 1])"),
+    ("fold in fp32", "acc = np.asarray(master[e], dtype=np.float64).copy()",
+     "acc = np.asarray(master[e], dtype=np.float32).copy()"),
+    ("fold drops range end", "for s in range(slot_begin, slot_end) if", "for s in range(slot_begin, slot_end - 1) if"),
+]
+
+PIN_SUBSET = [
+    (P.test_count_hand_example, {}),
+    (P.test_count_brute_force_with_invalid_ids, {"seed": 0}),
+    (P.test_ordinals_brute_force, {"seed": 1}),
+    (P.test_plan_hand_layout_example, {}),
+    *[(P.test_plan_hand_worked, {"case": c}) for c in P.HAND],
+    (P.test_plan_single_hot_expert_wraps, {"N": 77, "R": 5, "M": 3, "S": 1}),
+    (P.test_plan_two_ranks_closed_form, {"seed": 1}),
+    (P.test_plan_uniform_home_load, {}),
+    (P.test_plan_no_replication_possible, {"seed": 0, "S": 0, "D": 4}),
+    (P.test_plan_invariants_random_shapes, {"seed": 3}),
+    (P.test_layout_properties_workloads, {"cfg": 1, "layer": 0}),
+    (P.test_layout_properties_random_with_dropped, {"seed": 2}),
+    (P.test_layout_without_replication_is_stable_sort_by_expert, {}),
+    (P.test_permute_brute_force, {"seed": 0}),
+    (P.test_fold_exact_integers_and_untouched, {}),
+    (P.test_fold_rounds_once_from_fp64, {}),
+    (P.test_plan_against_brute_force_optimum_tiny, {"seed": 0}),
+    (P.test_topology_floor_is_reached, {}),
+]
+
+
+def _mutant(old, new):
+    src = inspect.getsource(base)
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    sys.modules["oracle_mutant"] = mod       # dataclasses look their module up
+    try:
+        exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    finally:
+        del sys.modules["oracle_mutant"]
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, old, new, monkeypatch):
+    mod = _mutant(old, new)
+    for attr in oracle.__dict__:
+        if not attr.startswith("_") and hasattr(mod, attr):
+            monkeypatch.setattr(P.O, attr, getattr(mod, attr))
+    failed = []
+    for fn, kw in PIN_SUBSET:
+        try:
+            fn(**kw)
+        except (AssertionError, IndexError, ValueError, KeyError, TypeError):
+            failed.append(fn.__name__)
+    assert failed, f"no pin caught the planted mistake: {name}"
+
+
+def test_unmutated_oracle_passes_subset():
+    for fn, kw in PIN_SUBSET:
+        fn(**kw)

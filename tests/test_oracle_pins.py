@@ -1,0 +1,376 @@
+"""Pins of the CPU oracle (no GPU).
+
+Each test checks the oracle against something other than itself: values
+worked out by hand (tests/golden), brute force written as plain loops,
+closed-form special cases, invariants, and the pages' printed numbers.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workload as W
+from pins import (brute_counts, brute_optimum, brute_ordinals, brute_segment_tokens,
+                  check_layout, check_plan_invariants, hall_min_quota, load_golden)
+
+
+# ---------------------------------------------------------------- count ----
+def test_count_hand_example():
+    g = load_golden("hand_layout.json")
+    c, dropped = O.count(np.array(g["topk_idx"], dtype=np.int32), g["E"])
+    assert c.tolist() == g["counts"] and dropped == g["dropped"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_count_brute_force_with_invalid_ids(seed):
+    rng = np.random.default_rng(seed)
+    E = int(rng.integers(1, 40))
+    ids = W.random_ids(rng, E, int(rng.integers(0, 600)), invalid_frac=0.2)
+    c, dropped = O.count(ids, E)
+    bc, bd = brute_counts(ids, E)
+    assert c.tolist() == bc and dropped == bd
+    assert c.sum() + dropped == ids.size
+
+
+# ------------------------------------------------------------- ordinals ----
+@pytest.mark.parametrize("seed", range(6))
+def test_ordinals_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(1, 20))
+    ids = W.random_ids(rng, E, int(rng.integers(0, 500)), invalid_frac=0.1)
+    assert O.ordinals(ids, E).tolist() == brute_ordinals(ids, E)
+
+
+# ----------------------------------------------------------------- plan ----
+HAND = load_golden("hand_plans.json")["cases"]
+
+
+@pytest.mark.parametrize("case", HAND, ids=[c["name"] for c in HAND])
+def test_plan_hand_worked(case):
+    pl = O.plan(np.array(case["c"]), case["E"], case["R"], case["S"], case["D"],
+                allow_zero_master=case.get("allow_zero_master", False))
+    assert pl.Q_star == case["Q_star"] and pl.grid_index == case["grid_index"]
+    for key in ("slot_expert", "slot_quota", "master_quota", "phys_load", "phys_off",
+                "inst_ptr", "inst_phys", "inst_end", "rank_after"):
+        if key in case:
+            assert getattr(pl, key).tolist() == case[key], key
+    check_plan_invariants(pl, case["c"], case.get("allow_zero_master", False))
+
+
+def test_plan_hand_layout_example():
+    g = load_golden("hand_layout.json")
+    idx = np.array(g["topk_idx"], dtype=np.int32)
+    pl, phys, pos = O.balance(idx, g["E"], g["R"], g["S"], g["D"])
+    assert pl.Q_star == g["Q_star"]
+    assert pl.slot_expert.tolist() == g["slot_expert"]
+    assert pl.slot_quota.tolist() == g["slot_quota"]
+    assert pl.phys_load.tolist() == g["phys_load"]
+    assert pl.phys_off.tolist() == g["phys_off"]
+    assert O.ordinals(idx, g["E"]).tolist() == g["ordinal"]
+    assert phys.tolist() == g["phys_idx"] and pos.tolist() == g["pos"]
+    inv, wp = O.layout(pos, np.array(g["topk_w"], dtype=np.float32), pl.total)
+    assert inv.tolist() == g["inv"]
+    assert np.array_equal(wp, np.array(g["w_perm"], dtype=np.float32))
+    hidden = np.arange(4 * 3, dtype=np.uint16).reshape(4, 3)
+    rows = O.permute(hidden, inv, g["k"], pl, 3, 6)
+    assert np.array_equal(rows, hidden[g["rank1_segment_tokens"]])
+    f = g["fold"]
+    masters = {1: np.array(f["master_e1"], dtype=np.float32)}
+    reps = np.array([f["replica_slot0"], f["replica_slot1"]], dtype=np.float32)
+    out = O.fold(masters, reps, pl, f["slot_begin"], f["slot_end"])
+    assert list(out) == [1] and out[1].tolist() == f["expected_e1"]
+
+
+def _plan_of(c, E, R, S, D, **kw):
+    pl = O.plan(np.asarray(c), E, R, S, D, **kw)
+    check_plan_invariants(pl, c, kw.get("allow_zero_master", False))
+    return pl
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("S,D", [(0, 4), (2, 1)])
+def test_plan_no_replication_possible(seed, S, D):
+    """S = 0 or D = 1: nothing can move, so Q* = max home load, no replicas."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 50, size=8)
+    pl = _plan_of(c, 8, 4, S, D)
+    assert pl.n_replicas == 0 and pl.Q_star == pl.Q_max
+    assert np.array_equal(pl.rank_after, pl.rank_before)
+
+
+def test_plan_uniform_home_load():
+    c = np.array([3, 7, 5, 5, 9, 1, 0, 10])   # every rank holds 10
+    pl = _plan_of(c, 8, 4, 2, 4)
+    assert pl.n_replicas == 0 and pl.Q_star == 10 and pl.grid_index == 0
+
+
+def test_plan_empty_layer():
+    pl = _plan_of(np.zeros(8, dtype=int), 8, 4, 1, 4)
+    assert pl.total == 0 and pl.n_replicas == 0 and pl.Q_star == 0
+    assert pl.imbalance_after() == 1.0
+
+
+@pytest.mark.parametrize("N,R,M,S", [(1000, 4, 2, 1), (4096, 8, 1, 2), (77, 5, 3, 1), (10, 4, 1, 1)])
+def test_plan_single_hot_expert_wraps(N, R, M, S):
+    """All pairs on expert 0, one domain: the load wraps over ranks 1, 2, ...
+    in order, each taking the full quota ceil(N/R) except the last
+    (McNaughton's wrap-around rule)."""
+    E = R * M
+    c = np.zeros(E, dtype=int)
+    c[0] = N
+    pl = _plan_of(c, E, R, S, R)
+    Q = math.ceil(N / R)
+    assert pl.Q_star == Q
+    left = N - Q
+    for r in range(1, R):
+        take = min(Q, left)
+        if take == 0:
+            assert pl.slot_expert[r * S] == -1
+            continue
+        assert pl.slot_expert[r * S] == 0 and pl.slot_quota[r * S] == take
+        left -= take
+    assert left == 0 and pl.master_quota[0] == Q
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_plan_two_ranks_closed_form(seed):
+    """R = 2, one expert per rank: the hot expert sends exactly H_hot - ceil(N/2)."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 1000, size=2)
+    pl = _plan_of(c, 2, 2, 1, 2)
+    hot = int(np.argmax(c)) if c[0] != c[1] else 0
+    send = int(c.max()) - math.ceil(int(c.sum()) / 2)
+    if send <= 0:
+        assert pl.n_replicas == 0
+    else:
+        assert pl.slot_expert.tolist()[1 - hot] == hot
+        assert pl.slot_quota[1 - hot] == send
+        assert pl.Q_star == math.ceil(int(c.sum()) / 2)
+
+
+def test_hall_bound_without_replicas_is_max_home_load():
+    c = [5, 1, 4, 4, 0, 2]
+    hosts = [1 << (e // 2) for e in range(6)]
+    assert hall_min_quota(c, hosts, 3) == 8
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_against_brute_force_optimum_tiny(seed):
+    """Tiny shape (E=8, R=4, S=1, D=4): no valid plan beats the brute-force
+    optimum, and the greedy stays within 0.04 of it in max/mean units."""
+    w = W.TINY
+    idx, _, _ = W.routing(w, layer=seed)
+    c, _ = O.count(idx, w.E)
+    pl = _plan_of(c, w.E, w.R, w.S, w.D)
+    opt = brute_optimum(c.tolist(), w.E, w.R, w.S, w.D)
+    mean = pl.total / w.R
+    assert pl.rank_after.max() >= opt
+    assert (pl.rank_after.max() - opt) / mean <= 0.04
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_plan_invariants_random_shapes(seed):
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([1, 2, 4, 8]))
+    R = D * int(rng.integers(1, 4))
+    M = int(rng.integers(1, 5))
+    S = int(rng.integers(0, 4))
+    E = R * M
+    alpha = float(rng.choice([0.05, 0.3, 1.0]))
+    c = rng.multinomial(int(rng.integers(0, 20000)), rng.dirichlet(np.full(E, alpha)))
+    _plan_of(c, E, R, S, D, allow_zero_master=bool(rng.integers(0, 2)))
+
+
+def test_plan_first_feasible_grid_point():
+    """Q* is the first quota on the grid the greedy reaches; every earlier
+    grid point is out of its reach."""
+    w = W.SINGLE
+    idx, _, _ = W.routing(w)
+    c, _ = O.count(idx, w.E)
+    pl = O.plan(c, w.E, w.R, w.S, w.D)
+    for g in range(pl.grid_index):
+        assert O.feasible(c.tolist(), pl.Q_lb + g * pl.tol, w.E, w.R, w.S, w.D) is None
+    assert pl.Q_star == min(pl.Q_lb + pl.grid_index * pl.tol, pl.Q_max)
+
+
+# ------------------------------------------------------- pages' numbers ----
+def _band_check(w, layer=0, mb=0):
+    idx, _, _ = W.routing(w, layer, mb)
+    c, _ = O.count(idx, w.E)
+    pl = _plan_of(c, w.E, w.R, w.S, w.D)
+    band = load_golden("pages_ep64_table.json")["band_after_balance"]
+    assert pl.imbalance_after() <= band[1], (w.cfg_id, layer, mb, pl.imbalance_after())
+    return pl
+
+
+@pytest.mark.parametrize("layer", range(8))
+def test_band_tiny(layer):
+    _band_check(W.TINY, layer)
+
+
+def test_band_single_layer():
+    _band_check(W.SINGLE)
+
+
+@pytest.mark.parametrize("layer", [0, 17, 42, 60])
+def test_band_deep_layers(layer):
+    _band_check(W.DEEP, layer)
+
+
+@pytest.mark.parametrize("mb", [0, 3, 11, 15])
+def test_band_stream(mb):
+    _band_check(W.STREAM, layer=mb % 32, mb=mb)
+
+
+def test_topology_floor_is_reached():
+    """With replication confined to domains of 8 ranks the best possible
+    max/mean is the hottest domain's mean over the global mean; the plan
+    lands on it (the pages: a floor slightly above 1.0 when the scale-up
+    domain is smaller than the EP group)."""
+    w = W.TOPO
+    idx, _, _ = W.routing(w)
+    c, _ = O.count(idx, w.E)
+    pl = _plan_of(c, w.E, w.R, w.S, w.D)
+    floor = pl.floor * w.R / pl.total
+    assert floor > 1.0
+    assert pl.imbalance_after() <= floor + 0.01
+
+
+def _zipf_counts_at(target, E, R, N, rng):
+    """Expert loads from a Zipf law whose exponent is tuned so that the
+    expected max/mean home-rank load hits ``target``."""
+    perm = rng.permutation(E)
+
+    def ratio(s):
+        p = np.arange(1, E + 1, dtype=float) ** (-s)
+        q = np.empty(E)
+        q[perm] = p / p.sum()
+        H = q.reshape(R, -1).sum(axis=1)
+        return H.max() * R, q
+
+    lo, hi = 0.0, 4.0
+    for _ in range(60):
+        mid = (lo + hi) / 2
+        if ratio(mid)[0] < target:
+            lo = mid
+        else:
+            hi = mid
+    return rng.multinomial(N, ratio(lo)[1])
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+def test_pages_ep64_table_shape(which):
+    """The pages' EP64 table: 256 experts, 4 masters + 2 redundant slots per
+    rank, top-8, 8k tokens per rank, initial max/mean 1.51 / 2.01 / 3.03,
+    final 1.01 at eps = 0.01.  Synthesized Zipf loads at those ratios must
+    land inside the pages' 1.01-1.04 post-balance band."""
+    g = load_golden("pages_ep64_table.json")
+    sh = g["shape"]
+    rng = np.random.default_rng([77, which])
+    N = sh["R"] * sh["tokens_per_rank"] * sh["k"]
+    c = _zipf_counts_at(g["initial_imbalance"][which], sh["E"], sh["R"], N, rng)
+    pl = _plan_of(c, sh["E"], sh["R"], sh["S"], sh["D"])
+    assert abs(pl.imbalance_before() - g["initial_imbalance"][which]) < 0.05
+    assert pl.imbalance_after() <= g["band_after_balance"][1]
+    assert pl.imbalance_after() <= g["final_imbalance"][which] + 0.005
+
+
+# ------------------------------------------------ reroute / layout --------
+@pytest.mark.parametrize("cfg,layer", [(1, 0), (1, 1), (1, 2)])
+def test_layout_properties_workloads(cfg, layer):
+    w = W.CONFIGS[cfg]
+    idx, wt, _ = W.routing(w, layer)
+    pl, phys, pos = O.balance(idx, w.E, w.R, w.S, w.D)
+    inv, wp = O.layout(pos, wt, pl.total)
+    check_layout(idx, wt, pl, phys, pos, inv, wp, w.E, w.k)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_layout_properties_random_with_dropped(seed):
+    rng = np.random.default_rng(500 + seed)
+    R, M, S, D, k = 4, int(rng.integers(1, 4)), int(rng.integers(0, 3)), int(rng.choice([1, 2, 4])), 3
+    E = R * M
+    T = int(rng.integers(0, 40))
+    idx = W.random_ids(rng, E, R * T * k, invalid_frac=0.1).reshape(-1, k) if T else np.zeros((0, k), np.int32)
+    wt = rng.random(idx.shape).astype(np.float32)
+    pl, phys, pos = O.balance(idx, E, R, S, D)
+    inv, wp = O.layout(pos, wt, pl.total)
+    check_layout(idx, wt, pl, phys, pos, inv, wp, E, k)
+
+
+def test_layout_without_replication_is_stable_sort_by_expert():
+    """S = 0: every pair stays on its master, and the layout is the stable
+    sort of pairs by expert id."""
+    rng = np.random.default_rng(3)
+    E, R, k = 12, 4, 2
+    idx = rng.integers(0, E, size=(50, k)).astype(np.int32)
+    pl, phys, pos = O.balance(idx, E, R, 0, 4)
+    flat = idx.reshape(-1)
+    assert np.array_equal(phys, flat)               # with S = 0, p == e
+    inv, _ = O.layout(pos, np.zeros(idx.shape, np.float32), pl.total)
+    assert np.array_equal(inv, np.argsort(flat, kind="stable"))
+
+
+# -------------------------------------------------------------- permute ----
+@pytest.mark.parametrize("seed", range(4))
+def test_permute_brute_force(seed):
+    w = W.TINY
+    idx, wt, _ = W.routing(w, layer=seed)
+    pl, phys, pos = O.balance(idx, w.E, w.R, w.S, w.D)
+    inv, _ = O.layout(pos, wt, pl.total)
+    hid = W.random_bits_hidden(w.tokens, 8, seed)
+    P1 = w.M + w.S
+    for r in range(w.R):
+        rows = O.permute(hid, inv, w.k, pl, r * P1, (r + 1) * P1)
+        toks = brute_segment_tokens(phys, w.k, r * P1, (r + 1) * P1)
+        assert np.array_equal(rows.view(np.uint16), hid[toks])
+    whole = O.permute(hid, inv, w.k, pl, 0, pl.P)
+    assert whole.shape[0] == pl.total
+
+
+# ----------------------------------------------------------------- fold ----
+def test_fold_exact_integers_and_untouched():
+    """Integer-valued fp32 gradients sum exactly: compare with Python ints."""
+    w = W.TINY
+    idx, _, _ = W.routing(w)
+    pl, _, _ = O.balance(idx, w.E, w.R, w.S, w.D)
+    rng = np.random.default_rng(9)
+    numel = 33
+    masters = {e: rng.integers(-1000, 1000, numel).astype(np.float32) for e in range(w.E)}
+    reps = rng.integers(-1000, 1000, (w.R * w.S, numel)).astype(np.float32)
+    out = O.fold(masters, reps, pl, 0, w.R * w.S)
+    for e in range(w.E):
+        slots = [s for s in range(w.R * w.S) if pl.slot_expert[s] == e]
+        if not slots:
+            assert e not in out
+            continue
+        want = [int(masters[e][i]) + sum(int(reps[s][i]) for s in slots) for i in range(numel)]
+        assert out[e].astype(np.int64).tolist() == want
+
+
+def test_fold_slot_range_selects_replicas():
+    w = W.SINGLE.with_(T=64)
+    idx, _, _ = W.routing(w)
+    pl, _, _ = O.balance(idx, w.E, w.R, w.S, w.D)
+    used = np.nonzero(pl.slot_expert >= 0)[0]
+    assert used.size >= 2
+    lo, hi = int(used[0]), int(used[0]) + 1
+    e = int(pl.slot_expert[lo])
+    masters = {e: np.ones(5, np.float32)}
+    reps = np.full((1, 5), 0.5, np.float32)
+    out = O.fold(masters, reps, pl, lo, hi)
+    assert list(out) == [e] and out[e].tolist() == [1.5] * 5
+    assert O.fold(masters, np.zeros((0, 5), np.float32), pl, lo, lo) == {}
+
+
+def test_fold_rounds_once_from_fp64():
+    """1 + 2^-24 + 2^-24 in fp32 step by step stays 1; summed once in fp64
+    and rounded it is 1 + 2^-23."""
+    pl = O.plan(np.array([8, 0, 0, 0]), 4, 4, 2, 4)
+    slots = [s for s in range(8) if pl.slot_expert[s] == 0]
+    assert len(slots) >= 2
+    reps = np.zeros((8, 1), np.float32)
+    reps[slots[0]] = reps[slots[1]] = np.float32(2.0 ** -24)
+    out = O.fold({0: np.array([1.0], np.float32)}, reps, pl, 0, 8)
+    assert out[0][0] == np.float32(1 + 2.0 ** -23)
