@@ -1,0 +1,254 @@
+/*
+ * ultraep.h -- C ABI of the MI355X (gfx950) exact-load expert rebalancing path.
+ *
+ * One call sequence per MoE layer and microbatch, after gating:
+ *
+ *   ultraep_balance          count the exact load per expert, solve the quota
+ *                            plan, and give every (token, k) pair its replica
+ *                            and its row in the replica-contiguous layout
+ *   ultraep_dispatch_layout  the layout's inverse index and permuted weights
+ *   ultraep_permute          gather bf16 hidden rows into the layout
+ *   ultraep_fold_grads       fold replica gradients back into their masters
+ *
+ * Sources, cited by page title and section:
+ *   [README]  "UltraEP" project README (mirror kd.iw.mk/studio-dots-ai/UltraEP)
+ *   [NEWS]    "Xiaohongshu's UltraEP Balances MoE Experts in 300 µs, Reaching
+ *             94.3% of Ideal" (news.hamidun.com)
+ *   [WEEKLY]  "UltraEP: Real-Time Load Balancing for Large-Scale MoE Training
+ *             and Inference" (aikit weekly)
+ *
+ * Conventions (all calls):
+ *   - R logical EP ranks with T tokens each; token g = r*T + t (rank-major).
+ *     top-k routing is int32 topk_idx[L][R*T][k]; pair n = g*k + j, N = R*T*k
+ *     pairs per layer (N < 2^31).  Ids outside [0, E) are dropped pairs.
+ *   - E experts, M = E/R masters per rank; expert e lives on rank e / M.
+ *   - S redundant slots per rank ([README] Interface, "Initialization": every
+ *     rank reserves the same number of redundant-expert slots); slot id
+ *     s = r*S + j.  Replicas stay within a scale-up domain of D consecutive
+ *     ranks ([README] principles, "Topology-aware replication").
+ *   - Physical experts P = R*(M+S), rank-major: p = r*(M+S) + j; j < M is the
+ *     master of expert r*M + j, j >= M is slot j-M of rank r.  A rank's
+ *     physical experts [r*(M+S), (r+1)*(M+S)) are its receive segment.
+ *   - Load is counted in pairs.
+ *   - Device pointers are caller-owned (any device allocator); the library
+ *     allocates no device memory and keeps no device state ([README]
+ *     principles: no dynamic allocation at runtime).  The context is host
+ *     memory, immutable after create, usable from several streams at once
+ *     as long as each call gets its own workspace and outputs.
+ *   - Every call is ordered on the given stream (a hipStream_t passed as
+ *     void*, NULL = the null stream), never synchronises the host, and reads
+ *     data-dependent sizes from the device plan, so the sequence can be
+ *     captured in a HIP graph ([README] principles: "CUDA graph" support).
+ *   - Return value: ULTRAEP_OK or a negative status (below).  Argument checks
+ *     happen on the host before anything is launched; on error nothing is
+ *     launched and outputs are untouched.  Data-dependent conditions that
+ *     cannot be reported synchronously are recorded in the plan header.
+ */
+#ifndef ULTRAEP_H
+#define ULTRAEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define ULTRAEP_OK 0
+#define ULTRAEP_EINVAL (-1)       /* bad argument: shape rules, null pointer, range */
+#define ULTRAEP_EUNSUPPORTED (-2) /* legal but beyond this build's limits or alignment */
+#define ULTRAEP_ELAUNCH (-3)      /* a HIP launch or runtime call failed */
+#define ULTRAEP_EWORKSPACE (-4)   /* workspace smaller than ultraep_workspace_bytes */
+
+/* Limits of this build. */
+#define ULTRAEP_MAX_EXPERTS 1024      /* E */
+#define ULTRAEP_MAX_MASTERS 16        /* M = E/R */
+#define ULTRAEP_MAX_SLOTS 8           /* S */
+#define ULTRAEP_MAX_DOMAIN 64         /* D: one rank per lane of a wave64 */
+#define ULTRAEP_MAX_TOTAL_SLOTS 2048  /* R*S */
+#define ULTRAEP_MAX_TOPK 64           /* k */
+
+typedef struct ultraep_ctx ultraep_ctx;
+
+/* Planning options ([README] "Performance Tuning", "Replication planning").
+ * eps_num/eps_den: the balancing tolerance eps (default 1/100, the pages'
+ *   default 0.01).  The quota grid steps by floor(total*eps/R), at least 1.
+ * allow_zero_master: 0 (default) = a master with load keeps at least one
+ *   pair; 1 = a master may give all of its load to replicas. */
+typedef struct ultraep_options {
+  int32_t eps_num;
+  int32_t eps_den;
+  int32_t allow_zero_master;
+  int32_t reserved[5]; /* must be zero */
+} ultraep_options;
+
+/* Create a planning context for E experts over R ranks with S redundant slots
+ * per rank and scale-up domains of D ranks ([README] Interface,
+ * "Initialization": one manager per EP group with a fixed number of
+ * redundant slots per rank).
+ * Rules: E % R == 0, R % D == 0, 1 <= E <= ULTRAEP_MAX_EXPERTS,
+ * E/R <= ULTRAEP_MAX_MASTERS, 0 <= S <= ULTRAEP_MAX_SLOTS,
+ * 1 <= D <= ULTRAEP_MAX_DOMAIN, R*S <= ULTRAEP_MAX_TOTAL_SLOTS.
+ * opt may be NULL (defaults).  *out receives a host object the caller frees
+ * with ultraep_destroy.  No HIP call is made. */
+int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
+                   const ultraep_options* opt, ultraep_ctx** out);
+
+/* Free a context (NULL is accepted). */
+int ultraep_destroy(ultraep_ctx* ctx);
+
+/* Bytes of one layer's plan record (a multiple of 256).  Plan records of L
+ * layers are laid out back to back.  The record is int32 words; the offset
+ * and length of each field are given by ultraep_plan_field. */
+int ultraep_plan_bytes(const ultraep_ctx* ctx, size_t* out);
+
+/* Plan record fields.  All int32. */
+enum ultraep_plan_field_id {
+  ULTRAEP_PLAN_HEADER = 0,       /* [64] see ULTRAEP_HDR_* */
+  ULTRAEP_PLAN_COUNTS = 1,       /* [E] pairs routed to each expert */
+  ULTRAEP_PLAN_MASTER_QUOTA = 2, /* [E] pairs the master keeps */
+  ULTRAEP_PLAN_SLOT_EXPERT = 3,  /* [R*S] expert replicated into slot s, -1 = empty */
+  ULTRAEP_PLAN_SLOT_QUOTA = 4,   /* [R*S] pairs served by slot s (0 if empty) */
+  ULTRAEP_PLAN_PHYS_LOAD = 5,    /* [P] pairs per physical expert */
+  ULTRAEP_PLAN_PHYS_OFF = 6,     /* [P+1] exclusive prefix of PHYS_LOAD: layout rows */
+  ULTRAEP_PLAN_INST_PTR = 7,     /* [E+1] CSR: expert e's instances are [ptr[e], ptr[e+1]) */
+  ULTRAEP_PLAN_INST_PHYS = 8,    /* [E+R*S] physical id of each instance, ascending per expert */
+  ULTRAEP_PLAN_INST_END = 9,     /* [E+R*S] cumulative end of the instance's ordinal range */
+  ULTRAEP_PLAN_INST_BASE = 10,   /* [E+R*S] layout row of ordinal o is INST_BASE + o */
+  ULTRAEP_PLAN_RANK_BEFORE = 11, /* [R] home load before balancing */
+  ULTRAEP_PLAN_RANK_AFTER = 12,  /* [R] load after balancing */
+  ULTRAEP_PLAN_NUM_FIELDS = 13
+};
+
+/* Header words (ULTRAEP_PLAN_HEADER). */
+enum ultraep_header_word {
+  ULTRAEP_HDR_MAGIC = 0,      /* 0x55455031 */
+  ULTRAEP_HDR_E = 1,
+  ULTRAEP_HDR_R = 2,
+  ULTRAEP_HDR_S = 3,
+  ULTRAEP_HDR_D = 4,
+  ULTRAEP_HDR_M = 5,
+  ULTRAEP_HDR_P = 6,
+  ULTRAEP_HDR_N = 7,          /* pairs in the layer */
+  ULTRAEP_HDR_TOTAL = 8,      /* valid pairs = layout rows */
+  ULTRAEP_HDR_DROPPED = 9,    /* pairs with an id outside [0, E) */
+  ULTRAEP_HDR_Q_STAR = 10,    /* the quota the plan reached (max rank load) */
+  ULTRAEP_HDR_Q_LB = 11,      /* first grid quota */
+  ULTRAEP_HDR_Q_MAX = 12,     /* max home load (always reachable) */
+  ULTRAEP_HDR_TOL = 13,       /* grid step */
+  ULTRAEP_HDR_GRID_INDEX = 14,/* index of Q_STAR on the grid */
+  ULTRAEP_HDR_FLOOR = 15,     /* max over domains of ceil(domain load / D) */
+  ULTRAEP_HDR_REPLICAS = 16,  /* filled slots */
+  ULTRAEP_HDR_ROUNDS = 17,    /* probe rounds the device solver ran (diagnostic only) */
+  ULTRAEP_HDR_WORDS = 64
+};
+
+#define ULTRAEP_PLAN_MAGIC 0x55455031
+
+/* Offset (bytes from the start of a record) and element count of a field. */
+int ultraep_plan_field(const ultraep_ctx* ctx, int32_t field, size_t* offset_bytes, size_t* count);
+
+/* Workspace bytes ultraep_balance needs for L layers of R*T*k pairs (per-tile
+ * expert histograms, turned into per-tile ordinal bases).  The workspace is
+ * scratch: nothing in it must be initialised, and ultraep_balance leaves in
+ * it nothing the other calls read. */
+int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_t k, size_t* out);
+
+/* Balance L layers ([README] Interface, "Forward and backward":
+ * update_placement plans from the exact post-gating load, reroute expands
+ * logical routing to physical replicas; [NEWS] "How balancing in 300
+ * microseconds works": a quota-driven scheduler right after gating).
+ *
+ * In:  topk_idx  int32 [L][R*T][k]
+ * Out: plans     L plan records (ultraep_plan_bytes each)
+ *      phys_idx  int32 [L][N]  physical expert of each pair, -1 if dropped
+ *      pos       int32 [L][N]  layout row of each pair, -1 if dropped
+ *
+ * Per layer:
+ *  1. c[e] = number of pairs with id e.
+ *  2. Quota grid: Q_lb = max over domains of ceil(domain load / D) (never
+ *     below ceil(total/R)), step tol = max(1, floor(total*eps/R)), up to the
+ *     max home load Q_max; Q* = the first grid quota the greedy reaches.
+ *  3. The greedy, per domain: ranks above Q shed their excess from their
+ *     hottest experts first (pairs desc, id asc), each master keeping one
+ *     pair unless allow_zero_master; the largest shed piece (ties: lower id)
+ *     goes whole to the tightest receiver that fits (least spare, then lowest
+ *     rank); if none fits and another shedding rank could host it, the
+ *     roomiest receiver is filled and the rest is swapped onto that rank,
+ *     which sheds as much more of its own largest queued expert (ties: lower
+ *     id); otherwise the roomiest receiver (most spare, then lowest rank) is
+ *     filled and the rest queued.  A receiver needs a free slot and must not
+ *     already host the expert.  Slot index = arrival order on the rank.
+ *  4. Instances of expert e: its master and replicas in ascending physical
+ *     id; instance i serves ordinals [start_i, end_i) where ordinal o(n) is
+ *     the number of earlier pairs (lower n) with the same expert.
+ *  5. phys_idx[n] = the instance's physical id; pos[n] = phys_off[p] +
+ *     o(n) - start_i.  So the layout lists pairs by (physical expert, n).
+ * The result is deterministic and identical on every run.
+ *
+ * Errors: EINVAL for null pointers (when L*N > 0), L < 0, T < 0,
+ * k outside [1, min(E, ULTRAEP_MAX_TOPK)]; EUNSUPPORTED when N >= 2^31 or a
+ * pointer is not 4-byte aligned; EWORKSPACE when workspace_bytes is short. */
+int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx, int64_t T,
+                    int32_t k, void* workspace, size_t workspace_bytes, void* plans,
+                    int32_t* phys_idx, int32_t* pos, void* stream);
+
+/* Inverse index and permuted routing weights of the dispatch layout
+ * ([README] Interface, "Forward and backward": tokens are dispatched to the
+ * physical experts that reroute produced).
+ * In:  pos [L][N] from ultraep_balance, topk_w fp32 [L][R*T][k]
+ * Out: inv [L][N]: inv[pos[n]] = n;  w_perm [L][N]: w_perm[pos[n]] = topk_w[n].
+ * Only rows [0, total) of each layer are written (total is in the plan
+ * header); pos entries outside [0, N) are ignored.
+ * Errors: EINVAL (null pointers with L*N > 0, L < 0, T < 0, bad k),
+ * EUNSUPPORTED (N >= 2^31, pointers not 4-byte aligned). */
+int ultraep_dispatch_layout(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_t k,
+                            const int32_t* pos, const float* topk_w, int32_t* inv,
+                            float* w_perm, void* stream);
+
+/* Gather the bf16 hidden rows of physical experts [p_begin, p_end) of one
+ * layer into the layout order (one rank's receive segment when the range is
+ * [r*(M+S), (r+1)*(M+S))).
+ * In:  plan (one record), inv [N] of that layer, hidden [hidden_rows][H] bf16
+ *      (raw 16-bit patterns, never converted)
+ * Out: out [rows][H] with rows = phys_off[p_end] - phys_off[p_begin]; row i is
+ *      hidden[inv[phys_off[p_begin] + i] / k].  Rows at or beyond
+ *      out_capacity_rows are not written (the caller sizes out from the plan
+ *      or from a bound); a row whose inv entry is negative or names a token
+ *      at or beyond hidden_rows is written as zeros.
+ * Errors: EINVAL (null pointers, H <= 0, k outside [1, 64], bad range
+ *      0 <= p_begin <= p_end <= P, out_capacity_rows < 0); EUNSUPPORTED
+ *      (H % 8 != 0 or hidden/out not 16-byte aligned: rows move as 16-byte
+ *      vectors). */
+int ultraep_permute(const ultraep_ctx* ctx, const void* plan, const int32_t* inv, int32_t k,
+                    const uint16_t* hidden, int64_t hidden_rows, int32_t H, int32_t p_begin,
+                    int32_t p_end, uint16_t* out, int64_t out_capacity_rows, void* stream);
+
+/* Fold replica gradients into their masters ([README] Interface, "Forward and
+ * backward": grad_reduce reduces replica weight gradients into the master
+ * experts' gradients; "Performance Tuning", "Expert communication":
+ * deterministic, non-atomic reduction).
+ * For every expert e with a replica in slots [slot_begin, slot_end):
+ *   master_grads[e][i] += the replicas' grads, added one after another in
+ *   fp32 in ascending slot order.
+ * In:  plan (one record); master_grads: DEVICE array of E device pointers
+ *      (entries of experts without a replica in the range may be NULL; a NULL
+ *      entry of a touched expert is skipped); replica_grads fp32
+ *      [slot_end - slot_begin][numel], slot s at row s - slot_begin.
+ * Out: the touched masters, in place.  Masters may not alias replica_grads.
+ * Errors: EINVAL (null pointers, numel < 0, bad slot range
+ *      0 <= slot_begin <= slot_end <= R*S).  Any alignment works; 16-byte
+ *      aligned buffers with numel % 4 == 0 take the vector path. */
+int ultraep_fold_grads(const ultraep_ctx* ctx, const void* plan, float* const* master_grads,
+                       const float* replica_grads, int64_t numel, int32_t slot_begin,
+                       int32_t slot_end, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ultraep_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULTRAEP_H */

@@ -1,0 +1,55 @@
+// Internal interface between the C ABI (ultraep_abi.hip) and the gfx950
+// kernels (ultraep_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ultraep.h"
+
+namespace ultraep {
+
+// Pairs handled by one count / reroute workgroup: 4 wave64s, 2048 pairs each.
+constexpr int kTile = 8192;
+constexpr int kTileThreads = 256;
+constexpr int kWavePairs = kTile / (kTileThreads / 64);
+constexpr int kChunks = kWavePairs / 64;
+// The plan solver runs in one workgroup of 16 waves per layer.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kHeaderWords = ULTRAEP_HDR_WORDS;
+
+struct PlanLayout {
+  int32_t off[ULTRAEP_PLAN_NUM_FIELDS];  // word offset of each field
+  int32_t len[ULTRAEP_PLAN_NUM_FIELDS];  // elements of each field
+  int32_t words;                         // record words, a multiple of 64 (256 bytes)
+};
+
+struct Shape {
+  int32_t E, R, S, D, M, P, ndom;
+  int32_t n_inst;                        // E + R*S instance entries
+  int32_t eps_num, eps_den, allow_zero;
+  PlanLayout lay;
+};
+
+inline int64_t ntiles_of(int64_t N) { return (N + kTile - 1) / kTile; }
+
+// Launchers.  All work is queued on `st`; none of them synchronises.
+hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, int32_t N,
+                          int32_t* tile_hist, int32_t* plans, int32_t* phys_idx, int32_t* pos,
+                          hipStream_t st);
+hipError_t launch_layout(int32_t L, int32_t N, const int32_t* pos, const float* w,
+                         int32_t* inv, float* w_perm, hipStream_t st);
+hipError_t launch_permute(const Shape& sh, const int32_t* plan, const int32_t* inv, int32_t k,
+                          const uint16_t* hidden, int64_t hidden_rows, int32_t H,
+                          int32_t p_begin, int32_t p_end, uint16_t* out, int64_t cap,
+                          hipStream_t st);
+hipError_t launch_fold(const Shape& sh, const int32_t* plan, float* const* masters,
+                       const float* reps, int64_t numel, int32_t slot_begin, int32_t slot_end,
+                       hipStream_t st);
+
+// Bytes of dynamic LDS the plan solver needs for this shape.
+size_t plan_lds_bytes(const Shape& sh);
+
+}  // namespace ultraep

@@ -1,0 +1,996 @@
+// gfx950 (CDNA4) kernels of the exact-load expert rebalancing path.
+//
+// Sources, cited by page title and section:
+//   [README] "UltraEP" project README (mirror kd.iw.mk/studio-dots-ai/UltraEP)
+//   [NEWS]   "Xiaohongshu's UltraEP Balances MoE Experts in 300 µs, Reaching
+//            94.3% of Ideal" (news.hamidun.com)
+//
+// Nothing here is a dense contraction, so no MFMA: the count, reroute,
+// layout, permute and fold kernels are HBM-streaming kernels built around
+// wave64 ballots, LDS-privatised counters and 16-byte vector accesses, and
+// the plan solver is a latency-bound single-workgroup kernel that keeps all
+// of its state in LDS and registers.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ultraep_internal.h"
+
+namespace ultraep {
+namespace {
+
+// ------------------------------------------------------------------------
+// wave64 helpers
+// ------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Number of set bits of m in lanes below the calling lane.
+__device__ __forceinline__ int count_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
+}
+
+// Wave-wide max / min of an unsigned value; every lane must be active.  The
+// butterfly inside each 16-lane row uses DPP (quad swaps, half-row and row
+// mirrors); the four row results are combined through scalar registers.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max(x, dpp<0x141>(x));  // row_half_mirror
+  x = max(x, dpp<0x140>(x));  // row_mirror
+  return max(max(readlane(x, 0), readlane(x, 16)), max(readlane(x, 32), readlane(x, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+  x = min(x, dpp<0xB1>(x));
+  x = min(x, dpp<0x4E>(x));
+  x = min(x, dpp<0x141>(x));
+  x = min(x, dpp<0x140>(x));
+  return min(min(readlane(x, 0), readlane(x, 16)), min(readlane(x, 32), readlane(x, 48)));
+}
+
+__device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(m); }
+
+// 16-byte vectors as native clang vectors (the nontemporal builtins take
+// these, not HIP's struct vector types).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Lanes of the wave holding the same value v (v < 2^nbits).  Every lane must
+// be active: the complement of a ballot is taken over all 64 lanes.
+__device__ __forceinline__ uint64_t match_peers(uint32_t v, int nbits) {
+  uint64_t peers = ~0ull;
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (v >> b) & 1u;
+    const uint64_t bb = ballot(bit);
+    peers &= bit ? bb : ~bb;
+  }
+  return peers;
+}
+
+// ------------------------------------------------------------------------
+// count: per-tile expert histogram ([README] intro: exact post-gating load)
+// ------------------------------------------------------------------------
+// One workgroup per (layer, tile of kTile pairs).  Each wave takes a
+// contiguous 2048-pair stretch, loads it 64 pairs at a time with dword loads
+// (256 B per wave instruction), groups equal expert ids with ballots and lets
+// one lane per group add the group size to an LDS counter, so a hot expert
+// costs one LDS atomic per wave instruction instead of one per pair.
+__global__ __launch_bounds__(kTileThreads) void count_kernel(
+    const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles, int32_t nbits,
+    int32_t* __restrict__ hist) {
+  extern __shared__ int32_t s_cnt[];
+  const int64_t blk = blockIdx.x;
+  const int32_t layer = static_cast<int32_t>(blk / ntiles);
+  const int32_t tile = static_cast<int32_t>(blk % ntiles);
+  for (int i = threadIdx.x; i < E; i += kTileThreads) s_cnt[i] = 0;
+  __syncthreads();
+
+  const int32_t* src = idx + static_cast<int64_t>(layer) * N + static_cast<int64_t>(tile) * kTile;
+  const int n_here = min(kTile, N - tile * kTile);
+  const int lane = lane_id();
+  const int base = (threadIdx.x >> 6) * kWavePairs;
+
+  uint32_t v[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = base + c * 64 + lane;
+    const uint32_t x = (i < n_here) ? static_cast<uint32_t>(__builtin_nontemporal_load(src + i))
+                                    : static_cast<uint32_t>(E);
+    v[c] = x < static_cast<uint32_t>(E) ? x : static_cast<uint32_t>(E);
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t peers = match_peers(v[c], nbits);
+    if (lane == lowest_lane(peers) && v[c] < static_cast<uint32_t>(E))
+      atomicAdd(&s_cnt[v[c]], __builtin_popcountll(peers));
+  }
+  __syncthreads();
+  int32_t* dst = hist + (static_cast<int64_t>(layer) * ntiles + tile) * E;
+  for (int i = threadIdx.x; i < E; i += kTileThreads) dst[i] = s_cnt[i];
+}
+
+// ------------------------------------------------------------------------
+// plan: quota solver, one workgroup per layer
+// ------------------------------------------------------------------------
+struct PlanParams {
+  int32_t E, R, S, D, M, P, ndom, n_inst;
+  int32_t N, ntiles;
+  int32_t eps_num, eps_den, allow_zero;
+  int32_t rec_words;
+  int32_t G, items;  // grid quotas per probe round, (quota, domain) items per round
+  int32_t off[ULTRAEP_PLAN_NUM_FIELDS];
+  int32_t len[ULTRAEP_PLAN_NUM_FIELDS];
+};
+
+enum Scalar {
+  kTotal = 0, kQmax, kFloor, kQlb, kTol, kK, kWin, kReplicas, kScalars = 16
+};
+
+struct PlanLds {
+  int32_t* c;      // [E]
+  int32_t* H;      // [R]
+  int32_t* part;   // [kPlanThreads]
+  int32_t* dom;    // [ndom]
+  int32_t* scal;   // [kScalars]
+  int32_t* ok;     // [items]
+  int32_t* res;    // [2][items][D*S]  hosted expert, then its quota
+  int32_t* mq;     // [E]
+  int32_t* nrep;   // [E]
+  int32_t* iptr;   // [E+1]
+  int32_t* pload;  // [P+1]
+  int32_t* slotE;  // [R*S]
+  int32_t* slotQ;  // [R*S]
+};
+
+__host__ __device__ inline size_t plan_lds_words(int E, int R, int S, int D, int P, int ndom,
+                                                 int items) {
+  return static_cast<size_t>(E) + R + kPlanThreads + ndom + kScalars + items +
+         2ull * items * D * S + E + E + (E + 1) + (P + 1) + 2ull * R * S;
+}
+
+__device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
+  PlanLds L;
+  int32_t* p = lds;
+  L.c = p; p += a.E;
+  L.H = p; p += a.R;
+  L.part = p; p += kPlanThreads;
+  L.dom = p; p += a.ndom;
+  L.scal = p; p += kScalars;
+  L.ok = p; p += a.items;
+  L.res = p; p += 2 * a.items * a.D * a.S;
+  L.mq = p; p += a.E;
+  L.nrep = p; p += a.E;
+  L.iptr = p; p += a.E + 1;
+  L.pload = p; p += a.P + 1;
+  L.slotE = p; p += a.R * a.S;
+  L.slotQ = p;
+  return L;
+}
+
+// In-place exclusive scan of a[0..n) in LDS by the whole workgroup; a[n]
+// receives the total.  tmp holds kPlanThreads words.
+__device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
+  const int tid = threadIdx.x;
+  const int per = (n + kPlanThreads - 1) / kPlanThreads;
+  const int b = min(tid * per, n), en = min(b + per, n);
+  int s = 0;
+  for (int i = b; i < en; ++i) s += a[i];
+  tmp[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < kPlanThreads; o <<= 1) {
+    const int v = tid >= o ? tmp[tid - o] : 0;
+    __syncthreads();
+    tmp[tid] += v;
+    __syncthreads();
+  }
+  int run = tmp[tid] - s;
+  for (int i = b; i < en; ++i) {
+    const int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (tid == kPlanThreads - 1) a[n] = tmp[kPlanThreads - 1];
+  __syncthreads();
+}
+
+// One feasibility probe: can domain d be brought to at most Q with the
+// greedy placement?  Runs on one wave; lane l plays rank d*D + l and holds
+// that rank's M queued pieces and S hosted replicas in registers.  On success
+// the hosted (expert, quota) lists go to res_e / res_q ([D][S]).
+//
+// The pages describe a quota-driven scheduler that replicates hot experts to
+// idle ranks and merges cold ones ([NEWS] "How balancing in 300 microseconds
+// works"; [README] "Replication planning": a master may be required to keep
+// part of its load) without giving its steps; this build's greedy:
+//  shed    a rank above Q gives up its excess from its hottest experts first
+//          (pairs desc, id asc), each master keeping one pair unless zero
+//          master quota is allowed;
+//  pop     the largest queued piece (ties: lowest expert id);
+//  fit     the receiver with the least spare that still takes it whole
+//          (ties: lowest rank);
+//  chain   else, if a shedding rank could host it, the roomiest receiver is
+//          filled and the rest goes to the rank of the largest such queued
+//          piece, which sheds that much more of its own expert;
+//  fill    else the roomiest receiver (most spare, ties: lowest rank) is
+//          filled and the rest queued;
+//  fail    else.
+// Each step fills a slot, so at most D*S steps run.
+template <int MMAX, int SMAX>
+__device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLds& L,
+                             int32_t* res_e, int32_t* res_q) {
+  const int lane = lane_id();
+  const int D = a.D, M = a.M, S = a.S;
+  const bool act = lane < D;
+  const int r = d * D + lane;
+  const int32_t Hr = act ? L.H[r] : 0;
+
+  int32_t ce[MMAX], pa[MMAX], room[MMAX];
+#pragma unroll
+  for (int j = 0; j < MMAX; ++j) {
+    ce[j] = (act && j < M) ? L.c[r * M + j] : 0;
+    pa[j] = 0;
+    room[j] = 0;
+  }
+  bool fail = false;
+  if (act && Hr > Q) {
+    int32_t X = Hr - Q;
+    uint32_t used = 0;
+    for (int step = 0; step < M; ++step) {
+      int bj = 0;
+      int32_t bc = -1;
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j)
+        if (j < M && !((used >> j) & 1u) && ce[j] > bc) {
+          bc = ce[j];
+          bj = j;
+        }
+      used |= 1u << bj;
+      const int32_t keep = (bc > 0 && !a.allow_zero) ? 1 : 0;
+      const int32_t t = min(X, bc - keep);
+      if (t > 0) {
+#pragma unroll
+        for (int j = 0; j < MMAX; ++j)
+          if (j == bj) {
+            pa[j] = t;
+            room[j] = bc - keep - t;
+          }
+        X -= t;
+      }
+    }
+    fail = X > 0;
+  }
+  if (ballot(fail)) return false;
+
+  int32_t spare = act ? max(0, Q - Hr) : 0;
+  int32_t freeslots = act ? S : 0;
+  int nh = 0;
+  int32_t he[SMAX], hq[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    he[s] = -1;
+    hq[s] = 0;
+  }
+  auto place = [&](int32_t e, int32_t x) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s == nh) {
+        he[s] = e;
+        hq[s] = x;
+      }
+    ++nh;
+    --freeslots;
+  };
+
+  const int max_steps = D * S + 1;
+  bool done = false;
+  for (int step = 0; step <= max_steps; ++step) {
+    // pop the largest piece
+    uint32_t mya = 0;
+    int myj = 0;
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j)
+      if (static_cast<uint32_t>(pa[j]) > mya) {
+        mya = static_cast<uint32_t>(pa[j]);
+        myj = j;
+      }
+    const uint32_t amax = wave_max(mya);
+    if (amax == 0) {
+      done = true;
+      break;
+    }
+    const int owner = lowest_lane(ballot(mya == amax));
+    const int jsel = static_cast<int>(readlane(static_cast<uint32_t>(myj), owner));
+    const int32_t e = (d * D + owner) * M + jsel;
+    int32_t amt = static_cast<int32_t>(amax);
+    if (lane == owner) {
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j)
+        if (j == jsel) pa[j] = 0;
+    }
+    bool hosts = false;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) hosts |= (he[s] == e);
+    const bool elig = act && lane != owner && freeslots > 0 && !hosts;
+
+    // fit: least spare that takes the whole piece
+    const uint32_t fitv = (elig && spare >= amt) ? static_cast<uint32_t>(spare) : 0xFFFFFFFFu;
+    const uint32_t fmin = wave_min(fitv);
+    if (fmin != 0xFFFFFFFFu) {
+      const int rr = lowest_lane(ballot(fitv == fmin));
+      if (lane == rr) {
+        place(e, amt);
+        spare -= amt;
+      }
+      continue;
+    }
+    // roomiest receiver
+    const uint32_t recv = (elig && spare > 0) ? static_cast<uint32_t>(spare) : 0u;
+    const uint32_t rmax = wave_max(recv);
+    // donor: largest queued piece on an eligible rank with room left
+    uint32_t dbest = 0;
+    int dj = 0;
+    if (elig) {
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j)
+        if (pa[j] > 0 && room[j] > 0 && static_cast<uint32_t>(pa[j]) > dbest) {
+          dbest = static_cast<uint32_t>(pa[j]);
+          dj = j;
+        }
+    }
+    const uint32_t dmax = wave_max(dbest);
+    if (dmax > 0) {
+      const int dl = lowest_lane(ballot(dbest == dmax));
+      const int djs = static_cast<int>(readlane(static_cast<uint32_t>(dj), dl));
+      if (rmax > 0) {
+        const int r2 = lowest_lane(ballot(recv == rmax));
+        if (lane == r2) {
+          place(e, spare);
+          spare = 0;
+        }
+        amt -= static_cast<int32_t>(rmax);
+      }
+      int32_t myroom = 0;
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j)
+        if (j == djs) myroom = room[j];
+      const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
+      const int32_t x = min(amt, droom);
+      if (lane == dl) {
+        place(e, x);
+#pragma unroll
+        for (int j = 0; j < MMAX; ++j)
+          if (j == djs) {
+            pa[j] += x;
+            room[j] -= x;
+          }
+      }
+      amt -= x;
+      if (amt > 0 && lane == owner) {
+#pragma unroll
+        for (int j = 0; j < MMAX; ++j)
+          if (j == jsel) pa[j] = amt;
+      }
+    } else if (rmax > 0) {
+      const int r2 = lowest_lane(ballot(recv == rmax));
+      if (lane == r2) {
+        place(e, spare);
+        spare = 0;
+      }
+      amt -= static_cast<int32_t>(rmax);
+      if (lane == owner) {
+#pragma unroll
+        for (int j = 0; j < MMAX; ++j)
+          if (j == jsel) pa[j] = amt;
+      }
+    } else {
+      break;  // fail
+    }
+  }
+  if (!done) return false;
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s < S) {
+        res_e[lane * S + s] = he[s];
+        res_q[lane * S + s] = hq[s];
+      }
+  }
+  return true;
+}
+
+template <int MMAX, int SMAX>
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int32_t* __restrict__ hist,
+                                                            int32_t* __restrict__ plans,
+                                                            PlanParams a) {
+  extern __shared__ int32_t lds[];
+  const PlanLds L = carve(lds, a);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = lane_id();
+  const int layer = blockIdx.x;
+  const int E = a.E, R = a.R, S = a.S, D = a.D, M = a.M, P = a.P;
+  int32_t* H = hist + static_cast<int64_t>(layer) * a.ntiles * E;
+  int32_t* rec = plans + static_cast<int64_t>(layer) * a.rec_words;
+
+  if (tid < kScalars) L.scal[tid] = 0;
+  for (int d = tid; d < a.ndom; d += kPlanThreads) L.dom[d] = 0;
+
+  // -- phase 0: per-expert exclusive prefix over tiles (in place) and totals.
+  {
+    const int nch = kPlanThreads / E;
+    const int clen = (a.ntiles + nch - 1) / nch;
+    const int e = tid % E, ch = tid / E;
+    const bool act = ch < nch;
+    const int t0 = min(ch * clen, a.ntiles), t1 = min(t0 + clen, a.ntiles);
+    int32_t sum = 0;
+    if (act) {
+#pragma unroll 8
+      for (int t = t0; t < t1; ++t) sum += H[static_cast<int64_t>(t) * E + e];
+    }
+    L.part[tid] = sum;
+    __syncthreads();
+    int32_t base = 0;
+    if (act) {
+      for (int q = 0; q < ch; ++q) base += L.part[q * E + e];
+      if (ch == nch - 1) L.c[e] = base + sum;
+    }
+    if (act) {
+      int32_t run = base;
+#pragma unroll 8
+      for (int t = t0; t < t1; ++t) {
+        const int64_t k = static_cast<int64_t>(t) * E + e;
+        const int32_t v = H[k];
+        H[k] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+  }
+  // -- phase 1: home loads, total, grid.
+  for (int r = tid; r < R; r += kPlanThreads) {
+    int32_t s = 0;
+    for (int j = 0; j < M; ++j) s += L.c[r * M + j];
+    L.H[r] = s;
+    atomicAdd(&L.scal[kTotal], s);
+    atomicMax(&L.scal[kQmax], s);
+    atomicAdd(&L.dom[r / D], s);
+  }
+  __syncthreads();
+  for (int d = tid; d < a.ndom; d += kPlanThreads)
+    atomicMax(&L.scal[kFloor], (L.dom[d] + D - 1) / D);
+  __syncthreads();
+  if (tid == 0) {
+    const int32_t total = L.scal[kTotal], qmax = L.scal[kQmax];
+    const int32_t qmean = (total + R - 1) / R;
+    const int32_t qlb = max(qmean, L.scal[kFloor]);
+    const int64_t tol64 = (static_cast<int64_t>(total) * a.eps_num) /
+                          (static_cast<int64_t>(R) * a.eps_den);
+    const int32_t tol = static_cast<int32_t>(tol64 < 1 ? 1 : tol64);
+    L.scal[kQlb] = qlb;
+    L.scal[kTol] = tol;
+    L.scal[kK] = qmax > qlb ? (qmax - qlb + tol - 1) / tol : 0;
+  }
+  __syncthreads();
+  const int32_t qlb = L.scal[kQlb], tol = L.scal[kTol], K = L.scal[kK], qmax = L.scal[kQmax];
+
+  // -- phase 2: probe rounds; each wave takes (grid quota, domain) items.
+  const bool no_moves = (S == 0 || D == 1);
+  int32_t winner = no_moves ? K : -1;
+  int32_t wg0 = 0, rounds = 0;
+  for (int32_t g0 = 0; winner < 0; g0 += a.G) {
+    ++rounds;
+    for (int item = wave; item < a.items; item += kPlanWaves) {
+      const int32_t g = g0 + item / a.ndom;
+      const int d = item % a.ndom;
+      bool okv = false;
+      if (g <= K) {
+        const int32_t Q = g < K ? qlb + g * tol : qmax;
+        okv = greedy_probe<MMAX, SMAX>(Q, d, a, L, L.res + static_cast<size_t>(item) * D * S,
+                                       L.res + static_cast<size_t>(a.items + item) * D * S);
+      }
+      if (lane == 0) L.ok[item] = okv ? 1 : 0;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int32_t w = -1;
+      for (int gg = 0; gg < a.G && w < 0 && g0 + gg <= K; ++gg) {
+        bool all = true;
+        for (int d = 0; d < a.ndom; ++d) all = all && L.ok[gg * a.ndom + d];
+        if (all) w = g0 + gg;
+      }
+      L.scal[kWin] = w;
+    }
+    __syncthreads();
+    winner = L.scal[kWin];
+    wg0 = g0;
+    __syncthreads();
+  }
+
+  // -- phase 3: the plan record.
+  for (int s = tid; s < R * S; s += kPlanThreads) {
+    int32_t e = -1, q = 0;
+    if (!no_moves) {
+      const int r = s / S, j = s % S, d = r / D, lr = r % D;
+      const int item = (winner - wg0) * a.ndom + d;
+      e = L.res[static_cast<size_t>(item) * D * S + lr * S + j];
+      q = L.res[static_cast<size_t>(a.items + item) * D * S + lr * S + j];
+    }
+    L.slotE[s] = e;
+    L.slotQ[s] = e >= 0 ? q : 0;
+  }
+  for (int e = tid; e < E; e += kPlanThreads) {
+    L.mq[e] = L.c[e];
+    L.nrep[e] = 1;
+  }
+  __syncthreads();
+  for (int s = tid; s < R * S; s += kPlanThreads) {
+    const int32_t e = L.slotE[s];
+    if (e >= 0) {
+      atomicSub(&L.mq[e], L.slotQ[s]);
+      atomicAdd(&L.nrep[e], 1);
+      atomicAdd(&L.scal[kReplicas], 1);
+    }
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += kPlanThreads) {
+    const int r = p / (M + S), j = p % (M + S);
+    L.pload[p] = j < M ? L.mq[r * M + j] : L.slotQ[r * S + (j - M)];
+  }
+  for (int e = tid; e < E; e += kPlanThreads) L.iptr[e] = L.nrep[e];
+  __syncthreads();
+  // record the loads before the scans overwrite them
+  for (int p = tid; p < P; p += kPlanThreads) rec[a.off[ULTRAEP_PLAN_PHYS_LOAD] + p] = L.pload[p];
+  for (int r = tid; r < R; r += kPlanThreads) {
+    int32_t s = 0;
+    for (int j = 0; j < M + S; ++j) s += L.pload[r * (M + S) + j];
+    rec[a.off[ULTRAEP_PLAN_RANK_AFTER] + r] = s;
+    rec[a.off[ULTRAEP_PLAN_RANK_BEFORE] + r] = L.H[r];
+  }
+  __syncthreads();
+  block_exclusive_scan(L.pload, P, L.part);  // pload -> phys_off
+  block_exclusive_scan(L.iptr, E, L.part);   // instance counts -> inst_ptr
+
+  int32_t* inst_phys = rec + a.off[ULTRAEP_PLAN_INST_PHYS];
+  int32_t* inst_end = rec + a.off[ULTRAEP_PLAN_INST_END];
+  int32_t* inst_base = rec + a.off[ULTRAEP_PLAN_INST_BASE];
+  for (int e = tid; e < E; e += kPlanThreads) {
+    const int home = e / M, d = home / D;
+    int i = L.iptr[e];
+    int32_t end = 0;
+    for (int r = d * D; r < (d + 1) * D; ++r) {
+      if (r == home) {
+        const int p = home * (M + S) + e % M;
+        const int32_t q = L.mq[e];
+        end += q;
+        inst_phys[i] = p;
+        inst_end[i] = end;
+        inst_base[i] = L.pload[p] - (end - q);
+        ++i;
+      }
+      for (int j = 0; j < S; ++j) {
+        if (L.slotE[r * S + j] == e) {
+          const int p = r * (M + S) + M + j;
+          const int32_t q = L.slotQ[r * S + j];
+          end += q;
+          inst_phys[i] = p;
+          inst_end[i] = end;
+          inst_base[i] = L.pload[p] - (end - q);
+          ++i;
+        }
+      }
+    }
+  }
+  // unused instance entries and the padding between fields get fixed values,
+  // so a record is a pure function of its inputs
+  for (int i = L.iptr[E] + tid; i < a.n_inst; i += kPlanThreads) {
+    inst_phys[i] = -1;
+    inst_end[i] = 0;
+    inst_base[i] = 0;
+  }
+  for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
+    const int end = f + 1 < ULTRAEP_PLAN_NUM_FIELDS ? a.off[f + 1] : a.rec_words;
+    for (int wd = a.off[f] + a.len[f] + tid; wd < end; wd += kPlanThreads) rec[wd] = 0;
+  }
+  for (int e = tid; e < E; e += kPlanThreads) {
+    rec[a.off[ULTRAEP_PLAN_COUNTS] + e] = L.c[e];
+    rec[a.off[ULTRAEP_PLAN_MASTER_QUOTA] + e] = L.mq[e];
+  }
+  for (int e = tid; e <= E; e += kPlanThreads) rec[a.off[ULTRAEP_PLAN_INST_PTR] + e] = L.iptr[e];
+  for (int p = tid; p <= P; p += kPlanThreads) rec[a.off[ULTRAEP_PLAN_PHYS_OFF] + p] = L.pload[p];
+  for (int s = tid; s < R * S; s += kPlanThreads) {
+    rec[a.off[ULTRAEP_PLAN_SLOT_EXPERT] + s] = L.slotE[s];
+    rec[a.off[ULTRAEP_PLAN_SLOT_QUOTA] + s] = L.slotQ[s];
+  }
+  if (tid < kHeaderWords) {
+    int32_t v = 0;
+    const int32_t total = L.scal[kTotal];
+    switch (tid) {
+      case ULTRAEP_HDR_MAGIC: v = static_cast<int32_t>(ULTRAEP_PLAN_MAGIC); break;
+      case ULTRAEP_HDR_E: v = E; break;
+      case ULTRAEP_HDR_R: v = R; break;
+      case ULTRAEP_HDR_S: v = S; break;
+      case ULTRAEP_HDR_D: v = D; break;
+      case ULTRAEP_HDR_M: v = M; break;
+      case ULTRAEP_HDR_P: v = P; break;
+      case ULTRAEP_HDR_N: v = a.N; break;
+      case ULTRAEP_HDR_TOTAL: v = total; break;
+      case ULTRAEP_HDR_DROPPED: v = a.N - total; break;
+      case ULTRAEP_HDR_Q_STAR: v = winner < K ? qlb + winner * tol : qmax; break;
+      case ULTRAEP_HDR_Q_LB: v = qlb; break;
+      case ULTRAEP_HDR_Q_MAX: v = qmax; break;
+      case ULTRAEP_HDR_TOL: v = tol; break;
+      case ULTRAEP_HDR_GRID_INDEX: v = winner; break;
+      case ULTRAEP_HDR_FLOOR: v = L.scal[kFloor]; break;
+      case ULTRAEP_HDR_REPLICAS: v = L.scal[kReplicas]; break;
+      case ULTRAEP_HDR_ROUNDS: v = rounds; break;
+      default: v = 0; break;
+    }
+    rec[a.off[ULTRAEP_PLAN_HEADER] + tid] = v;
+  }
+}
+
+// ------------------------------------------------------------------------
+// reroute: replica and layout row of every pair ([README] Interface,
+// "Forward and backward": reroute expands logical routing to replicas)
+// ------------------------------------------------------------------------
+// Same tiling as count.  A pair's ordinal among its expert's pairs is the
+// tile's base (from the plan kernel's scan) + the pairs of earlier waves in
+// the tile + the pair's rank inside its wave, which the wave tracks with
+// ballot groups and per-wave LDS counters, so no sort is needed and the
+// result does not depend on scheduling.
+__global__ __launch_bounds__(kTileThreads) void reroute_kernel(
+    const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles, int32_t nbits,
+    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans, int32_t rec_words,
+    int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase, int32_t n_inst,
+    int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos) {
+  extern __shared__ int32_t lds[];
+  int32_t* cntw = lds;                 // [4][E]
+  int32_t* iptr = cntw + 4 * E;        // [E+1]
+  int32_t* iend = iptr + E + 1;        // [n_inst]
+  int32_t* iphys = iend + n_inst;      // [n_inst]
+  int32_t* ibase = iphys + n_inst;     // [n_inst]
+
+  const int64_t blk = blockIdx.x;
+  const int32_t layer = static_cast<int32_t>(blk / ntiles);
+  const int32_t tile = static_cast<int32_t>(blk % ntiles);
+  const int32_t* plan = plans + static_cast<int64_t>(layer) * rec_words;
+  for (int i = threadIdx.x; i < 4 * E; i += kTileThreads) cntw[i] = 0;
+  for (int i = threadIdx.x; i <= E; i += kTileThreads) iptr[i] = plan[off_iptr + i];
+  for (int i = threadIdx.x; i < n_inst; i += kTileThreads) {
+    iend[i] = plan[off_iend + i];
+    iphys[i] = plan[off_iphys + i];
+    ibase[i] = plan[off_ibase + i];
+  }
+  __syncthreads();
+
+  const int64_t first = static_cast<int64_t>(layer) * N + static_cast<int64_t>(tile) * kTile;
+  const int n_here = min(kTile, N - tile * kTile);
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int base = wave * kWavePairs;
+  int32_t* my = cntw + wave * E;
+
+  uint32_t v[kChunks];
+  int32_t lr[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = base + c * 64 + lane;
+    const uint32_t x = (i < n_here) ? static_cast<uint32_t>(__builtin_nontemporal_load(idx + first + i))
+                                    : static_cast<uint32_t>(E);
+    v[c] = x < static_cast<uint32_t>(E) ? x : static_cast<uint32_t>(E);
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t peers = match_peers(v[c], nbits);
+    const bool valid = v[c] < static_cast<uint32_t>(E);
+    const int32_t old = valid ? my[v[c]] : 0;
+    if (valid && lane == lowest_lane(peers)) my[v[c]] = old + __builtin_popcountll(peers);
+    lr[c] = old + count_below(peers);
+  }
+  __syncthreads();
+  const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
+  for (int e = threadIdx.x; e < E; e += kTileThreads) {
+    int32_t run = tb[e];
+#pragma unroll
+    for (int w = 0; w < kTileThreads / 64; ++w) {
+      const int32_t t = cntw[w * E + e];
+      cntw[w * E + e] = run;
+      run += t;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = base + c * 64 + lane;
+    if (i >= n_here) continue;
+    int32_t p = -1, row = -1;
+    if (v[c] < static_cast<uint32_t>(E)) {
+      const int e = static_cast<int>(v[c]);
+      const int32_t o = my[e] + lr[c];
+      int k = iptr[e];
+      const int last = iptr[e + 1] - 1;
+      while (k < last && o >= iend[k]) ++k;
+      p = iphys[k];
+      row = ibase[k] + o;
+    }
+    phys_idx[first + i] = p;
+    pos[first + i] = row;
+  }
+}
+
+// ------------------------------------------------------------------------
+// layout: inverse index and permuted weights
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__ pos,
+                                                     const float* __restrict__ w, int32_t L,
+                                                     int32_t N, int32_t* __restrict__ inv,
+                                                     float* __restrict__ w_perm) {
+  const int32_t stride = gridDim.x * blockDim.x;
+  for (int32_t layer = 0; layer < L; ++layer) {
+    const int64_t lb = static_cast<int64_t>(layer) * N;
+    for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < N; i += stride) {
+      const int32_t p = __builtin_nontemporal_load(pos + lb + i);
+      const float wt = __builtin_nontemporal_load(w + lb + i);
+      if (p >= 0 && p < N) {
+        inv[lb + p] = i;
+        w_perm[lb + p] = wt;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// permute: bf16 rows into the layout order
+// ------------------------------------------------------------------------
+// One wave per output row: the row index and its source token are wave
+// uniform, and the row moves as 16-byte vectors, 1 KiB per wave
+// instruction.  Up to 8 vectors per lane are loaded before any is stored so
+// enough bytes are in flight per CU; stores are non-temporal because the
+// layout is consumed by the next kernel, not re-read here.
+constexpr int kPermThreads = 256;
+constexpr int kPermUnroll = 8;
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t* __restrict__ phys_off, const int32_t* __restrict__ inv, int32_t k,
+    const u32x4* __restrict__ hidden, int64_t hidden_rows, int32_t H8, int32_t p_begin,
+    int32_t p_end, u32x4* __restrict__ out, int64_t cap) {
+  const int32_t seg0 = phys_off[p_begin];
+  const int64_t rows = min(static_cast<int64_t>(phys_off[p_end] - seg0), cap);
+  const int lane = lane_id();
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kPermThreads / 64);
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + (threadIdx.x >> 6);
+       row < rows; row += waves) {
+    const int32_t n = inv[seg0 + row];
+    const int64_t tok = n >= 0 ? n / k : -1;
+    u32x4* dst = out + row * H8;
+    if (tok < 0 || tok >= hidden_rows) {
+      for (int c = lane; c < H8; c += 64) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, dst + c);
+      continue;
+    }
+    const u32x4* src = hidden + tok * H8;
+    for (int c0 = 0; c0 < H8; c0 += 64 * kPermUnroll) {
+      u32x4 t[kPermUnroll];
+#pragma unroll
+      for (int u = 0; u < kPermUnroll; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < H8) t[u] = src[c];
+      }
+#pragma unroll
+      for (int u = 0; u < kPermUnroll; ++u) {
+        const int c = c0 + u * 64 + lane;
+        if (c < H8) __builtin_nontemporal_store(t[u], dst + c);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// fold: replica gradients into masters ([README] "Performance Tuning",
+// "Expert communication": deterministic, non-atomic reduction)
+// ------------------------------------------------------------------------
+// blockIdx.y picks a slot of the range; only the lowest in-range slot of an
+// expert does that expert's work, so each master is written by exactly one
+// set of workgroups and the sum order (master, then slots ascending) is
+// fixed.  blockIdx.x strides over the elements.
+constexpr int kFoldThreads = 256;
+constexpr int kFoldMaxReps = 64;
+
+__global__ __launch_bounds__(kFoldThreads) void fold_kernel(
+    const int32_t* __restrict__ slot_expert, const int32_t* __restrict__ inst_ptr,
+    const int32_t* __restrict__ inst_phys, int32_t M, int32_t S, float* const* __restrict__ masters,
+    const float* __restrict__ reps, int64_t numel, int32_t slot_begin, int32_t slot_end) {
+  __shared__ int32_t s_list[kFoldMaxReps];
+  __shared__ int32_t s_n;
+  const int32_t s0 = slot_begin + static_cast<int32_t>(blockIdx.y);
+  const int32_t e = slot_expert[s0];
+  if (e < 0) return;
+  if (threadIdx.x == 0) {
+    // e's instances are in ascending physical id, i.e. ascending slot id for
+    // its replicas; keep those in the range.
+    int n = 0;
+    bool first = true;
+    for (int32_t i = inst_ptr[e]; i < inst_ptr[e + 1]; ++i) {
+      const int32_t p = inst_phys[i];
+      const int32_t j = p % (M + S);
+      if (j < M) continue;
+      const int32_t s = (p / (M + S)) * S + (j - M);
+      if (s < slot_begin || s >= slot_end) continue;
+      if (n == 0 && s != s0) first = false;
+      if (n < kFoldMaxReps) s_list[n] = s - slot_begin;
+      ++n;
+    }
+    s_n = first ? n : 0;
+  }
+  __syncthreads();
+  const int n = min(s_n, kFoldMaxReps);
+  float* m = masters[e];
+  if (n == 0 || m == nullptr) return;
+
+  const int64_t tstride = static_cast<int64_t>(gridDim.x) * kFoldThreads;
+  const bool vec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(m) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(reps) & 15) == 0);
+  if (vec) {
+    const int64_t n4 = numel / 4;
+    f32x4* m4 = reinterpret_cast<f32x4*>(m);
+    const f32x4* r4 = reinterpret_cast<const f32x4*>(reps);
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x; i < n4;
+         i += tstride) {
+      f32x4 acc = m4[i];
+      for (int q = 0; q < n; ++q) {
+        const f32x4 g = __builtin_nontemporal_load(r4 + static_cast<int64_t>(s_list[q]) * n4 + i);
+        acc.x += g.x;
+        acc.y += g.y;
+        acc.z += g.z;
+        acc.w += g.w;
+      }
+      m4[i] = acc;
+    }
+  } else {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x; i < numel;
+         i += tstride) {
+      float acc = m[i];
+      for (int q = 0; q < n; ++q) acc += reps[static_cast<int64_t>(s_list[q]) * numel + i];
+      m[i] = acc;
+    }
+  }
+}
+
+inline int bit_width(uint32_t x) { return 32 - __builtin_clz(x); }
+
+template <int MMAX, int SMAX>
+hipError_t launch_plan_t(const PlanParams& pp, int32_t L, size_t lds, int32_t* hist,
+                         int32_t* plans, hipStream_t st) {
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<MMAX, SMAX>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  plan_kernel<MMAX, SMAX><<<dim3(L), dim3(kPlanThreads), lds, st>>>(hist, plans, pp);
+  return hipGetLastError();
+}
+
+template <int SMAX>
+hipError_t launch_plan_m(int M, const PlanParams& pp, int32_t L, size_t lds, int32_t* hist,
+                         int32_t* plans, hipStream_t st) {
+  if (M <= 2) return launch_plan_t<2, SMAX>(pp, L, lds, hist, plans, st);
+  if (M <= 4) return launch_plan_t<4, SMAX>(pp, L, lds, hist, plans, st);
+  if (M <= 8) return launch_plan_t<8, SMAX>(pp, L, lds, hist, plans, st);
+  return launch_plan_t<16, SMAX>(pp, L, lds, hist, plans, st);
+}
+
+void plan_rounds(const Shape& sh, int32_t* G, int32_t* items) {
+  if (sh.ndom <= kPlanWaves) {
+    *G = kPlanWaves / sh.ndom;
+    *items = *G * sh.ndom;
+  } else {
+    *G = 1;
+    *items = sh.ndom;
+  }
+}
+
+}  // namespace
+
+size_t plan_lds_bytes(const Shape& sh) {
+  int32_t G, items;
+  plan_rounds(sh, &G, &items);
+  return 4 * plan_lds_words(sh.E, sh.R, sh.S, sh.D, sh.P, sh.ndom, items);
+}
+
+hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, int32_t N,
+                          int32_t* tile_hist, int32_t* plans, int32_t* phys_idx, int32_t* pos,
+                          hipStream_t st) {
+  if (L <= 0) return hipSuccess;
+  const int32_t ntiles = static_cast<int32_t>(ntiles_of(N));
+  const int nbits = bit_width(static_cast<uint32_t>(sh.E));
+  const int64_t blocks = static_cast<int64_t>(L) * ntiles;
+  if (blocks > 0) {
+    hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads),
+                       sizeof(int32_t) * sh.E, st, idx, N, sh.E, ntiles, nbits, tile_hist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  PlanParams pp{};
+  pp.E = sh.E; pp.R = sh.R; pp.S = sh.S; pp.D = sh.D; pp.M = sh.M; pp.P = sh.P;
+  pp.ndom = sh.ndom; pp.n_inst = sh.n_inst; pp.N = N; pp.ntiles = ntiles;
+  pp.eps_num = sh.eps_num; pp.eps_den = sh.eps_den; pp.allow_zero = sh.allow_zero;
+  pp.rec_words = sh.lay.words;
+  plan_rounds(sh, &pp.G, &pp.items);
+  for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
+    pp.off[f] = sh.lay.off[f];
+    pp.len[f] = sh.lay.len[f];
+  }
+  const size_t lds = plan_lds_bytes(sh);
+  hipError_t e;
+  if (sh.S <= 2)
+    e = launch_plan_m<2>(sh.M, pp, L, lds, tile_hist, plans, st);
+  else if (sh.S <= 4)
+    e = launch_plan_m<4>(sh.M, pp, L, lds, tile_hist, plans, st);
+  else
+    e = launch_plan_m<8>(sh.M, pp, L, lds, tile_hist, plans, st);
+  if (e != hipSuccess) return e;
+  if (blocks > 0) {
+    const size_t rl = sizeof(int32_t) * (4 * sh.E + sh.E + 1 + 3 * sh.n_inst);
+    hipLaunchKernelGGL(reroute_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads), rl,
+                       st, idx, N, sh.E, ntiles, nbits, tile_hist, plans, sh.lay.words,
+                       sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
+                       sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE],
+                       sh.n_inst, phys_idx, pos);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_layout(int32_t L, int32_t N, const int32_t* pos, const float* w, int32_t* inv,
+                         float* w_perm, hipStream_t st) {
+  const int64_t total = static_cast<int64_t>(L) * N;
+  if (total <= 0) return hipSuccess;
+  const int64_t want = (static_cast<int64_t>(N) + 255) / 256;
+  const uint32_t blocks = static_cast<uint32_t>(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(layout_kernel, dim3(blocks), dim3(256), 0, st, pos, w, L, N, inv, w_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const Shape& sh, const int32_t* plan, const int32_t* inv, int32_t k,
+                          const uint16_t* hidden, int64_t hidden_rows, int32_t H, int32_t p_begin,
+                          int32_t p_end, uint16_t* out, int64_t cap, hipStream_t st) {
+  if (cap <= 0 || p_begin == p_end) return hipSuccess;
+  const int64_t want = (cap + 3) / 4;
+  const uint32_t blocks = static_cast<uint32_t>(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(kPermThreads), 0, st,
+                     plan + sh.lay.off[ULTRAEP_PLAN_PHYS_OFF], inv, k,
+                     reinterpret_cast<const u32x4*>(hidden), hidden_rows, H / 8, p_begin, p_end,
+                     reinterpret_cast<u32x4*>(out), cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const Shape& sh, const int32_t* plan, float* const* masters,
+                       const float* reps, int64_t numel, int32_t slot_begin, int32_t slot_end,
+                       hipStream_t st) {
+  const int32_t nslots = slot_end - slot_begin;
+  if (nslots <= 0 || numel <= 0) return hipSuccess;
+  const int64_t per_block = static_cast<int64_t>(kFoldThreads) * 4 * 4;
+  const int64_t want = (numel + per_block - 1) / per_block;
+  const uint32_t bx = static_cast<uint32_t>(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(fold_kernel, dim3(bx, static_cast<uint32_t>(nslots)), dim3(kFoldThreads), 0, st,
+                     plan + sh.lay.off[ULTRAEP_PLAN_SLOT_EXPERT], plan + sh.lay.off[ULTRAEP_PLAN_INST_PTR],
+                     plan + sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.M, sh.S, masters, reps, numel,
+                     slot_begin, slot_end);
+  return hipGetLastError();
+}
+
+}  // namespace ultraep

@@ -1,0 +1,123 @@
+"""The C ABI on the host (no GPU): symbols, argument checks, plan layout.
+
+Every call here either makes no HIP call at all (create, sizes, layout) or
+fails its host-side argument check before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_load_ultraep_amd as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ultraep.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(U.LIB_PATH), reason="libultraep.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ultraep_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) == 10, names
+    lib = ctypes.CDLL(U.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(U._SIGNATURES)
+
+
+def test_status_strings():
+    for code, text in U.STATUS.items():
+        assert U.status_string(code) == text
+    assert U.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("E,R,S,D,code", [
+    (8, 3, 1, 1, -1),      # E % R
+    (8, 4, 1, 3, -1),      # R % D
+    (8, 4, -1, 4, -1),     # S < 0
+    (0, 4, 1, 4, -1),
+    (2048, 64, 1, 64, -2),  # E beyond limit
+    (64, 2, 1, 2, -2),     # M = 32 beyond limit
+    (64, 64, 9, 64, -2),   # S beyond limit
+    (256, 128, 1, 128, -2),  # D beyond one wave
+    (1024, 1024, 4, 64, -2),  # R*S beyond limit
+])
+def test_create_rejects(E, R, S, D, code):
+    with pytest.raises(U.UltraEPError) as ei:
+        U.ultraep_create(E, R, S, D)
+    assert ei.value.status == code
+
+
+def test_create_rejects_bad_options():
+    with pytest.raises(U.UltraEPError):
+        U.ultraep_create(8, 4, 1, 4, eps=(1, 0))
+
+
+def test_plan_layout_fields():
+    ctx = U.ultraep_create(256, 64, 2, 64)
+    E, R, S, P = 256, 64, 2, ctx.P
+    want = {"header": 64, "counts": E, "master_quota": E, "slot_expert": R * S, "slot_quota": R * S,
+            "phys_load": P, "phys_off": P + 1, "inst_ptr": E + 1, "inst_phys": E + R * S,
+            "inst_end": E + R * S, "inst_base": E + R * S, "rank_before": R, "rank_after": R}
+    end = 0
+    for name in U.PLAN_FIELDS:
+        off, cnt = ctx.fields[name]
+        assert cnt == want[name] and off % 4 == 0 and off >= end
+        end = off + cnt
+    assert ctx.plan_bytes % 256 == 0 and end <= ctx.plan_words
+
+
+def test_workspace_bytes():
+    ctx = U.ultraep_create(128, 64, 2, 64)
+    ntiles = -(-64 * 8192 * 8 // 8192)
+    assert ctx.workspace_bytes(1, 8192, 8) == 4 * ntiles * 128
+    assert ctx.workspace_bytes(3, 8192, 8) == 3 * 4 * ntiles * 128
+    with pytest.raises(U.UltraEPError) as ei:
+        ctx.workspace_bytes(1, 8192, 0)
+    assert ei.value.status == -1
+    with pytest.raises(U.UltraEPError) as ei:
+        ctx.workspace_bytes(1, 1 << 30, 8)   # N >= 2^31
+    assert ei.value.status == -2
+
+
+FAKE = 1 << 20   # never dereferenced: every call below fails its host check
+
+
+def test_balance_argument_checks():
+    ctx = U.ultraep_create(8, 4, 1, 4)
+    f = U.lib().ultraep_balance
+    assert f(ctx.handle, -1, FAKE, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1
+    assert f(ctx.handle, 1, FAKE, 16, 0, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1   # k = 0
+    assert f(ctx.handle, 1, FAKE, 16, 9, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1   # k > E
+    assert f(ctx.handle, 1, None, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1   # null idx
+    assert f(ctx.handle, 1, FAKE + 2, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -2  # misaligned
+    assert f(ctx.handle, 1, FAKE, 16, 2, FAKE, 4, FAKE, FAKE, FAKE, None) == -4   # workspace short
+    assert f(None, 1, FAKE, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1
+    assert f(ctx.handle, 0, None, 16, 2, None, 0, None, None, None, None) == 0    # L = 0: no-op
+
+
+def test_permute_and_fold_argument_checks():
+    ctx = U.ultraep_create(8, 4, 1, 4)
+    p = U.lib().ultraep_permute
+    assert p(ctx.handle, FAKE, FAKE, 2, FAKE, 10, 12, 0, 3, FAKE, 10, None) == -2    # H % 8
+    assert p(ctx.handle, FAKE, FAKE, 2, FAKE + 8, 10, 16, 0, 3, FAKE, 10, None) == -2  # hidden not 16-B aligned
+    assert p(ctx.handle, FAKE, FAKE, 2, FAKE, 10, 16, 3, 2, FAKE, 10, None) == -1     # p_end < p_begin
+    assert p(ctx.handle, FAKE, FAKE, 2, FAKE, 10, 16, 0, ctx.P + 1, FAKE, 10, None) == -1
+    assert p(ctx.handle, FAKE, FAKE, 0, FAKE, 10, 16, 0, 3, FAKE, 10, None) == -1     # k = 0
+    assert p(ctx.handle, None, FAKE, 2, FAKE, 10, 16, 0, 3, FAKE, 10, None) == -1
+    g = U.lib().ultraep_fold_grads
+    assert g(ctx.handle, FAKE, FAKE, FAKE, 16, 0, 5, None) == -1     # slot_end > R*S
+    assert g(ctx.handle, FAKE, FAKE, FAKE, 16, 2, 1, None) == -1
+    assert g(ctx.handle, FAKE, FAKE, FAKE, -1, 0, 1, None) == -1
+    assert g(ctx.handle, FAKE, None, FAKE, 16, 0, 1, None) == -1
+    assert g(ctx.handle, FAKE, FAKE + 4, FAKE, 16, 0, 1, None) == -2  # pointer table misaligned
+    lay = U.lib().ultraep_dispatch_layout
+    assert lay(ctx.handle, 1, 16, 2, None, FAKE, FAKE, FAKE, None) == -1
+    assert lay(ctx.handle, 1, 16, 2, FAKE + 1, FAKE, FAKE, FAKE, None) == -2
