@@ -66,7 +66,7 @@ extern "C" {
 #define ULTRAEP_MAX_MASTERS 16        /* M = E/R */
 #define ULTRAEP_MAX_SLOTS 8           /* S */
 #define ULTRAEP_MAX_DOMAIN 64         /* D: one rank per lane of a wave64 */
-#define ULTRAEP_MAX_TOTAL_SLOTS 2048  /* R*S */
+#define ULTRAEP_MAX_TOTAL_SLOTS 1024  /* R*S */
 #define ULTRAEP_MAX_TOPK 64           /* k */
 
 typedef struct ultraep_ctx ultraep_ctx;
@@ -89,7 +89,10 @@ typedef struct ultraep_options {
  * redundant slots per rank).
  * Rules: E % R == 0, R % D == 0, 1 <= E <= ULTRAEP_MAX_EXPERTS,
  * E/R <= ULTRAEP_MAX_MASTERS, 0 <= S <= ULTRAEP_MAX_SLOTS,
- * 1 <= D <= ULTRAEP_MAX_DOMAIN, R*S <= ULTRAEP_MAX_TOTAL_SLOTS.
+ * 1 <= D <= ULTRAEP_MAX_DOMAIN, R*S <= ULTRAEP_MAX_TOTAL_SLOTS, and the
+ * per-workgroup tables (E experts, E + R*S instances) must fit one CU's
+ * 160 KiB of LDS, which holds whenever E + R*S <= 1792 (EUNSUPPORTED
+ * otherwise).
  * opt may be NULL (defaults).  *out receives a host object the caller frees
  * with ultraep_destroy.  No HIP call is made. */
 int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
@@ -150,9 +153,9 @@ enum ultraep_header_word {
 int ultraep_plan_field(const ultraep_ctx* ctx, int32_t field, size_t* offset_bytes, size_t* count);
 
 /* Workspace bytes ultraep_balance needs for L layers of R*T*k pairs (per-tile
- * expert histograms, turned into per-tile ordinal bases).  The workspace is
- * scratch: nothing in it must be initialised, and ultraep_balance leaves in
- * it nothing the other calls read. */
+ * expert histograms and per-tile ordinal bases).  The workspace is scratch:
+ * nothing in it must be initialised, and ultraep_balance leaves in it nothing
+ * the other calls read. */
 int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_t k, size_t* out);
 
 /* Balance L layers ([README] Interface, "Forward and backward":
@@ -161,9 +164,15 @@ int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_
  * microseconds works": a quota-driven scheduler right after gating).
  *
  * In:  topk_idx  int32 [L][R*T][k]
+ *      topk_w    fp32  [L][R*T][k] routing weights, or NULL (see layout below)
  * Out: plans     L plan records (ultraep_plan_bytes each)
  *      phys_idx  int32 [L][N]  physical expert of each pair, -1 if dropped
  *      pos       int32 [L][N]  layout row of each pair, -1 if dropped
+ *      inv       int32 [L][N]  optional: inv[pos[n]] = n         } the dispatch
+ *      w_perm    fp32  [L][N]  optional: w_perm[pos[n]] = w[n]   } layout
+ * topk_w, inv and w_perm are given together or all NULL.  Given, the layout
+ * is written by the same kernel that reroutes (rows [0, total) of each layer;
+ * ultraep_dispatch_layout computes the same from pos separately).
  *
  * Per layer:
  *  1. c[e] = number of pairs with id e.
@@ -187,12 +196,14 @@ int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_
  *     o(n) - start_i.  So the layout lists pairs by (physical expert, n).
  * The result is deterministic and identical on every run.
  *
- * Errors: EINVAL for null pointers (when L*N > 0), L < 0, T < 0,
- * k outside [1, min(E, ULTRAEP_MAX_TOPK)]; EUNSUPPORTED when N >= 2^31 or a
- * pointer is not 4-byte aligned; EWORKSPACE when workspace_bytes is short. */
-int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx, int64_t T,
-                    int32_t k, void* workspace, size_t workspace_bytes, void* plans,
-                    int32_t* phys_idx, int32_t* pos, void* stream);
+ * Errors: EINVAL for null pointers (when L*N > 0), only some of topk_w /
+ * inv / w_perm given, L < 0, T < 0, k outside [1, min(E, ULTRAEP_MAX_TOPK)];
+ * EUNSUPPORTED when N >= 2^31 or a pointer is not 4-byte aligned;
+ * EWORKSPACE when workspace_bytes is short. */
+int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
+                    const float* topk_w, int64_t T, int32_t k, void* workspace,
+                    size_t workspace_bytes, void* plans, int32_t* phys_idx, int32_t* pos,
+                    int32_t* inv, float* w_perm, void* stream);
 
 /* Inverse index and permuted routing weights of the dispatch layout
  * ([README] Interface, "Forward and backward": tokens are dispatched to the

@@ -54,7 +54,7 @@ _SIGNATURES = {
     "ultraep_plan_bytes": (_I32, [_P, ctypes.POINTER(_SZ)]),
     "ultraep_plan_field": (_I32, [_P, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "ultraep_workspace_bytes": (_I32, [_P, _I32, _I64, _I32, ctypes.POINTER(_SZ)]),
-    "ultraep_balance": (_I32, [_P, _I32, _P, _I64, _I32, _P, _SZ, _P, _P, _P, _P]),
+    "ultraep_balance": (_I32, [_P, _I32, _P, _P, _I64, _I32, _P, _SZ, _P, _P, _P, _P, _P, _P]),
     "ultraep_dispatch_layout": (_I32, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P]),
     "ultraep_permute": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _I32, _I32, _P, _I64, _P]),
     "ultraep_fold_grads": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _P]),
@@ -147,13 +147,15 @@ def ultraep_create(E: int, R: int, slots_per_rank: int, D: int, eps=(1, 100),
 
 
 def ultraep_balance(ctx: Context, topk_idx, T: int, k: int, workspace, plans, phys_idx, pos,
-                    L: Optional[int] = None, stream=None) -> None:
-    """Count, plan and reroute L layers (topk_idx int32 [L, R*T, k] or [R*T, k])."""
+                    topk_w=None, inv=None, w_perm=None, L: Optional[int] = None, stream=None) -> None:
+    """Count, plan and reroute L layers (topk_idx int32 [L, R*T, k] or [R*T, k]).
+
+    With topk_w, inv and w_perm the dispatch layout is written in the same pass."""
     if L is None:
         L = topk_idx.shape[0] if topk_idx.dim() == 3 else 1
-    st = lib().ultraep_balance(ctx.handle, L, _ptr(topk_idx), T, k, _ptr(workspace),
+    st = lib().ultraep_balance(ctx.handle, L, _ptr(topk_idx), _ptr(topk_w), T, k, _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _ptr(plans),
-                               _ptr(phys_idx), _ptr(pos), _stream(stream))
+                               _ptr(phys_idx), _ptr(pos), _ptr(inv), _ptr(w_perm), _stream(stream))
     _check("ultraep_balance", st)
 
 

@@ -96,7 +96,7 @@ int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
   sh.eps_den = o.eps_den;
   sh.allow_zero = o.allow_zero_master;
   build_layout(&sh);
-  if (ultraep::plan_lds_bytes(sh) > 160 * 1024) {
+  if (ultraep::plan_lds_bytes(sh) > 160 * 1024 || ultraep::rerouting_lds_bytes(sh, true) > 160 * 1024) {
     delete c;
     return ULTRAEP_EUNSUPPORTED;
   }
@@ -129,14 +129,15 @@ int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_
   const int st = pairs_per_layer(ctx, T, k, &N);
   if (st != ULTRAEP_OK) return st;
   const size_t ntiles = static_cast<size_t>(ultraep::ntiles_of(N));
-  *out = sizeof(int32_t) * static_cast<size_t>(L) * ntiles * static_cast<size_t>(ctx->sh.E);
+  *out = 2 * sizeof(int32_t) * static_cast<size_t>(L) * ntiles * static_cast<size_t>(ctx->sh.E);
   if (*out == 0) *out = 256;
   return ULTRAEP_OK;
 }
 
-int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx, int64_t T,
-                    int32_t k, void* workspace, size_t workspace_bytes, void* plans,
-                    int32_t* phys_idx, int32_t* pos, void* stream) {
+int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
+                    const float* topk_w, int64_t T, int32_t k, void* workspace,
+                    size_t workspace_bytes, void* plans, int32_t* phys_idx, int32_t* pos,
+                    int32_t* inv, float* w_perm, void* stream) {
   if (!ctx || L < 0) return ULTRAEP_EINVAL;
   int32_t N = 0;
   int st = pairs_per_layer(ctx, T, k, &N);
@@ -144,15 +145,19 @@ int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx, 
   if (L == 0) return ULTRAEP_OK;
   if (!plans || !workspace) return ULTRAEP_EINVAL;
   if (N > 0 && (!topk_idx || !phys_idx || !pos)) return ULTRAEP_EINVAL;
+  const bool layout = inv || w_perm || topk_w;
+  if (layout && N > 0 && (!inv || !w_perm || !topk_w)) return ULTRAEP_EINVAL;
   if (!aligned(topk_idx, 4) || !aligned(phys_idx, 4) || !aligned(pos, 4) || !aligned(plans, 4) ||
-      !aligned(workspace, 4))
+      !aligned(workspace, 4) || !aligned(topk_w, 4) || !aligned(inv, 4) || !aligned(w_perm, 4))
     return ULTRAEP_EUNSUPPORTED;
   size_t need = 0;
   st = ultraep_workspace_bytes(ctx, L, T, k, &need);
   if (st != ULTRAEP_OK) return st;
   if (workspace_bytes < need) return ULTRAEP_EWORKSPACE;
-  return from_hip(ultraep::launch_balance(ctx->sh, L, topk_idx, N, static_cast<int32_t*>(workspace),
+  return from_hip(ultraep::launch_balance(ctx->sh, L, topk_idx, topk_w, N,
+                                          static_cast<int32_t*>(workspace),
                                           static_cast<int32_t*>(plans), phys_idx, pos,
+                                          layout ? inv : nullptr, w_perm,
                                           static_cast<hipStream_t>(stream)));
 }
 

@@ -36,9 +36,11 @@ struct Shape {
 inline int64_t ntiles_of(int64_t N) { return (N + kTile - 1) / kTile; }
 
 // Launchers.  All work is queued on `st`; none of them synchronises.
-hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, int32_t N,
-                          int32_t* tile_hist, int32_t* plans, int32_t* phys_idx, int32_t* pos,
-                          hipStream_t st);
+// ws: 2*L*ntiles*E int32 (tile histograms, tile ordinal bases).  With inv
+// non-null the dispatch layout (inv, w_perm from w) is written too.
+hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const float* w,
+                          int32_t N, int32_t* ws, int32_t* plans, int32_t* phys_idx, int32_t* pos,
+                          int32_t* inv, float* w_perm, hipStream_t st);
 hipError_t launch_layout(int32_t L, int32_t N, const int32_t* pos, const float* w,
                          int32_t* inv, float* w_perm, hipStream_t st);
 hipError_t launch_permute(const Shape& sh, const int32_t* plan, const int32_t* inv, int32_t k,
@@ -49,7 +51,8 @@ hipError_t launch_fold(const Shape& sh, const int32_t* plan, float* const* maste
                        const float* reps, int64_t numel, int32_t slot_begin, int32_t slot_end,
                        hipStream_t st);
 
-// Bytes of dynamic LDS the plan solver needs for this shape.
+// Bytes of dynamic LDS the plan solver / reroute kernel need for this shape.
 size_t plan_lds_bytes(const Shape& sh);
+size_t rerouting_lds_bytes(const Shape& sh, bool layout);
 
 }  // namespace ultraep

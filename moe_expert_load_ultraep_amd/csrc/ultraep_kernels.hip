@@ -70,55 +70,103 @@ __device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Lanes of the wave holding the same value v (v < 2^nbits).  Every lane must
-// be active: the complement of a ballot is taken over all 64 lanes.
-__device__ __forceinline__ uint64_t match_peers(uint32_t v, int nbits) {
-  uint64_t peers = ~0ull;
-  for (int b = 0; b < nbits; ++b) {
-    const bool bit = (v >> b) & 1u;
-    const uint64_t bb = ballot(bit);
-    peers &= bit ? bb : ~bb;
+// Lanes of the wave holding the same value v: every lane ORs its lane bit
+// into an LDS word owned by its value, then reads the word back.  LDS
+// operations of one wave complete in program order, so the read sees all of
+// this instruction's ORs; the caller clears the word (one lane per group)
+// before the next use.  Every lane must be active.
+__device__ __forceinline__ uint64_t match_peers_lds(unsigned long long* words, uint32_t v,
+                                                    int lane) {
+  atomicOr(&words[v], 1ull << lane);
+  return __atomic_load_n(&words[v], __ATOMIC_RELAXED);
+}
+
+// Expert ids of one wave's stretch of a tile: chunk c, lane l holds pair
+// base + 64c + l.  Every load is issued unconditionally (indices past the
+// tile are clamped to its last pair and masked afterwards) so all kChunks
+// loads are in flight together instead of one round trip per chunk.  Ids
+// outside [0, E) and padding become E.
+__device__ __forceinline__ void load_tile_ids(const int32_t* __restrict__ src, int base,
+                                              int n_here, int lane, int32_t E,
+                                              uint32_t (&v)[kChunks]) {
+  const int last = n_here - 1;
+  int32_t raw[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    raw[c] = __builtin_nontemporal_load(src + min(base + c * 64 + lane, last));
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t x = static_cast<uint32_t>(raw[c]);
+    v[c] = (base + c * 64 + lane < n_here && x < static_cast<uint32_t>(E)) ? x
+                                                                           : static_cast<uint32_t>(E);
   }
-  return peers;
+}
+
+// Exclusive scan of a[0..n) in LDS by a workgroup of NT threads; a[n]
+// receives the total.  tmp holds NT/64 + 1 words.  Wave-level scans use
+// cross-lane shuffles, so only two barriers are needed.
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+template <int NT>
+__device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
+  constexpr int W = NT / 64;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int per = (n + NT - 1) / NT;
+  const int b = min(tid * per, n), en = min(b + per, n);
+  int32_t s = 0;
+  for (int i = b; i < en; ++i) s += a[i];
+  const int32_t inc = wave_inclusive_scan(s);
+  if (lane == 63) tmp[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int32_t t = lane < W ? tmp[lane] : 0;
+    const int32_t ti = wave_inclusive_scan(t);
+    if (lane < W) tmp[lane] = ti - t;
+    if (lane == W - 1) tmp[W] = ti;
+  }
+  __syncthreads();
+  int32_t run = tmp[wave] + inc - s;
+  for (int i = b; i < en; ++i) {
+    const int32_t v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (tid == 0) a[n] = tmp[W];
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------------
 // count: per-tile expert histogram ([README] intro: exact post-gating load)
 // ------------------------------------------------------------------------
-// One workgroup per (layer, tile of kTile pairs).  Each wave takes a
-// contiguous 2048-pair stretch, loads it 64 pairs at a time with dword loads
-// (256 B per wave instruction), groups equal expert ids with ballots and lets
-// one lane per group add the group size to an LDS counter, so a hot expert
-// costs one LDS atomic per wave instruction instead of one per pair.
+// One workgroup per (layer, tile of kTile pairs).  Each wave loads its
+// 2048-pair stretch with all loads in flight at once and adds each valid id
+// to an LDS counter.  The order of the additions does not matter here, so a
+// plain LDS atomic per pair is the cheapest form: equal ids in one wave
+// instruction only serialise inside the LDS, they cost no VALU work.
 __global__ __launch_bounds__(kTileThreads) void count_kernel(
-    const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles, int32_t nbits,
+    const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles,
     int32_t* __restrict__ hist) {
-  extern __shared__ int32_t s_cnt[];
+  extern __shared__ __align__(16) int32_t s_cnt[];
   const int64_t blk = blockIdx.x;
   const int32_t layer = static_cast<int32_t>(blk / ntiles);
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
   for (int i = threadIdx.x; i < E; i += kTileThreads) s_cnt[i] = 0;
-  __syncthreads();
-
   const int32_t* src = idx + static_cast<int64_t>(layer) * N + static_cast<int64_t>(tile) * kTile;
   const int n_here = min(kTile, N - tile * kTile);
-  const int lane = lane_id();
-  const int base = (threadIdx.x >> 6) * kWavePairs;
-
   uint32_t v[kChunks];
+  load_tile_ids(src, (threadIdx.x >> 6) * kWavePairs, n_here, lane_id(), E, v);
+  __syncthreads();
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const int i = base + c * 64 + lane;
-    const uint32_t x = (i < n_here) ? static_cast<uint32_t>(__builtin_nontemporal_load(src + i))
-                                    : static_cast<uint32_t>(E);
-    v[c] = x < static_cast<uint32_t>(E) ? x : static_cast<uint32_t>(E);
-  }
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const uint64_t peers = match_peers(v[c], nbits);
-    if (lane == lowest_lane(peers) && v[c] < static_cast<uint32_t>(E))
-      atomicAdd(&s_cnt[v[c]], __builtin_popcountll(peers));
-  }
+  for (int c = 0; c < kChunks; ++c)
+    if (v[c] < static_cast<uint32_t>(E)) atomicAdd(&s_cnt[v[c]], 1);
   __syncthreads();
   int32_t* dst = hist + (static_cast<int64_t>(layer) * ntiles + tile) * E;
   for (int i = threadIdx.x; i < E; i += kTileThreads) dst[i] = s_cnt[i];
@@ -133,6 +181,8 @@ struct PlanParams {
   int32_t eps_num, eps_den, allow_zero;
   int32_t rec_words;
   int32_t G, items;  // grid quotas per probe round, (quota, domain) items per round
+  int32_t scan_wgs;  // workgroups per layer that build the tile ordinal bases
+  int32_t scan_ew;   // experts per scan workgroup
   int32_t off[ULTRAEP_PLAN_NUM_FIELDS];
   int32_t len[ULTRAEP_PLAN_NUM_FIELDS];
 };
@@ -150,22 +200,27 @@ struct PlanLds {
   int32_t* ok;     // [items]
   int32_t* res;    // [2][items][D*S]  hosted expert, then its quota
   int32_t* mq;     // [E]
-  int32_t* nrep;   // [E]
+  unsigned long long* rmask;  // [E] domain ranks (bit r % D) holding a replica of e
   int32_t* iptr;   // [E+1]
   int32_t* pload;  // [P+1]
   int32_t* slotE;  // [R*S]
   int32_t* slotQ;  // [R*S]
 };
 
+// The scan workgroups use only the first kPlanThreads words of the same
+// allocation.
 __host__ __device__ inline size_t plan_lds_words(int E, int R, int S, int D, int P, int ndom,
                                                  int items) {
   return static_cast<size_t>(E) + R + kPlanThreads + ndom + kScalars + items +
-         2ull * items * D * S + E + E + (E + 1) + (P + 1) + 2ull * R * S;
+         2ull * items * D * S + E + 2ull * E + (E + 1) + (P + 1) + 2ull * R * S;
 }
 
 __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
   PlanLds L;
   int32_t* p = lds;
+  // 64-bit words first: the allocation is 16-byte aligned, so they are
+  // naturally aligned for the 64-bit LDS atomics
+  L.rmask = reinterpret_cast<unsigned long long*>(p); p += 2 * a.E;
   L.c = p; p += a.E;
   L.H = p; p += a.R;
   L.part = p; p += kPlanThreads;
@@ -174,38 +229,11 @@ __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
   L.ok = p; p += a.items;
   L.res = p; p += 2 * a.items * a.D * a.S;
   L.mq = p; p += a.E;
-  L.nrep = p; p += a.E;
   L.iptr = p; p += a.E + 1;
   L.pload = p; p += a.P + 1;
   L.slotE = p; p += a.R * a.S;
   L.slotQ = p;
   return L;
-}
-
-// In-place exclusive scan of a[0..n) in LDS by the whole workgroup; a[n]
-// receives the total.  tmp holds kPlanThreads words.
-__device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
-  const int tid = threadIdx.x;
-  const int per = (n + kPlanThreads - 1) / kPlanThreads;
-  const int b = min(tid * per, n), en = min(b + per, n);
-  int s = 0;
-  for (int i = b; i < en; ++i) s += a[i];
-  tmp[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < kPlanThreads; o <<= 1) {
-    const int v = tid >= o ? tmp[tid - o] : 0;
-    __syncthreads();
-    tmp[tid] += v;
-    __syncthreads();
-  }
-  int run = tmp[tid] - s;
-  for (int i = b; i < en; ++i) {
-    const int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  if (tid == kPlanThreads - 1) a[n] = tmp[kPlanThreads - 1];
-  __syncthreads();
 }
 
 // One feasibility probe: can domain d be brought to at most Q with the
@@ -327,21 +355,11 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
     for (int s = 0; s < SMAX; ++s) hosts |= (he[s] == e);
     const bool elig = act && lane != owner && freeslots > 0 && !hosts;
 
-    // fit: least spare that takes the whole piece
+    // fit (least spare that takes the whole piece), roomiest receiver and
+    // donor (largest queued piece on an eligible rank with room left) are
+    // independent reductions, issued together so their latencies overlap
     const uint32_t fitv = (elig && spare >= amt) ? static_cast<uint32_t>(spare) : 0xFFFFFFFFu;
-    const uint32_t fmin = wave_min(fitv);
-    if (fmin != 0xFFFFFFFFu) {
-      const int rr = lowest_lane(ballot(fitv == fmin));
-      if (lane == rr) {
-        place(e, amt);
-        spare -= amt;
-      }
-      continue;
-    }
-    // roomiest receiver
     const uint32_t recv = (elig && spare > 0) ? static_cast<uint32_t>(spare) : 0u;
-    const uint32_t rmax = wave_max(recv);
-    // donor: largest queued piece on an eligible rank with room left
     uint32_t dbest = 0;
     int dj = 0;
     if (elig) {
@@ -352,7 +370,17 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
           dj = j;
         }
     }
+    const uint32_t fmin = wave_min(fitv);
+    const uint32_t rmax = wave_max(recv);
     const uint32_t dmax = wave_max(dbest);
+    if (fmin != 0xFFFFFFFFu) {
+      const int rr = lowest_lane(ballot(fitv == fmin));
+      if (lane == rr) {
+        place(e, amt);
+        spare -= amt;
+      }
+      continue;
+    }
     if (dmax > 0) {
       const int dl = lowest_lane(ballot(dbest == dmax));
       const int djs = static_cast<int>(readlane(static_cast<uint32_t>(dj), dl));
@@ -413,50 +441,104 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
   return true;
 }
 
+// Tile ordinal bases for the experts [e0, e0 + ew) of one layer: base[t][e]
+// = number of pairs of e in tiles before t.  Thread (el, ch) sums a
+// contiguous run of tiles of one expert, the runs are scanned in LDS, and the
+// run is re-read and written out as running prefixes.  Loads go in batches
+// of 16 with clamped indices so each batch is one round trip.
+__device__ void tile_base_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base,
+                               int32_t ntiles, int32_t E, int32_t e0, int32_t ew, int32_t* part) {
+  constexpr int B = 16;
+  const int tid = threadIdx.x;
+  const int nch = kPlanThreads / ew;
+  const int el = tid % ew, ch = tid / ew;
+  const bool act = ch < nch && e0 + el < E && ntiles > 0;
+  const int clen = (ntiles + nch - 1) / nch;
+  const int t0 = min(ch * clen, ntiles), t1 = min(t0 + clen, ntiles);
+  const int e = e0 + el;
+  int32_t sum = 0;
+  if (act) {
+    for (int tb = t0; tb < t1; tb += B) {
+      int32_t x[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * E + e];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (tb + u < t1) sum += x[u];
+    }
+  }
+  part[tid] = sum;
+  __syncthreads();
+  if (act) {
+    int32_t run = 0;
+    for (int q = 0; q < ch; ++q) run += part[q * ew + el];
+    for (int tb = t0; tb < t1; tb += B) {
+      int32_t x[B];
+#pragma unroll
+      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * E + e];
+#pragma unroll
+      for (int u = 0; u < B; ++u)
+        if (tb + u < t1) {
+          base[static_cast<int64_t>(tb + u) * E + e] = run;
+          run += x[u];
+        }
+    }
+  }
+}
+
+// One launch per batch of layers: workgroup 0 of each layer's group solves
+// the plan; the other scan_wgs workgroups build the tile ordinal bases the
+// reroute kernel needs, on other CUs, while the plan is being solved.
 template <int MMAX, int SMAX>
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(int32_t* __restrict__ hist,
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ hist,
+                                                            int32_t* __restrict__ tile_base,
                                                             int32_t* __restrict__ plans,
                                                             PlanParams a) {
-  extern __shared__ int32_t lds[];
+  extern __shared__ __align__(16) int32_t lds[];
+  const int group = 1 + a.scan_wgs;
+  const int layer = blockIdx.x / group;
+  const int role = blockIdx.x % group;
+  const int E = a.E, R = a.R, S = a.S, D = a.D, M = a.M, P = a.P;
+  const int32_t* H = hist + static_cast<int64_t>(layer) * a.ntiles * E;
+  if (role > 0) {
+    const int e0 = (role - 1) * a.scan_ew;
+    tile_base_scan(H, tile_base + static_cast<int64_t>(layer) * a.ntiles * E, a.ntiles, E, e0,
+                   a.scan_ew, lds);
+    return;
+  }
   const PlanLds L = carve(lds, a);
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = lane_id();
-  const int layer = blockIdx.x;
-  const int E = a.E, R = a.R, S = a.S, D = a.D, M = a.M, P = a.P;
-  int32_t* H = hist + static_cast<int64_t>(layer) * a.ntiles * E;
   int32_t* rec = plans + static_cast<int64_t>(layer) * a.rec_words;
 
   if (tid < kScalars) L.scal[tid] = 0;
   for (int d = tid; d < a.ndom; d += kPlanThreads) L.dom[d] = 0;
 
-  // -- phase 0: per-expert exclusive prefix over tiles (in place) and totals.
+  // -- phase 0: pairs per expert = sum of the tile histograms.  Thread
+  // (e, ch) takes tiles ch, ch + nch, ... so each batch of loads reads whole
+  // histogram rows; batches of 32 loads are issued before any is used.
   {
+    constexpr int B = 32;
     const int nch = kPlanThreads / E;
-    const int clen = (a.ntiles + nch - 1) / nch;
     const int e = tid % E, ch = tid / E;
-    const bool act = ch < nch;
-    const int t0 = min(ch * clen, a.ntiles), t1 = min(t0 + clen, a.ntiles);
     int32_t sum = 0;
-    if (act) {
-#pragma unroll 8
-      for (int t = t0; t < t1; ++t) sum += H[static_cast<int64_t>(t) * E + e];
+    if (ch < nch && a.ntiles > 0) {
+      for (int tb = ch; tb < a.ntiles; tb += B * nch) {
+        int32_t x[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          x[u] = H[static_cast<int64_t>(min(tb + u * nch, a.ntiles - 1)) * E + e];
+#pragma unroll
+        for (int u = 0; u < B; ++u)
+          if (tb + u * nch < a.ntiles) sum += x[u];
+      }
     }
     L.part[tid] = sum;
     __syncthreads();
-    int32_t base = 0;
-    if (act) {
-      for (int q = 0; q < ch; ++q) base += L.part[q * E + e];
-      if (ch == nch - 1) L.c[e] = base + sum;
-    }
-    if (act) {
-      int32_t run = base;
-#pragma unroll 8
-      for (int t = t0; t < t1; ++t) {
-        const int64_t k = static_cast<int64_t>(t) * E + e;
-        const int32_t v = H[k];
-        H[k] = run;
-        run += v;
-      }
+    if (ch == 0) {
+      int32_t c = 0;
+      for (int q = 0; q < nch; ++q) c += L.part[q * E + e];
+      L.c[e] = c;
     }
     __syncthreads();
   }
@@ -534,14 +616,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int32_t* __restrict_
   }
   for (int e = tid; e < E; e += kPlanThreads) {
     L.mq[e] = L.c[e];
-    L.nrep[e] = 1;
+    L.rmask[e] = 0;
   }
   __syncthreads();
   for (int s = tid; s < R * S; s += kPlanThreads) {
     const int32_t e = L.slotE[s];
     if (e >= 0) {
       atomicSub(&L.mq[e], L.slotQ[s]);
-      atomicAdd(&L.nrep[e], 1);
+      atomicOr(&L.rmask[e], 1ull << ((s / S) % D));
       atomicAdd(&L.scal[kReplicas], 1);
     }
   }
@@ -550,7 +632,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int32_t* __restrict_
     const int r = p / (M + S), j = p % (M + S);
     L.pload[p] = j < M ? L.mq[r * M + j] : L.slotQ[r * S + (j - M)];
   }
-  for (int e = tid; e < E; e += kPlanThreads) L.iptr[e] = L.nrep[e];
+  for (int e = tid; e < E; e += kPlanThreads) L.iptr[e] = 1 + __builtin_popcountll(L.rmask[e]);
   __syncthreads();
   // record the loads before the scans overwrite them
   for (int p = tid; p < P; p += kPlanThreads) rec[a.off[ULTRAEP_PLAN_PHYS_LOAD] + p] = L.pload[p];
@@ -561,37 +643,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int32_t* __restrict_
     rec[a.off[ULTRAEP_PLAN_RANK_BEFORE] + r] = L.H[r];
   }
   __syncthreads();
-  block_exclusive_scan(L.pload, P, L.part);  // pload -> phys_off
-  block_exclusive_scan(L.iptr, E, L.part);   // instance counts -> inst_ptr
+  block_exclusive_scan<kPlanThreads>(L.pload, P, L.part);  // pload -> phys_off
+  block_exclusive_scan<kPlanThreads>(L.iptr, E, L.part);   // instance counts -> inst_ptr
 
+  // instances of e in ascending physical id = ascending rank inside e's
+  // domain: walk the set bits of e's rank mask (its replicas and its home)
   int32_t* inst_phys = rec + a.off[ULTRAEP_PLAN_INST_PHYS];
   int32_t* inst_end = rec + a.off[ULTRAEP_PLAN_INST_END];
   int32_t* inst_base = rec + a.off[ULTRAEP_PLAN_INST_BASE];
   for (int e = tid; e < E; e += kPlanThreads) {
     const int home = e / M, d = home / D;
+    const uint64_t in_domain = D == 64 ? ~0ull : ((1ull << D) - 1);
+    uint64_t m = (L.rmask[e] | (1ull << (home % D))) & in_domain;
     int i = L.iptr[e];
     int32_t end = 0;
-    for (int r = d * D; r < (d + 1) * D; ++r) {
-      if (r == home) {
-        const int p = home * (M + S) + e % M;
-        const int32_t q = L.mq[e];
-        end += q;
-        inst_phys[i] = p;
-        inst_end[i] = end;
-        inst_base[i] = L.pload[p] - (end - q);
-        ++i;
+    while (m) {
+      const int r = d * D + __builtin_ctzll(m);
+      m &= m - 1;
+      int p = home * (M + S) + e % M;
+      int32_t q = L.mq[e];
+      if (r != home) {
+        for (int j = 0; j < S; ++j)
+          if (L.slotE[r * S + j] == e) {
+            p = r * (M + S) + M + j;
+            q = L.slotQ[r * S + j];
+          }
       }
-      for (int j = 0; j < S; ++j) {
-        if (L.slotE[r * S + j] == e) {
-          const int p = r * (M + S) + M + j;
-          const int32_t q = L.slotQ[r * S + j];
-          end += q;
-          inst_phys[i] = p;
-          inst_end[i] = end;
-          inst_base[i] = L.pload[p] - (end - q);
-          ++i;
-        }
-      }
+      end += q;
+      inst_phys[i] = p;
+      inst_end[i] = end;
+      inst_base[i] = L.pload[p] - (end - q);
+      ++i;
     }
   }
   // unused instance entries and the padding between fields get fixed values,
@@ -648,87 +730,201 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(int32_t* __restrict_
 // "Forward and backward": reroute expands logical routing to replicas)
 // ------------------------------------------------------------------------
 // Same tiling as count.  A pair's ordinal among its expert's pairs is the
-// tile's base (from the plan kernel's scan) + the pairs of earlier waves in
-// the tile + the pair's rank inside its wave, which the wave tracks with
-// ballot groups and per-wave LDS counters, so no sort is needed and the
+// tile's base (from the plan launch's scan workgroups) + the pairs of earlier
+// waves in the tile + the pair's rank inside its wave, which the wave tracks
+// with ballot groups and per-wave LDS counters, so no sort is needed and the
 // result does not depend on scheduling.
-__global__ __launch_bounds__(kTileThreads) void reroute_kernel(
-    const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles, int32_t nbits,
-    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans, int32_t rec_words,
-    int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase, int32_t n_inst,
-    int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos) {
-  extern __shared__ int32_t lds[];
-  int32_t* cntw = lds;                 // [4][E]
-  int32_t* iptr = cntw + 4 * E;        // [E+1]
-  int32_t* iend = iptr + E + 1;        // [n_inst]
-  int32_t* iphys = iend + n_inst;      // [n_inst]
-  int32_t* ibase = iphys + n_inst;     // [n_inst]
+//
+// With LAYOUT the kernel also writes the inverse index and permuted weights.
+// Inside one tile, the pairs that land on one instance have consecutive
+// ordinals, so they fill one contiguous run of layout rows.  Each pair is
+// first placed at its run's slot in LDS; the runs are then written out with
+// consecutive lanes on consecutive rows, instead of one 4-byte scatter per
+// pair.
+struct RerouteLds {
+  unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids
+  int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
+  int32_t* tcnt;   // [E] pairs of each expert in the tile
+  int32_t* kfirst; // [E] first instance of e that holds ordinals of this tile
+  int32_t* iptr;   // [E+1]
+  int32_t* iend;   // [n_inst]
+  int32_t* iphys;  // [n_inst]
+  int32_t* ibase;  // [n_inst]
+  int32_t* roff;   // [n_inst+1] run offsets inside the tile's staging area
+  int32_t* ro0;    // [n_inst] first ordinal of the run
+  int32_t* tmp;    // [kTileThreads/64 + 1]
+  float* wt;       // [kTile] the tile's routing weights, in pair order
+  uint32_t* sp;    // [kTile] staged slot: run index << 16 | pair index inside the tile
+};
 
+constexpr int kTileWaves = kTileThreads / 64;
+
+__host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layout) {
+  size_t words = 2ull * kTileWaves * (E + 1) + static_cast<size_t>(kTileWaves) * E + 2ull * E +
+                 (E + 1) + 3ull * n_inst;
+  if (layout) words += (n_inst + 1) + n_inst + (kTileWaves + 1) + 2ull * kTile;
+  return 4 * words;
+}
+
+template <bool LAYOUT>
+__global__ __launch_bounds__(kTileThreads) void reroute_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t E,
+    int32_t ntiles, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans,
+    int32_t rec_words, int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase,
+    int32_t n_inst, int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos,
+    int32_t* __restrict__ inv, float* __restrict__ w_perm) {
+  extern __shared__ __align__(16) int32_t lds[];
+  RerouteLds S;
+  {
+    int32_t* q = lds;
+    S.peers = reinterpret_cast<unsigned long long*>(q); q += 2 * kTileWaves * (E + 1);
+    S.cntw = q; q += kTileWaves * E;
+    S.tcnt = q; q += E;
+    S.kfirst = q; q += E;
+    S.iptr = q; q += E + 1;
+    S.iend = q; q += n_inst;
+    S.iphys = q; q += n_inst;
+    S.ibase = q; q += n_inst;
+    if (LAYOUT) {
+      S.roff = q; q += n_inst + 1;
+      S.ro0 = q; q += n_inst;
+      S.tmp = q; q += kTileWaves + 1;
+      S.wt = reinterpret_cast<float*>(q); q += kTile;
+      S.sp = reinterpret_cast<uint32_t*>(q);
+    }
+  }
   const int64_t blk = blockIdx.x;
   const int32_t layer = static_cast<int32_t>(blk / ntiles);
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
   const int32_t* plan = plans + static_cast<int64_t>(layer) * rec_words;
-  for (int i = threadIdx.x; i < 4 * E; i += kTileThreads) cntw[i] = 0;
-  for (int i = threadIdx.x; i <= E; i += kTileThreads) iptr[i] = plan[off_iptr + i];
-  for (int i = threadIdx.x; i < n_inst; i += kTileThreads) {
-    iend[i] = plan[off_iend + i];
-    iphys[i] = plan[off_iphys + i];
-    ibase[i] = plan[off_ibase + i];
-  }
-  __syncthreads();
-
-  const int64_t first = static_cast<int64_t>(layer) * N + static_cast<int64_t>(tile) * kTile;
+  const int64_t lb = static_cast<int64_t>(layer) * N;
+  const int64_t first = lb + static_cast<int64_t>(tile) * kTile;
   const int n_here = min(kTile, N - tile * kTile);
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int base = wave * kWavePairs;
-  int32_t* my = cntw + wave * E;
 
   uint32_t v[kChunks];
+  load_tile_ids(idx + first, base, n_here, lane, E, v);
+  if (LAYOUT) {
+    constexpr int kPer = kTile / kTileThreads;
+    float x[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      x[u] = __builtin_nontemporal_load(
+          w + first + min(u * kTileThreads + static_cast<int>(threadIdx.x), n_here - 1));
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) S.wt[u * kTileThreads + threadIdx.x] = x[u];
+  }
+  for (int i = threadIdx.x; i < kTileWaves * (E + 1); i += kTileThreads) S.peers[i] = 0;
+  for (int i = threadIdx.x; i < kTileWaves * E; i += kTileThreads) S.cntw[i] = 0;
+  for (int i = threadIdx.x; i <= E; i += kTileThreads) S.iptr[i] = plan[off_iptr + i];
+  for (int i = threadIdx.x; i < n_inst; i += kTileThreads) {
+    S.iend[i] = plan[off_iend + i];
+    S.iphys[i] = plan[off_iphys + i];
+    S.ibase[i] = plan[off_ibase + i];
+  }
+  __syncthreads();
+
+  // pass 1: rank of each pair among the wave's earlier pairs of its expert
+  int32_t* my = S.cntw + wave * E;
+  unsigned long long* mw = S.peers + wave * (E + 1);
   int32_t lr[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const int i = base + c * 64 + lane;
-    const uint32_t x = (i < n_here) ? static_cast<uint32_t>(__builtin_nontemporal_load(idx + first + i))
-                                    : static_cast<uint32_t>(E);
-    v[c] = x < static_cast<uint32_t>(E) ? x : static_cast<uint32_t>(E);
-  }
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const uint64_t peers = match_peers(v[c], nbits);
+    const uint64_t peers = match_peers_lds(mw, v[c], lane);
     const bool valid = v[c] < static_cast<uint32_t>(E);
     const int32_t old = valid ? my[v[c]] : 0;
-    if (valid && lane == lowest_lane(peers)) my[v[c]] = old + __builtin_popcountll(peers);
+    if (lane == lowest_lane(peers)) {
+      if (valid) my[v[c]] = old + __builtin_popcountll(peers);
+      mw[v[c]] = 0;
+    }
     lr[c] = old + count_below(peers);
   }
   __syncthreads();
   const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
   for (int e = threadIdx.x; e < E; e += kTileThreads) {
-    int32_t run = tb[e];
+    const int32_t b0 = tb[e];
+    int32_t run = b0;
 #pragma unroll
-    for (int w = 0; w < kTileThreads / 64; ++w) {
-      const int32_t t = cntw[w * E + e];
-      cntw[w * E + e] = run;
+    for (int q = 0; q < kTileWaves; ++q) {
+      const int32_t t = S.cntw[q * E + e];
+      S.cntw[q * E + e] = run;
       run += t;
     }
+    S.tcnt[e] = run - b0;
+    // the tile's ordinals of e start in this instance; a pair's instance is
+    // then at most a few steps further
+    int k = S.iptr[e];
+    const int last = S.iptr[e + 1] - 1;
+    while (k < last && b0 >= S.iend[k]) ++k;
+    S.kfirst[e] = k;
   }
   __syncthreads();
+
+  if (LAYOUT) {
+    // runs: instance i of expert e holds the tile's ordinals
+    // [max(start_i, b), min(end_i, b + count)) where b is the tile base of e
+    for (int e = threadIdx.x; e < E; e += kTileThreads) {
+      const int32_t b0 = S.cntw[e], b1 = b0 + S.tcnt[e];
+      int32_t start = 0;
+      for (int i = S.iptr[e]; i < S.iptr[e + 1]; ++i) {
+        const int32_t end = S.iend[i];
+        const int32_t lo = max(start, b0), hi = min(end, b1);
+        S.roff[i] = max(0, hi - lo);
+        S.ro0[i] = lo;
+        start = end;
+      }
+    }
+    // instance entries beyond the plan's used ones are empty runs
+    for (int i = S.iptr[E] + threadIdx.x; i < n_inst; i += kTileThreads) {
+      S.roff[i] = 0;
+      S.ro0[i] = 0;
+    }
+    __syncthreads();
+    block_exclusive_scan<kTileThreads>(S.roff, n_inst, S.tmp);
+  }
+
+  // pass 2: instance, physical expert and layout row of each pair
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int i = base + c * 64 + lane;
-    if (i >= n_here) continue;
     int32_t p = -1, row = -1;
     if (v[c] < static_cast<uint32_t>(E)) {
       const int e = static_cast<int>(v[c]);
       const int32_t o = my[e] + lr[c];
-      int k = iptr[e];
-      const int last = iptr[e + 1] - 1;
-      while (k < last && o >= iend[k]) ++k;
-      p = iphys[k];
-      row = ibase[k] + o;
+      int k = S.kfirst[e];
+      const int last = S.iptr[e + 1] - 1;
+      while (k < last && o >= S.iend[k]) ++k;
+      p = S.iphys[k];
+      row = S.ibase[k] + o;
+      if (LAYOUT) {
+        const int32_t sl = S.roff[k] + (o - S.ro0[k]);
+        if (sl >= 0 && sl < kTile) S.sp[sl] = (static_cast<uint32_t>(k) << 16) | static_cast<uint32_t>(i);
+      }
     }
-    phys_idx[first + i] = p;
-    pos[first + i] = row;
+    if (i < n_here) {
+      phys_idx[first + i] = p;
+      pos[first + i] = row;
+    }
+  }
+  if (LAYOUT) {
+    __syncthreads();
+    // write the staged slots in order: consecutive threads take consecutive
+    // slots, which are consecutive layout rows inside each run.  A tile holds
+    // at most n_here valid pairs; the clamp and the row check only matter for
+    // a corrupted plan record.
+    const int nt = min(S.roff[n_inst], n_here);
+    const int32_t tile0 = tile * kTile;
+    for (int j = threadIdx.x; j < nt; j += kTileThreads) {
+      const uint32_t sp = S.sp[j];
+      const int r = static_cast<int>(sp >> 16), n = static_cast<int>(sp & 0xFFFFu);
+      const int32_t row = S.ibase[r] + S.ro0[r] + (j - S.roff[r]);
+      if (r < n_inst && row >= 0 && row < N && n < n_here) {
+        inv[lb + row] = tile0 + n;
+        w_perm[lb + row] = S.wt[n];
+      }
+    }
   }
 }
 
@@ -756,13 +952,30 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
 // ------------------------------------------------------------------------
 // permute: bf16 rows into the layout order
 // ------------------------------------------------------------------------
-// One wave per output row: the row index and its source token are wave
-// uniform, and the row moves as 16-byte vectors, 1 KiB per wave
-// instruction.  Up to 8 vectors per lane are loaded before any is stored so
-// enough bytes are in flight per CU; stores are non-temporal because the
-// layout is consumed by the next kernel, not re-read here.
+// Each wave copies blocks of kPermRows consecutive rows: one lane-parallel
+// load fetches the block's inverse-index entries, then the rows are moved two
+// at a time as 16-byte vectors (2 x 8 KiB in flight per wave for H = 4096).
+// Every row is addressed through its own buffer resource whose size is the
+// row's byte length, or 0 for a row that must be zero-filled: loads past the
+// size return zeros and stores past it are dropped, so ragged row tails and
+// invalid rows need no per-lane branches and every load of a step is issued
+// before the first store.  Loads and stores are non-temporal (the rows are
+// streamed once).
 constexpr int kPermThreads = 256;
 constexpr int kPermUnroll = 8;
+constexpr int kPermRows = 8;
+constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kNonTemporal = 2;           // cache policy bit: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           kBufferWord3);
+}
+
+__device__ __forceinline__ int64_t perm_token(int32_t n, int32_t k, int64_t hidden_rows) {
+  const int64_t t = n >= 0 ? n / k : -1;
+  return t < hidden_rows ? t : -1;
+}
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     const int32_t* __restrict__ phys_off, const int32_t* __restrict__ inv, int32_t k,
@@ -771,28 +984,41 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int32_t seg0 = phys_off[p_begin];
   const int64_t rows = min(static_cast<int64_t>(phys_off[p_end] - seg0), cap);
   const int lane = lane_id();
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * (kPermThreads / 64);
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + (threadIdx.x >> 6);
-       row < rows; row += waves) {
-    const int32_t n = inv[seg0 + row];
-    const int64_t tok = n >= 0 ? n / k : -1;
-    u32x4* dst = out + row * H8;
-    if (tok < 0 || tok >= hidden_rows) {
-      for (int c = lane; c < H8; c += 64) __builtin_nontemporal_store(u32x4{0u, 0u, 0u, 0u}, dst + c);
-      continue;
-    }
-    const u32x4* src = hidden + tok * H8;
-    for (int c0 = 0; c0 < H8; c0 += 64 * kPermUnroll) {
-      u32x4 t[kPermUnroll];
+  const uint32_t rowb = static_cast<uint32_t>(H8) * 16u;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPermThreads / 64);
+  // wave-uniform values are passed through readfirstlane so the buffer
+  // resources built from them live in scalar registers
+  const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + wv;
+       blk * kPermRows < rows; blk += nwaves) {
+    const int64_t r0 = blk * kPermRows;
+    const int nb = static_cast<int>(min(static_cast<int64_t>(kPermRows), rows - r0));
+    const int32_t myn = lane < nb ? inv[seg0 + r0 + lane] : -1;
+    const int32_t mytok = static_cast<int32_t>(perm_token(myn, k, hidden_rows));
+    for (int q = 0; q < nb; q += 2) {
+      const bool has_b = q + 1 < nb;
+      const int32_t ta = __builtin_amdgcn_readlane(mytok, q);
+      const int32_t tb = has_b ? __builtin_amdgcn_readlane(mytok, q + 1) : -1;
+      const __amdgpu_buffer_rsrc_t sa =
+          row_rsrc(hidden + static_cast<int64_t>(ta < 0 ? 0 : ta) * H8, ta < 0 ? 0u : rowb);
+      const __amdgpu_buffer_rsrc_t sb =
+          row_rsrc(hidden + static_cast<int64_t>(tb < 0 ? 0 : tb) * H8, tb < 0 ? 0u : rowb);
+      const __amdgpu_buffer_rsrc_t da = row_rsrc(out + (r0 + q) * H8, rowb);
+      const __amdgpu_buffer_rsrc_t db = row_rsrc(out + (r0 + q + (has_b ? 1 : 0)) * H8, has_b ? rowb : 0u);
+      for (int c0 = 0; c0 < H8; c0 += 64 * kPermUnroll) {
+        u32x4 xa[kPermUnroll], xb[kPermUnroll];
 #pragma unroll
-      for (int u = 0; u < kPermUnroll; ++u) {
-        const int c = c0 + u * 64 + lane;
-        if (c < H8) t[u] = src[c];
-      }
+        for (int u = 0; u < kPermUnroll; ++u) {
+          const int off = (c0 + u * 64 + lane) * 16;
+          xa[u] = __builtin_amdgcn_raw_buffer_load_b128(sa, off, 0, kNonTemporal);
+          xb[u] = __builtin_amdgcn_raw_buffer_load_b128(sb, off, 0, kNonTemporal);
+        }
 #pragma unroll
-      for (int u = 0; u < kPermUnroll; ++u) {
-        const int c = c0 + u * 64 + lane;
-        if (c < H8) __builtin_nontemporal_store(t[u], dst + c);
+        for (int u = 0; u < kPermUnroll; ++u) {
+          const int off = (c0 + u * 64 + lane) * 16;
+          __builtin_amdgcn_raw_buffer_store_b128(xa[u], da, off, 0, kNonTemporal);
+          __builtin_amdgcn_raw_buffer_store_b128(xb[u], db, off, 0, kNonTemporal);
+        }
       }
     }
   }
@@ -869,41 +1095,43 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
   }
 }
 
-inline int bit_width(uint32_t x) { return 32 - __builtin_clz(x); }
-
 template <int MMAX, int SMAX>
-hipError_t launch_plan_t(const PlanParams& pp, int32_t L, size_t lds, int32_t* hist,
-                         int32_t* plans, hipStream_t st) {
+hipError_t launch_plan_t(const PlanParams& pp, int32_t L, size_t lds, const int32_t* hist,
+                         int32_t* tbase, int32_t* plans, hipStream_t st) {
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<MMAX, SMAX>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
-  plan_kernel<MMAX, SMAX><<<dim3(L), dim3(kPlanThreads), lds, st>>>(hist, plans, pp);
+  const uint32_t grid = static_cast<uint32_t>(L) * static_cast<uint32_t>(1 + pp.scan_wgs);
+  plan_kernel<MMAX, SMAX><<<dim3(grid), dim3(kPlanThreads), lds, st>>>(hist, tbase, plans, pp);
   return hipGetLastError();
 }
 
 template <int SMAX>
-hipError_t launch_plan_m(int M, const PlanParams& pp, int32_t L, size_t lds, int32_t* hist,
-                         int32_t* plans, hipStream_t st) {
-  if (M <= 2) return launch_plan_t<2, SMAX>(pp, L, lds, hist, plans, st);
-  if (M <= 4) return launch_plan_t<4, SMAX>(pp, L, lds, hist, plans, st);
-  if (M <= 8) return launch_plan_t<8, SMAX>(pp, L, lds, hist, plans, st);
-  return launch_plan_t<16, SMAX>(pp, L, lds, hist, plans, st);
+hipError_t launch_plan_m(int M, const PlanParams& pp, int32_t L, size_t lds, const int32_t* hist,
+                         int32_t* tbase, int32_t* plans, hipStream_t st) {
+  if (M <= 2) return launch_plan_t<2, SMAX>(pp, L, lds, hist, tbase, plans, st);
+  if (M <= 4) return launch_plan_t<4, SMAX>(pp, L, lds, hist, tbase, plans, st);
+  if (M <= 8) return launch_plan_t<8, SMAX>(pp, L, lds, hist, tbase, plans, st);
+  return launch_plan_t<16, SMAX>(pp, L, lds, hist, tbase, plans, st);
 }
 
+// Grid quotas per probe round: enough (quota, domain) items for one wave
+// per SIMD.  More probe waves than SIMDs only share issue slots: the probes
+// of a round run in lock step, and the first one usually succeeds.
 void plan_rounds(const Shape& sh, int32_t* G, int32_t* items) {
-  if (sh.ndom <= kPlanWaves) {
-    *G = kPlanWaves / sh.ndom;
-    *items = *G * sh.ndom;
-  } else {
-    *G = 1;
-    *items = sh.ndom;
-  }
+  constexpr int kSimds = 4;
+  *G = sh.ndom < kSimds ? kSimds / sh.ndom : 1;
+  *items = *G * sh.ndom;
 }
 
 }  // namespace
+
+size_t rerouting_lds_bytes(const Shape& sh, bool layout) {
+  return reroute_lds_bytes(sh.E, sh.n_inst, layout);
+}
 
 size_t plan_lds_bytes(const Shape& sh) {
   int32_t G, items;
@@ -911,16 +1139,17 @@ size_t plan_lds_bytes(const Shape& sh) {
   return 4 * plan_lds_words(sh.E, sh.R, sh.S, sh.D, sh.P, sh.ndom, items);
 }
 
-hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, int32_t N,
-                          int32_t* tile_hist, int32_t* plans, int32_t* phys_idx, int32_t* pos,
-                          hipStream_t st) {
+hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const float* w,
+                          int32_t N, int32_t* ws, int32_t* plans, int32_t* phys_idx, int32_t* pos,
+                          int32_t* inv, float* w_perm, hipStream_t st) {
   if (L <= 0) return hipSuccess;
   const int32_t ntiles = static_cast<int32_t>(ntiles_of(N));
-  const int nbits = bit_width(static_cast<uint32_t>(sh.E));
   const int64_t blocks = static_cast<int64_t>(L) * ntiles;
+  int32_t* hist = ws;
+  int32_t* tbase = ws + static_cast<int64_t>(L) * ntiles * sh.E;
   if (blocks > 0) {
     hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads),
-                       sizeof(int32_t) * sh.E, st, idx, N, sh.E, ntiles, nbits, tile_hist);
+                       sizeof(int32_t) * sh.E, st, idx, N, sh.E, ntiles, hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -930,6 +1159,13 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, int32_
   pp.eps_num = sh.eps_num; pp.eps_den = sh.eps_den; pp.allow_zero = sh.allow_zero;
   pp.rec_words = sh.lay.words;
   plan_rounds(sh, &pp.G, &pp.items);
+  // scan workgroups: enough that each thread's run of tiles is about one
+  // batch of loads, at most one per expert
+  {
+    const int64_t ew = ntiles > 0 ? (16ll * kPlanThreads) / ntiles : sh.E;
+    pp.scan_ew = static_cast<int32_t>(ew < 1 ? 1 : (ew > sh.E ? sh.E : ew));
+    pp.scan_wgs = ntiles > 0 ? (sh.E + pp.scan_ew - 1) / pp.scan_ew : 0;
+  }
   for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
     pp.off[f] = sh.lay.off[f];
     pp.len[f] = sh.lay.len[f];
@@ -937,19 +1173,38 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, int32_
   const size_t lds = plan_lds_bytes(sh);
   hipError_t e;
   if (sh.S <= 2)
-    e = launch_plan_m<2>(sh.M, pp, L, lds, tile_hist, plans, st);
+    e = launch_plan_m<2>(sh.M, pp, L, lds, hist, tbase, plans, st);
   else if (sh.S <= 4)
-    e = launch_plan_m<4>(sh.M, pp, L, lds, tile_hist, plans, st);
+    e = launch_plan_m<4>(sh.M, pp, L, lds, hist, tbase, plans, st);
   else
-    e = launch_plan_m<8>(sh.M, pp, L, lds, tile_hist, plans, st);
+    e = launch_plan_m<8>(sh.M, pp, L, lds, hist, tbase, plans, st);
   if (e != hipSuccess) return e;
   if (blocks > 0) {
-    const size_t rl = sizeof(int32_t) * (4 * sh.E + sh.E + 1 + 3 * sh.n_inst);
-    hipLaunchKernelGGL(reroute_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads), rl,
-                       st, idx, N, sh.E, ntiles, nbits, tile_hist, plans, sh.lay.words,
-                       sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
-                       sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE],
-                       sh.n_inst, phys_idx, pos);
+    const bool layout = inv != nullptr;
+    const size_t rl = reroute_lds_bytes(sh.E, sh.n_inst, layout);
+    if (layout) {
+      if (rl > 65536) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&reroute_kernel<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
+        if (e != hipSuccess) return e;
+      }
+      reroute_kernel<true><<<dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads), rl, st>>>(
+          idx, w, N, sh.E, ntiles, tbase, plans, sh.lay.words,
+          sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
+          sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE], sh.n_inst,
+          phys_idx, pos, inv, w_perm);
+    } else {
+      if (rl > 65536) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&reroute_kernel<false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
+        if (e != hipSuccess) return e;
+      }
+      reroute_kernel<false><<<dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads), rl, st>>>(
+          idx, w, N, sh.E, ntiles, tbase, plans, sh.lay.words,
+          sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
+          sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE], sh.n_inst,
+          phys_idx, pos, inv, w_perm);
+    }
     e = hipGetLastError();
   }
   return e;
@@ -969,8 +1224,8 @@ hipError_t launch_permute(const Shape& sh, const int32_t* plan, const int32_t* i
                           const uint16_t* hidden, int64_t hidden_rows, int32_t H, int32_t p_begin,
                           int32_t p_end, uint16_t* out, int64_t cap, hipStream_t st) {
   if (cap <= 0 || p_begin == p_end) return hipSuccess;
-  const int64_t want = (cap + 3) / 4;
-  const uint32_t blocks = static_cast<uint32_t>(want < 4096 ? want : 4096);
+  const int64_t want = (cap + 4 * kPermRows - 1) / (4 * kPermRows);
+  const uint32_t blocks = static_cast<uint32_t>(want < 8192 ? want : 8192);
   hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(kPermThreads), 0, st,
                      plan + sh.lay.off[ULTRAEP_PLAN_PHYS_OFF], inv, k,
                      reinterpret_cast<const u32x4*>(hidden), hidden_rows, H / 8, p_begin, p_end,

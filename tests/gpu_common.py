@@ -28,18 +28,28 @@ def routing_cached(cfg_id: int, layer: int, mb: int, T: int | None = None):
     return idx, wt
 
 
-def run_balance(ctx, idx_layers: np.ndarray, w_layers: np.ndarray | None, T: int, k: int, dev="cuda"):
-    """Balance (and, with weights, lay out) L layers; returns host copies."""
+def run_balance(ctx, idx_layers: np.ndarray, w_layers: np.ndarray | None, T: int, k: int, dev="cuda",
+                fused: bool = True):
+    """Balance (and, with weights, lay out) L layers; returns host copies.
+
+    fused: the layout is written by ultraep_balance itself; otherwise by a
+    separate ultraep_dispatch_layout call."""
     import torch
     L = idx_layers.shape[0]
     buf = U.Buffers(ctx, L, T, k, dev)
     d_idx = torch.from_numpy(np.array(idx_layers, copy=True)).to(dev)
-    U.ultraep_balance(ctx, d_idx, T, k, buf.workspace, buf.plans, buf.phys_idx, buf.pos, L=L)
     out = {"buf": buf}
+    buf.inv.fill_(-7)
     if w_layers is not None:
         d_w = torch.from_numpy(np.array(w_layers, copy=True)).to(dev)
-        buf.inv.fill_(-7)
-        U.ultraep_dispatch_layout(ctx, T, k, buf.pos, d_w, buf.inv, buf.w_perm, L=L)
+        if fused:
+            U.ultraep_balance(ctx, d_idx, T, k, buf.workspace, buf.plans, buf.phys_idx, buf.pos,
+                              topk_w=d_w, inv=buf.inv, w_perm=buf.w_perm, L=L)
+        else:
+            U.ultraep_balance(ctx, d_idx, T, k, buf.workspace, buf.plans, buf.phys_idx, buf.pos, L=L)
+            U.ultraep_dispatch_layout(ctx, T, k, buf.pos, d_w, buf.inv, buf.w_perm, L=L)
+    else:
+        U.ultraep_balance(ctx, d_idx, T, k, buf.workspace, buf.plans, buf.phys_idx, buf.pos, L=L)
     torch.cuda.synchronize()
     out["plans"] = buf.plans.cpu().numpy()
     out["phys"] = buf.phys_idx.cpu().numpy()

@@ -47,12 +47,19 @@ def test_status_strings():
     (64, 2, 1, 2, -2),     # M = 32 beyond limit
     (64, 64, 9, 64, -2),   # S beyond limit
     (256, 128, 1, 128, -2),  # D beyond one wave
-    (1024, 1024, 4, 64, -2),  # R*S beyond limit
+    (1024, 1024, 2, 64, -2),  # R*S beyond limit
+    (1024, 1024, 1, 64, -2),  # E + R*S beyond one CU's LDS
 ])
 def test_create_rejects(E, R, S, D, code):
     with pytest.raises(U.UltraEPError) as ei:
         U.ultraep_create(E, R, S, D)
     assert ei.value.status == code
+
+
+@pytest.mark.parametrize("E,R,S,D", [(1024, 512, 1, 64), (512, 512, 2, 64), (1024, 64, 8, 64),
+                                     (256, 64, 2, 64), (160, 40, 3, 8), (8, 4, 1, 4)])
+def test_create_accepts_limits(E, R, S, D):
+    U.ultraep_create(E, R, S, D).close()
 
 
 def test_create_rejects_bad_options():
@@ -77,8 +84,8 @@ def test_plan_layout_fields():
 def test_workspace_bytes():
     ctx = U.ultraep_create(128, 64, 2, 64)
     ntiles = -(-64 * 8192 * 8 // 8192)
-    assert ctx.workspace_bytes(1, 8192, 8) == 4 * ntiles * 128
-    assert ctx.workspace_bytes(3, 8192, 8) == 3 * 4 * ntiles * 128
+    assert ctx.workspace_bytes(1, 8192, 8) == 2 * 4 * ntiles * 128
+    assert ctx.workspace_bytes(3, 8192, 8) == 3 * 2 * 4 * ntiles * 128
     with pytest.raises(U.UltraEPError) as ei:
         ctx.workspace_bytes(1, 8192, 0)
     assert ei.value.status == -1
@@ -93,14 +100,24 @@ FAKE = 1 << 20   # never dereferenced: every call below fails its host check
 def test_balance_argument_checks():
     ctx = U.ultraep_create(8, 4, 1, 4)
     f = U.lib().ultraep_balance
-    assert f(ctx.handle, -1, FAKE, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1
-    assert f(ctx.handle, 1, FAKE, 16, 0, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1   # k = 0
-    assert f(ctx.handle, 1, FAKE, 16, 9, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1   # k > E
-    assert f(ctx.handle, 1, None, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1   # null idx
-    assert f(ctx.handle, 1, FAKE + 2, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -2  # misaligned
-    assert f(ctx.handle, 1, FAKE, 16, 2, FAKE, 4, FAKE, FAKE, FAKE, None) == -4   # workspace short
-    assert f(None, 1, FAKE, 16, 2, FAKE, 1 << 20, FAKE, FAKE, FAKE, None) == -1
-    assert f(ctx.handle, 0, None, 16, 2, None, 0, None, None, None, None) == 0    # L = 0: no-op
+    h, F = ctx.handle, FAKE
+
+    def call(L=1, idx=F, w=None, T=16, k=2, ws=F, wsb=1 << 20, plans=F, phys=F, pos=F, inv=None, wp=None, ctxh=h):
+        return f(ctxh, L, idx, w, T, k, ws, wsb, plans, phys, pos, inv, wp, None)
+
+    assert call(L=-1) == -1
+    assert call(k=0) == -1
+    assert call(k=9) == -1                 # k > E
+    assert call(T=-1) == -1
+    assert call(idx=None) == -1
+    assert call(w=F, inv=F) == -1          # layout outputs given only in part
+    assert call(w=F) == -1
+    assert call(idx=F + 2) == -2           # misaligned
+    assert call(w=F, inv=F, wp=F + 1) == -2
+    assert call(wsb=4) == -4               # workspace short
+    assert call(T=1 << 28, k=8) == -2      # N >= 2^31
+    assert call(ctxh=None) == -1
+    assert call(L=0, idx=None, ws=None, plans=None, phys=None, pos=None) == 0   # L = 0: no-op
 
 
 def test_permute_and_fold_argument_checks():

@@ -104,12 +104,14 @@ def test_hand_worked_plans_on_gpu():
     (32, 8, 3, 4, 2049, 4, 0.01, True),    # zero-quota masters allowed
     (64, 64, 1, 64, 700, 1, 0.0, False),   # k = 1, M = 1
     (1024, 64, 8, 64, 512, 16, 0.0, False),    # M = 16, S = 8 (largest register tiles)
-    (1024, 1024, 2, 64, 16, 8, 0.0, False),    # R*S = 2048 (slot limit), 16 domains
-    (1024, 1024, 1, 8, 16, 8, 0.0, False),     # 128 domains: more items than waves
+    (512, 512, 2, 64, 32, 8, 0.0, False),      # R*S = 1024 (slot limit), 8 domains
+    (1024, 512, 1, 64, 32, 8, 0.0, False),     # E = 1024 with 512 slots
+    (512, 512, 1, 8, 32, 8, 0.0, False),       # 64 domains: more items than waves
     (160, 40, 3, 8, 1000, 8, 0.0, False),
 ])
-def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero):
-    say(f"edge E={E} R={R} S={S} D={D} T={T} k={k}")
+@pytest.mark.parametrize("fused", [True, False])
+def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero, fused):
+    say(f"edge E={E} R={R} S={S} D={D} T={T} k={k} fused={fused}")
     rng = np.random.default_rng([E, R, S, D, T, k])
     p = rng.dirichlet(np.full(E, 0.2))
     N = R * T * k
@@ -119,7 +121,7 @@ def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero):
     idx = idx.reshape(R * T, k)
     wt = rng.random((R * T, k)).astype(np.float32)
     ctx = U.ultraep_create(E, R, S, D, allow_zero_master=allow_zero)
-    got = run_balance(ctx, idx[None], wt[None], T, k)
+    got = run_balance(ctx, idx[None], wt[None], T, k, fused=fused)
     pl, phys, pos = assert_layer_equal(ctx, got, 0, idx, wt, E, R, S, D, allow_zero_master=allow_zero)
     check_plan_invariants(pl, pl.c, allow_zero)
 
@@ -160,6 +162,11 @@ def _full_config(cfg_id, layers, check_layers, mb=0):
 
 def test_config2_single_layer_full():
     w, ctx, got, idx = _full_config(2, [0], {0})
+    # the separate layout call gives the same rows
+    wt = routing_cached(2, 0, 0)[1]
+    sep = run_balance(ctx, idx, wt[None], w.T, w.k, fused=False)
+    for key in ("inv", "w_perm"):
+        assert np.array_equal(sep[key].view(np.uint32), got[key].view(np.uint32)), key
     g = ctx.decode_plan(got["plans"][0])
     assert g["rank_after"].max() * w.R / g["total"] <= 1.04
 
