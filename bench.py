@@ -37,7 +37,62 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = single layer, the headline)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size of the device-to-device copy that measures the HBM copy ceiling")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "permute_kernel_traffic_single_layer.md")
+KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_load_ultraep_amd", "csrc", "ultraep_kernels.hip")
+
+
+def permute_source_sha256():
+    """Hash of the permute kernel's source (its comment block, constants,
+    helpers and body), so recorded counters go stale only when it changes."""
+    import hashlib
+    text = open(KERNEL_SOURCE).read()
+    start = text.index("// One wave per output row")
+    end = text.index("\n}\n", text.index("void permute_kernel(", start)) + 3
+    return hashlib.sha256(text[start:end].encode()).hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per permute launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when the kernel source changed since."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = permute_source_sha256()
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_val or m_src.group(1) != src:
+        return None
+    return float(m_val.group(1))
+
+
+def copy_ceiling(torch, dev, mib):
+    """Device-to-device copy rate (read + write bytes / time): the practical
+    HBM ceiling a streaming kernel is compared with."""
+    n = mib << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = 10
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        b.copy_(a)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    del a, b
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(w, idx, wt, hidden, seg, masters, reps, slots, budget_s):
@@ -107,9 +162,13 @@ def main():
     seg = (r_max * P1, (r_max + 1) * P1)
     seg_rows = int(plan["phys_off"][seg[1]] - plan["phys_off"][seg[0]])
     out = torch.empty((seg_rows, w.H), dtype=torch.int16, device=dev)
-    slots = (r_max * w.S, (r_max + 1) * w.S)
+    # fold unit: the redundant slots of the rank with the most filled slots
+    # (lowest such rank); each filled slot is one replica to fold
+    filled = (plan["slot_expert"].reshape(w.R, w.S) >= 0).sum(axis=1)
+    r_fold = int(np.argmax(filled))
+    slots = (r_fold * w.S, (r_fold + 1) * w.S)
     fold_experts = sorted({int(e) for e in plan["slot_expert"][slots[0]:slots[1]] if e >= 0})
-    n_fold_slots = sum(1 for e in plan["slot_expert"][slots[0]:slots[1]] if e >= 0)
+    n_fold_slots = int(filled[r_fold])
     masters_h = W.grads(w, max(1, len(fold_experts)), stream=1)
     reps_h = W.grads(w, w.S, stream=2)
     d_m = torch.from_numpy(masters_h).to(dev)
@@ -160,6 +219,8 @@ def main():
     gbps = lambda b, ms: b / (ms * 1e-3) / 1e9                       # noqa: E731
 
     total = plan["total"]
+    ceiling = copy_ceiling(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
+    traffic = recorded_traffic()
     result = {
         "metric": METRIC,
         "value": w.N / (ms_step * 1e-3),
@@ -176,7 +237,8 @@ def main():
         "config": {"workload": w.name, "E": w.E, "R": w.R, "S": w.S, "D": w.D, "top_k": w.k,
                    "tokens_per_rank": w.T, "hidden": w.H, "layers_per_step": L,
                    "permute_segment": f"rank {r_max} ({seg_rows} rows)",
-                   "fold": f"rank {r_max} slots {slots[0]}..{slots[1] - 1}, {w.fold_rows}x{w.fold_cols} fp32",
+                   "fold": f"rank {r_fold} slots {slots[0]}..{slots[1] - 1} ({n_fold_slots} filled), "
+                           f"{w.fold_rows}x{w.fold_cols} fp32 per slot",
                    "parallelism": "1 GPU; EP group simulated as logical ranks"},
         "balance_reroute_us_per_layer": (t_bal + t_lay) * 1e3 / L,
         "routed_pairs_per_s_balance_layout": w.N / ((t_bal + t_lay) * 1e-3),
@@ -190,9 +252,11 @@ def main():
         "imbalance_before": plan["rank_before"].max() * w.R / total,
         "imbalance_after": plan["rank_after"].max() * w.R / total,
         "replicas": plan["replicas"],
+        "hbm_copy_ceiling_GBps": ceiling,
+        "permute_frac_of_copy_ceiling": gbps(perm_bytes, t_perm) / ceiling if ceiling else None,
         "roofline": {"bound": "hbm", "kernel": "permute_kernel", "achieved": gbps(perm_bytes, t_perm),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps(perm_bytes, t_perm) / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": gbps(perm_bytes, t_perm) / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": perm_bytes},
     }
     if not args.no_cpu_baseline:

@@ -63,6 +63,14 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
   return min(min(readlane(x, 0), readlane(x, 16)), min(readlane(x, 32), readlane(x, 48)));
 }
 
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  x += dpp<0xB1>(x);
+  x += dpp<0x4E>(x);
+  x += dpp<0x141>(x);
+  x += dpp<0x140>(x);
+  return readlane(x, 0) + readlane(x, 16) + readlane(x, 32) + readlane(x, 48);
+}
+
 __device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(m); }
 
 // 16-byte vectors as native clang vectors (the nontemporal builtins take
@@ -267,15 +275,17 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
   const int r = d * D + lane;
   const int32_t Hr = act ? L.H[r] : 0;
 
-  int32_t ce[MMAX], pa[MMAX], room[MMAX];
+  int32_t pa[MMAX], room[MMAX];
 #pragma unroll
   for (int j = 0; j < MMAX; ++j) {
-    ce[j] = (act && j < M) ? L.c[r * M + j] : 0;
     pa[j] = 0;
     room[j] = 0;
   }
   bool fail = false;
   if (act && Hr > Q) {
+    int32_t ce[MMAX];
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j) ce[j] = j < M ? L.c[r * M + j] : 0;
     int32_t X = Hr - Q;
     uint32_t used = 0;
     for (int step = 0; step < M; ++step) {
@@ -305,140 +315,121 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
   if (ballot(fail)) return false;
 
   int32_t spare = act ? max(0, Q - Hr) : 0;
-  int32_t freeslots = act ? S : 0;
-  int nh = 0;
+  int32_t nh = act ? 0 : S;  // filled slots; inactive lanes look full
   int32_t he[SMAX], hq[SMAX];
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
     he[s] = -1;
     hq[s] = 0;
   }
-  auto place = [&](int32_t e, int32_t x) {
+  // place x pairs of expert e on the lane `who` (branch-free selects)
+  auto place = [&](int who, int32_t e, int32_t x) {
+    const bool me = lane == who;
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s)
-      if (s == nh) {
-        he[s] = e;
-        hq[s] = x;
-      }
-    ++nh;
-    --freeslots;
+    for (int s = 0; s < SMAX; ++s) {
+      const bool here = me && s == nh;
+      he[s] = here ? e : he[s];
+      hq[s] = here ? x : hq[s];
+    }
+    nh += me ? 1 : 0;
   };
 
   const int max_steps = D * S + 1;
-  bool done = false;
   for (int step = 0; step <= max_steps; ++step) {
-    // pop the largest piece
+    // pop the largest piece (ties: lowest expert id = lowest lane, lowest j)
     uint32_t mya = 0;
     int myj = 0;
 #pragma unroll
-    for (int j = 0; j < MMAX; ++j)
-      if (static_cast<uint32_t>(pa[j]) > mya) {
-        mya = static_cast<uint32_t>(pa[j]);
-        myj = j;
-      }
+    for (int j = 0; j < MMAX; ++j) {
+      const bool bigger = static_cast<uint32_t>(pa[j]) > mya;
+      mya = bigger ? static_cast<uint32_t>(pa[j]) : mya;
+      myj = bigger ? j : myj;
+    }
     const uint32_t amax = wave_max(mya);
     if (amax == 0) {
-      done = true;
-      break;
+      if (act) {
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+          if (s < S) {
+            res_e[lane * S + s] = he[s];
+            res_q[lane * S + s] = hq[s];
+          }
+      }
+      return true;
     }
     const int owner = lowest_lane(ballot(mya == amax));
     const int jsel = static_cast<int>(readlane(static_cast<uint32_t>(myj), owner));
     const int32_t e = (d * D + owner) * M + jsel;
     int32_t amt = static_cast<int32_t>(amax);
-    if (lane == owner) {
 #pragma unroll
-      for (int j = 0; j < MMAX; ++j)
-        if (j == jsel) pa[j] = 0;
-    }
+    for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? 0 : pa[j];
     bool hosts = false;
 #pragma unroll
     for (int s = 0; s < SMAX; ++s) hosts |= (he[s] == e);
-    const bool elig = act && lane != owner && freeslots > 0 && !hosts;
+    const bool elig = lane != owner && nh < S && !hosts;
 
-    // fit (least spare that takes the whole piece), roomiest receiver and
-    // donor (largest queued piece on an eligible rank with room left) are
-    // independent reductions, issued together so their latencies overlap
-    const uint32_t fitv = (elig && spare >= amt) ? static_cast<uint32_t>(spare) : 0xFFFFFFFFu;
-    const uint32_t recv = (elig && spare > 0) ? static_cast<uint32_t>(spare) : 0u;
+    // One key serves both receiver choices: a receiver that takes the whole
+    // piece gets the top bit and the inverted spare (the largest key is the
+    // tightest fit, ties to the lowest lane); otherwise the key is the spare
+    // itself (the largest key is the roomiest receiver).
+    const uint32_t key = (elig && spare > 0)
+                             ? (spare >= amt ? (0x80000000u | (0x7FFFFFFFu - static_cast<uint32_t>(spare)))
+                                             : static_cast<uint32_t>(spare))
+                             : 0u;
+    // donor: largest queued piece on an eligible rank with room left
     uint32_t dbest = 0;
     int dj = 0;
-    if (elig) {
 #pragma unroll
-      for (int j = 0; j < MMAX; ++j)
-        if (pa[j] > 0 && room[j] > 0 && static_cast<uint32_t>(pa[j]) > dbest) {
-          dbest = static_cast<uint32_t>(pa[j]);
-          dj = j;
-        }
+    for (int j = 0; j < MMAX; ++j) {
+      const bool cand = elig && pa[j] > 0 && room[j] > 0 && static_cast<uint32_t>(pa[j]) > dbest;
+      dbest = cand ? static_cast<uint32_t>(pa[j]) : dbest;
+      dj = cand ? j : dj;
     }
-    const uint32_t fmin = wave_min(fitv);
-    const uint32_t rmax = wave_max(recv);
+    const uint32_t kmax = wave_max(key);
     const uint32_t dmax = wave_max(dbest);
-    if (fmin != 0xFFFFFFFFu) {
-      const int rr = lowest_lane(ballot(fitv == fmin));
-      if (lane == rr) {
-        place(e, amt);
-        spare -= amt;
-      }
+    if (kmax & 0x80000000u) {  // fit
+      const int rr = lowest_lane(ballot(key == kmax));
+      spare -= lane == rr ? amt : 0;
+      place(rr, e, amt);
       continue;
     }
-    if (dmax > 0) {
+    const uint32_t rmax = kmax;  // roomiest receiver's spare (0: none)
+    if (dmax > 0) {              // chain through the donor's rank
       const int dl = lowest_lane(ballot(dbest == dmax));
       const int djs = static_cast<int>(readlane(static_cast<uint32_t>(dj), dl));
       if (rmax > 0) {
-        const int r2 = lowest_lane(ballot(recv == rmax));
-        if (lane == r2) {
-          place(e, spare);
-          spare = 0;
-        }
+        const int r2 = lowest_lane(ballot(key == rmax));
+        place(r2, e, static_cast<int32_t>(rmax));
+        spare = lane == r2 ? 0 : spare;
         amt -= static_cast<int32_t>(rmax);
       }
       int32_t myroom = 0;
 #pragma unroll
-      for (int j = 0; j < MMAX; ++j)
-        if (j == djs) myroom = room[j];
+      for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
       const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
       const int32_t x = min(amt, droom);
-      if (lane == dl) {
-        place(e, x);
+      place(dl, e, x);
 #pragma unroll
-        for (int j = 0; j < MMAX; ++j)
-          if (j == djs) {
-            pa[j] += x;
-            room[j] -= x;
-          }
+      for (int j = 0; j < MMAX; ++j) {
+        const bool here = lane == dl && j == djs;
+        pa[j] += here ? x : 0;
+        room[j] -= here ? x : 0;
       }
       amt -= x;
-      if (amt > 0 && lane == owner) {
-#pragma unroll
-        for (int j = 0; j < MMAX; ++j)
-          if (j == jsel) pa[j] = amt;
-      }
-    } else if (rmax > 0) {
-      const int r2 = lowest_lane(ballot(recv == rmax));
-      if (lane == r2) {
-        place(e, spare);
-        spare = 0;
-      }
+    } else if (rmax > 0) {  // fill the roomiest receiver
+      const int r2 = lowest_lane(ballot(key == rmax));
+      place(r2, e, static_cast<int32_t>(rmax));
+      spare = lane == r2 ? 0 : spare;
       amt -= static_cast<int32_t>(rmax);
-      if (lane == owner) {
-#pragma unroll
-        for (int j = 0; j < MMAX; ++j)
-          if (j == jsel) pa[j] = amt;
-      }
     } else {
-      break;  // fail
+      return false;
+    }
+    if (amt > 0) {
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? amt : pa[j];
     }
   }
-  if (!done) return false;
-  if (act) {
-#pragma unroll
-    for (int s = 0; s < SMAX; ++s)
-      if (s < S) {
-        res_e[lane * S + s] = he[s];
-        res_q[lane * S + s] = hq[s];
-      }
-  }
-  return true;
+  return false;
 }
 
 // Tile ordinal bases for the experts [e0, e0 + ew) of one layer: base[t][e]
@@ -542,29 +533,44 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     }
     __syncthreads();
   }
-  // -- phase 1: home loads, total, grid.
-  for (int r = tid; r < R; r += kPlanThreads) {
-    int32_t s = 0;
-    for (int j = 0; j < M; ++j) s += L.c[r * M + j];
-    L.H[r] = s;
-    atomicAdd(&L.scal[kTotal], s);
-    atomicMax(&L.scal[kQmax], s);
-    atomicAdd(&L.dom[r / D], s);
-  }
-  __syncthreads();
-  for (int d = tid; d < a.ndom; d += kPlanThreads)
-    atomicMax(&L.scal[kFloor], (L.dom[d] + D - 1) / D);
-  __syncthreads();
-  if (tid == 0) {
-    const int32_t total = L.scal[kTotal], qmax = L.scal[kQmax];
-    const int32_t qmean = (total + R - 1) / R;
-    const int32_t qlb = max(qmean, L.scal[kFloor]);
-    const int64_t tol64 = (static_cast<int64_t>(total) * a.eps_num) /
-                          (static_cast<int64_t>(R) * a.eps_den);
-    const int32_t tol = static_cast<int32_t>(tol64 < 1 ? 1 : tol64);
-    L.scal[kQlb] = qlb;
-    L.scal[kTol] = tol;
-    L.scal[kK] = qmax > qlb ? (qmax - qlb + tol - 1) / tol : 0;
+  // -- phase 1: home loads, total, grid (wave 0, wave reductions only: LDS
+  // atomics on one address would be serialised lane by lane).
+  if (wave == 0) {
+    uint32_t total = 0, qmax = 0, floor = 0;
+    for (int r0 = 0; r0 < R; r0 += 64) {
+      const int r = r0 + lane;
+      int32_t h = 0;
+      if (r < R) {
+        for (int j = 0; j < M; ++j) h += L.c[r * M + j];
+        L.H[r] = h;
+      }
+      total += wave_sum(static_cast<uint32_t>(h));
+      qmax = max(qmax, wave_max(static_cast<uint32_t>(h)));
+    }
+    for (int d0 = 0; d0 < a.ndom; d0 += 64) {
+      const int d = d0 + lane;
+      uint32_t fl = 0;
+      if (d < a.ndom) {
+        uint32_t dl = 0;
+        for (int q = 0; q < D; ++q) dl += static_cast<uint32_t>(L.H[d * D + q]);
+        fl = (dl + D - 1) / D;
+      }
+      floor = max(floor, wave_max(fl));
+    }
+    if (lane == 0) {
+      const int32_t qmean = (static_cast<int32_t>(total) + R - 1) / R;
+      const int32_t qlb = max(qmean, static_cast<int32_t>(floor));
+      const int64_t tol64 = (static_cast<int64_t>(total) * a.eps_num) /
+                            (static_cast<int64_t>(R) * a.eps_den);
+      const int32_t tol = static_cast<int32_t>(tol64 < 1 ? 1 : tol64);
+      L.scal[kTotal] = static_cast<int32_t>(total);
+      L.scal[kQmax] = static_cast<int32_t>(qmax);
+      L.scal[kFloor] = static_cast<int32_t>(floor);
+      L.scal[kQlb] = qlb;
+      L.scal[kTol] = tol;
+      L.scal[kK] = static_cast<int32_t>(qmax) > qlb ? (static_cast<int32_t>(qmax) - qlb + tol - 1) / tol : 0;
+      L.scal[kReplicas] = 0;
+    }
   }
   __syncthreads();
   const int32_t qlb = L.scal[kQlb], tol = L.scal[kTol], K = L.scal[kK], qmax = L.scal[kQmax];
@@ -624,8 +630,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (e >= 0) {
       atomicSub(&L.mq[e], L.slotQ[s]);
       atomicOr(&L.rmask[e], 1ull << ((s / S) % D));
-      atomicAdd(&L.scal[kReplicas], 1);
     }
+  }
+  if (wave == 0) {
+    uint32_t filled = 0;
+    for (int s0 = 0; s0 < R * S; s0 += 64)
+      filled += __builtin_popcountll(ballot(s0 + lane < R * S && L.slotE[s0 + lane] >= 0));
+    if (lane == 0) L.scal[kReplicas] = static_cast<int32_t>(filled);
   }
   __syncthreads();
   for (int p = tid; p < P; p += kPlanThreads) {
@@ -952,18 +963,18 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
 // ------------------------------------------------------------------------
 // permute: bf16 rows into the layout order
 // ------------------------------------------------------------------------
-// Each wave copies blocks of kPermRows consecutive rows: one lane-parallel
-// load fetches the block's inverse-index entries, then the rows are moved two
-// at a time as 16-byte vectors (2 x 8 KiB in flight per wave for H = 4096).
-// Every row is addressed through its own buffer resource whose size is the
-// row's byte length, or 0 for a row that must be zero-filled: loads past the
-// size return zeros and stores past it are dropped, so ragged row tails and
-// invalid rows need no per-lane branches and every load of a step is issued
-// before the first store.  Loads and stores are non-temporal (the rows are
-// streamed once).
+// One wave per output row: the row's source token is one uniform load, and
+// the row moves in steps of 64 lanes x 4 x 16 bytes.  Every row is addressed
+// through its own buffer resource whose size is the row's byte length, or 0
+// for a row that must be zero-filled: loads past the size return zeros and
+// stores past it are dropped, so ragged row tails and invalid rows need no
+// per-lane branches.  Loads and stores are non-temporal (each row is streamed
+// once).  A launch-shape sweep on a full-size segment (H = 4096) put one row
+// per wave with 4 vectors per lane in flight ahead of several rows per wave
+// or more vectors per lane: many small independent streams keep more of
+// HBM's channels busy than a few deep ones.
 constexpr int kPermThreads = 256;
-constexpr int kPermUnroll = 8;
-constexpr int kPermRows = 8;
+constexpr int kPermUnroll = 4;
 constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
 constexpr int kNonTemporal = 2;           // cache policy bit: non-temporal
 
@@ -972,8 +983,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uin
                                            kBufferWord3);
 }
 
-__device__ __forceinline__ int64_t perm_token(int32_t n, int32_t k, int64_t hidden_rows) {
-  const int64_t t = n >= 0 ? n / k : -1;
+__device__ __forceinline__ int32_t perm_token(int32_t n, int32_t k, int64_t hidden_rows) {
+  const int32_t t = n >= 0 ? n / k : -1;
   return t < hidden_rows ? t : -1;
 }
 
@@ -986,40 +997,23 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int lane = lane_id();
   const uint32_t rowb = static_cast<uint32_t>(H8) * 16u;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPermThreads / 64);
-  // wave-uniform values are passed through readfirstlane so the buffer
-  // resources built from them live in scalar registers
+  // wave-uniform values go through readfirstlane so the buffer resources
+  // built from them live in scalar registers
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  for (int64_t blk = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + wv;
-       blk * kPermRows < rows; blk += nwaves) {
-    const int64_t r0 = blk * kPermRows;
-    const int nb = static_cast<int>(min(static_cast<int64_t>(kPermRows), rows - r0));
-    const int32_t myn = lane < nb ? inv[seg0 + r0 + lane] : -1;
-    const int32_t mytok = static_cast<int32_t>(perm_token(myn, k, hidden_rows));
-    for (int q = 0; q < nb; q += 2) {
-      const bool has_b = q + 1 < nb;
-      const int32_t ta = __builtin_amdgcn_readlane(mytok, q);
-      const int32_t tb = has_b ? __builtin_amdgcn_readlane(mytok, q + 1) : -1;
-      const __amdgpu_buffer_rsrc_t sa =
-          row_rsrc(hidden + static_cast<int64_t>(ta < 0 ? 0 : ta) * H8, ta < 0 ? 0u : rowb);
-      const __amdgpu_buffer_rsrc_t sb =
-          row_rsrc(hidden + static_cast<int64_t>(tb < 0 ? 0 : tb) * H8, tb < 0 ? 0u : rowb);
-      const __amdgpu_buffer_rsrc_t da = row_rsrc(out + (r0 + q) * H8, rowb);
-      const __amdgpu_buffer_rsrc_t db = row_rsrc(out + (r0 + q + (has_b ? 1 : 0)) * H8, has_b ? rowb : 0u);
-      for (int c0 = 0; c0 < H8; c0 += 64 * kPermUnroll) {
-        u32x4 xa[kPermUnroll], xb[kPermUnroll];
+  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + wv; row < rows;
+       row += nwaves) {
+    const int32_t t = __builtin_amdgcn_readfirstlane(perm_token(inv[seg0 + row], k, hidden_rows));
+    const __amdgpu_buffer_rsrc_t src =
+        row_rsrc(hidden + static_cast<int64_t>(t < 0 ? 0 : t) * H8, t < 0 ? 0u : rowb);
+    const __amdgpu_buffer_rsrc_t dst = row_rsrc(out + row * H8, rowb);
+    for (int c0 = 0; c0 < H8; c0 += 64 * kPermUnroll) {
+      u32x4 x[kPermUnroll];
 #pragma unroll
-        for (int u = 0; u < kPermUnroll; ++u) {
-          const int off = (c0 + u * 64 + lane) * 16;
-          xa[u] = __builtin_amdgcn_raw_buffer_load_b128(sa, off, 0, kNonTemporal);
-          xb[u] = __builtin_amdgcn_raw_buffer_load_b128(sb, off, 0, kNonTemporal);
-        }
+      for (int u = 0; u < kPermUnroll; ++u)
+        x[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
 #pragma unroll
-        for (int u = 0; u < kPermUnroll; ++u) {
-          const int off = (c0 + u * 64 + lane) * 16;
-          __builtin_amdgcn_raw_buffer_store_b128(xa[u], da, off, 0, kNonTemporal);
-          __builtin_amdgcn_raw_buffer_store_b128(xb[u], db, off, 0, kNonTemporal);
-        }
-      }
+      for (int u = 0; u < kPermUnroll; ++u)
+        __builtin_amdgcn_raw_buffer_store_b128(x[u], dst, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
     }
   }
 }
@@ -1224,8 +1218,8 @@ hipError_t launch_permute(const Shape& sh, const int32_t* plan, const int32_t* i
                           const uint16_t* hidden, int64_t hidden_rows, int32_t H, int32_t p_begin,
                           int32_t p_end, uint16_t* out, int64_t cap, hipStream_t st) {
   if (cap <= 0 || p_begin == p_end) return hipSuccess;
-  const int64_t want = (cap + 4 * kPermRows - 1) / (4 * kPermRows);
-  const uint32_t blocks = static_cast<uint32_t>(want < 8192 ? want : 8192);
+  const int64_t want = (cap + 3) / 4;  // one row per wave
+  const uint32_t blocks = static_cast<uint32_t>(want < (1 << 20) ? want : (1 << 20));
   hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(kPermThreads), 0, st,
                      plan + sh.lay.off[ULTRAEP_PLAN_PHYS_OFF], inv, k,
                      reinterpret_cast<const u32x4*>(hidden), hidden_rows, H / 8, p_begin, p_end,
