@@ -10,11 +10,9 @@
 
 namespace ultraep {
 
-// Pairs handled by one count / reroute workgroup: 4 wave64s, 2048 pairs each.
+// Pairs handled by one count / reroute workgroup.  The workgroup's waves
+// split the tile into equal stretches (see TileShape in the kernels).
 constexpr int kTile = 8192;
-constexpr int kTileThreads = 256;
-constexpr int kWavePairs = kTile / (kTileThreads / 64);
-constexpr int kChunks = kWavePairs / 64;
 // The plan solver runs in one workgroup of 16 waves per layer.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanWaves = kPlanThreads / 64;

@@ -89,21 +89,33 @@ __device__ __forceinline__ uint64_t match_peers_lds(unsigned long long* words, u
   return __atomic_load_n(&words[v], __ATOMIC_RELAXED);
 }
 
+// A tile of kTile pairs worked on by W waves: wave q owns the stretch of
+// kWavePairs pairs from q * kWavePairs, in kChunks chunks of 64.
+template <int W>
+struct TileShape {
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kWavePairs = kTile / W;
+  static constexpr int kChunks = kWavePairs / 64;
+  static_assert(kChunks * 64 * W == kTile, "tile must split into whole chunks");
+};
+
 // Expert ids of one wave's stretch of a tile: chunk c, lane l holds pair
 // base + 64c + l.  Every load is issued unconditionally (indices past the
-// tile are clamped to its last pair and masked afterwards) so all kChunks
-// loads are in flight together instead of one round trip per chunk.  Ids
-// outside [0, E) and padding become E.
+// tile are clamped to its last pair and masked afterwards) so all C loads
+// are in flight together instead of one round trip per chunk.  Ids outside
+// [0, E) and padding become E.
+template <int C>
 __device__ __forceinline__ void load_tile_ids(const int32_t* __restrict__ src, int base,
                                               int n_here, int lane, int32_t E,
-                                              uint32_t (&v)[kChunks]) {
+                                              uint32_t (&v)[C]) {
   const int last = n_here - 1;
-  int32_t raw[kChunks];
+  int32_t raw[C];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c)
+  for (int c = 0; c < C; ++c)
     raw[c] = __builtin_nontemporal_load(src + min(base + c * 64 + lane, last));
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
+  for (int c = 0; c < C; ++c) {
     const uint32_t x = static_cast<uint32_t>(raw[c]);
     v[c] = (base + c * 64 + lane < n_here && x < static_cast<uint32_t>(E)) ? x
                                                                            : static_cast<uint32_t>(E);
@@ -154,30 +166,33 @@ __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
 // ------------------------------------------------------------------------
 // count: per-tile expert histogram ([README] intro: exact post-gating load)
 // ------------------------------------------------------------------------
-// One workgroup per (layer, tile of kTile pairs).  Each wave loads its
-// 2048-pair stretch with all loads in flight at once and adds each valid id
-// to an LDS counter.  The order of the additions does not matter here, so a
-// plain LDS atomic per pair is the cheapest form: equal ids in one wave
-// instruction only serialise inside the LDS, they cost no VALU work.
-__global__ __launch_bounds__(kTileThreads) void count_kernel(
+// One workgroup of 16 waves per (layer, tile of kTile pairs).  Each wave
+// loads its 512-pair stretch with all loads in flight at once and adds each
+// valid id to an LDS counter.  The order of the additions does not matter
+// here, so a plain LDS atomic per pair is the cheapest form: equal ids in one
+// wave instruction only serialise inside the LDS, they cost no VALU work.
+using CountTile = TileShape<16>;
+
+__global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
     const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles,
     int32_t* __restrict__ hist) {
+  using T = CountTile;
   extern __shared__ __align__(16) int32_t s_cnt[];
   const int64_t blk = blockIdx.x;
   const int32_t layer = static_cast<int32_t>(blk / ntiles);
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
-  for (int i = threadIdx.x; i < E; i += kTileThreads) s_cnt[i] = 0;
+  for (int i = threadIdx.x; i < E; i += T::kThreads) s_cnt[i] = 0;
   const int32_t* src = idx + static_cast<int64_t>(layer) * N + static_cast<int64_t>(tile) * kTile;
   const int n_here = min(kTile, N - tile * kTile);
-  uint32_t v[kChunks];
-  load_tile_ids(src, (threadIdx.x >> 6) * kWavePairs, n_here, lane_id(), E, v);
+  uint32_t v[T::kChunks];
+  load_tile_ids(src, (threadIdx.x >> 6) * T::kWavePairs, n_here, lane_id(), E, v);
   __syncthreads();
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c)
+  for (int c = 0; c < T::kChunks; ++c)
     if (v[c] < static_cast<uint32_t>(E)) atomicAdd(&s_cnt[v[c]], 1);
   __syncthreads();
   int32_t* dst = hist + (static_cast<int64_t>(layer) * ntiles + tile) * E;
-  for (int i = threadIdx.x; i < E; i += kTileThreads) dst[i] = s_cnt[i];
+  for (int i = threadIdx.x; i < E; i += T::kThreads) dst[i] = s_cnt[i];
 }
 
 // ------------------------------------------------------------------------
@@ -755,7 +770,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 struct RerouteLds {
   unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids
   int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
-  int32_t* tcnt;   // [E] pairs of each expert in the tile
+  int32_t* tcnt;   // [E] the tile's ordinal base of e, then the tile's pairs of e
   int32_t* kfirst; // [E] first instance of e that holds ordinals of this tile
   int32_t* iptr;   // [E+1]
   int32_t* iend;   // [n_inst]
@@ -763,33 +778,33 @@ struct RerouteLds {
   int32_t* ibase;  // [n_inst]
   int32_t* roff;   // [n_inst+1] run offsets inside the tile's staging area
   int32_t* ro0;    // [n_inst] first ordinal of the run
-  int32_t* tmp;    // [kTileThreads/64 + 1]
+  int32_t* tmp;    // [waves + 1]
   float* wt;       // [kTile] the tile's routing weights, in pair order
   uint32_t* sp;    // [kTile] staged slot: run index << 16 | pair index inside the tile
 };
 
-constexpr int kTileWaves = kTileThreads / 64;
-
-__host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layout) {
-  size_t words = 2ull * kTileWaves * (E + 1) + static_cast<size_t>(kTileWaves) * E + 2ull * E +
-                 (E + 1) + 3ull * n_inst;
-  if (layout) words += (n_inst + 1) + n_inst + (kTileWaves + 1) + 2ull * kTile;
+__host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layout, int waves) {
+  size_t words = 2ull * waves * (E + 1) + static_cast<size_t>(waves) * E + 2ull * E + (E + 1) +
+                 3ull * n_inst;
+  if (layout) words += (n_inst + 1) + n_inst + (waves + 1) + 2ull * kTile;
   return 4 * words;
 }
 
-template <bool LAYOUT>
-__global__ __launch_bounds__(kTileThreads) void reroute_kernel(
+template <bool LAYOUT, int W>
+__global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t E,
     int32_t ntiles, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans,
     int32_t rec_words, int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase,
     int32_t n_inst, int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos,
     int32_t* __restrict__ inv, float* __restrict__ w_perm) {
+  using T = TileShape<W>;
+  constexpr int NT = T::kThreads;
   extern __shared__ __align__(16) int32_t lds[];
   RerouteLds S;
   {
     int32_t* q = lds;
-    S.peers = reinterpret_cast<unsigned long long*>(q); q += 2 * kTileWaves * (E + 1);
-    S.cntw = q; q += kTileWaves * E;
+    S.peers = reinterpret_cast<unsigned long long*>(q); q += 2 * W * (E + 1);
+    S.cntw = q; q += W * E;
     S.tcnt = q; q += E;
     S.kfirst = q; q += E;
     S.iptr = q; q += E + 1;
@@ -799,7 +814,7 @@ __global__ __launch_bounds__(kTileThreads) void reroute_kernel(
     if (LAYOUT) {
       S.roff = q; q += n_inst + 1;
       S.ro0 = q; q += n_inst;
-      S.tmp = q; q += kTileWaves + 1;
+      S.tmp = q; q += W + 1;
       S.wt = reinterpret_cast<float*>(q); q += kTile;
       S.sp = reinterpret_cast<uint32_t*>(q);
     }
@@ -813,36 +828,39 @@ __global__ __launch_bounds__(kTileThreads) void reroute_kernel(
   const int n_here = min(kTile, N - tile * kTile);
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int base = wave * kWavePairs;
+  const int base = wave * T::kWavePairs;
+  const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
 
-  uint32_t v[kChunks];
+  // every global load of the kernel is issued before the first wait
+  uint32_t v[T::kChunks];
   load_tile_ids(idx + first, base, n_here, lane, E, v);
   if (LAYOUT) {
-    constexpr int kPer = kTile / kTileThreads;
+    constexpr int kPer = kTile / NT;
     float x[kPer];
 #pragma unroll
     for (int u = 0; u < kPer; ++u)
       x[u] = __builtin_nontemporal_load(
-          w + first + min(u * kTileThreads + static_cast<int>(threadIdx.x), n_here - 1));
+          w + first + min(u * NT + static_cast<int>(threadIdx.x), n_here - 1));
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) S.wt[u * kTileThreads + threadIdx.x] = x[u];
+    for (int u = 0; u < kPer; ++u) S.wt[u * NT + threadIdx.x] = x[u];
   }
-  for (int i = threadIdx.x; i < kTileWaves * (E + 1); i += kTileThreads) S.peers[i] = 0;
-  for (int i = threadIdx.x; i < kTileWaves * E; i += kTileThreads) S.cntw[i] = 0;
-  for (int i = threadIdx.x; i <= E; i += kTileThreads) S.iptr[i] = plan[off_iptr + i];
-  for (int i = threadIdx.x; i < n_inst; i += kTileThreads) {
+  for (int i = threadIdx.x; i < W * (E + 1); i += NT) S.peers[i] = 0;
+  for (int i = threadIdx.x; i < W * E; i += NT) S.cntw[i] = 0;
+  for (int i = threadIdx.x; i <= E; i += NT) S.iptr[i] = plan[off_iptr + i];
+  for (int i = threadIdx.x; i < n_inst; i += NT) {
     S.iend[i] = plan[off_iend + i];
     S.iphys[i] = plan[off_iphys + i];
     S.ibase[i] = plan[off_ibase + i];
   }
+  for (int e = threadIdx.x; e < E; e += NT) S.tcnt[e] = tb[e];
   __syncthreads();
 
   // pass 1: rank of each pair among the wave's earlier pairs of its expert
   int32_t* my = S.cntw + wave * E;
   unsigned long long* mw = S.peers + wave * (E + 1);
-  int32_t lr[kChunks];
+  int32_t lr[T::kChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
+  for (int c = 0; c < T::kChunks; ++c) {
     const uint64_t peers = match_peers_lds(mw, v[c], lane);
     const bool valid = v[c] < static_cast<uint32_t>(E);
     const int32_t old = valid ? my[v[c]] : 0;
@@ -853,12 +871,11 @@ __global__ __launch_bounds__(kTileThreads) void reroute_kernel(
     lr[c] = old + count_below(peers);
   }
   __syncthreads();
-  const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
-  for (int e = threadIdx.x; e < E; e += kTileThreads) {
-    const int32_t b0 = tb[e];
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int32_t b0 = S.tcnt[e];
     int32_t run = b0;
 #pragma unroll
-    for (int q = 0; q < kTileWaves; ++q) {
+    for (int q = 0; q < W; ++q) {
       const int32_t t = S.cntw[q * E + e];
       S.cntw[q * E + e] = run;
       run += t;
@@ -876,7 +893,7 @@ __global__ __launch_bounds__(kTileThreads) void reroute_kernel(
   if (LAYOUT) {
     // runs: instance i of expert e holds the tile's ordinals
     // [max(start_i, b), min(end_i, b + count)) where b is the tile base of e
-    for (int e = threadIdx.x; e < E; e += kTileThreads) {
+    for (int e = threadIdx.x; e < E; e += NT) {
       const int32_t b0 = S.cntw[e], b1 = b0 + S.tcnt[e];
       int32_t start = 0;
       for (int i = S.iptr[e]; i < S.iptr[e + 1]; ++i) {
@@ -888,17 +905,17 @@ __global__ __launch_bounds__(kTileThreads) void reroute_kernel(
       }
     }
     // instance entries beyond the plan's used ones are empty runs
-    for (int i = S.iptr[E] + threadIdx.x; i < n_inst; i += kTileThreads) {
+    for (int i = S.iptr[E] + threadIdx.x; i < n_inst; i += NT) {
       S.roff[i] = 0;
       S.ro0[i] = 0;
     }
     __syncthreads();
-    block_exclusive_scan<kTileThreads>(S.roff, n_inst, S.tmp);
+    block_exclusive_scan<NT>(S.roff, n_inst, S.tmp);
   }
 
   // pass 2: instance, physical expert and layout row of each pair
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
+  for (int c = 0; c < T::kChunks; ++c) {
     const int i = base + c * 64 + lane;
     int32_t p = -1, row = -1;
     if (v[c] < static_cast<uint32_t>(E)) {
@@ -927,7 +944,7 @@ __global__ __launch_bounds__(kTileThreads) void reroute_kernel(
     // a corrupted plan record.
     const int nt = min(S.roff[n_inst], n_here);
     const int32_t tile0 = tile * kTile;
-    for (int j = threadIdx.x; j < nt; j += kTileThreads) {
+    for (int j = threadIdx.x; j < nt; j += NT) {
       const uint32_t sp = S.sp[j];
       const int r = static_cast<int>(sp >> 16), n = static_cast<int>(sp & 0xFFFFu);
       const int32_t row = S.ibase[r] + S.ro0[r] + (j - S.roff[r]);
@@ -1121,10 +1138,59 @@ void plan_rounds(const Shape& sh, int32_t* G, int32_t* items) {
   *items = *G * sh.ndom;
 }
 
+// Waves per reroute workgroup: the most whose per-wave grouping tables still
+// fit one CU's LDS.  With 16 waves one workgroup fills a CU's four SIMDs four
+// waves deep, which hides the LDS round trips of the per-pair passes.
+constexpr size_t kLdsBytes = 160 * 1024;
+
+int reroute_waves(const Shape& sh, bool layout) {
+  for (int waves : {16, 8})
+    if (reroute_lds_bytes(sh.E, sh.n_inst, layout, waves) <= kLdsBytes) return waves;
+  return 4;
+}
+
+template <bool LAYOUT, int W>
+hipError_t launch_reroute(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
+                          int32_t N, int32_t ntiles, const int32_t* tbase, const int32_t* plans,
+                          int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                          hipStream_t st) {
+  const size_t rl = reroute_lds_bytes(sh.E, sh.n_inst, LAYOUT, W);
+  const void* fn = reinterpret_cast<const void*>(&reroute_kernel<LAYOUT, W>);
+  if (rl > 65536) {
+    const hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
+    if (e != hipSuccess) return e;
+  }
+  reroute_kernel<LAYOUT, W><<<dim3(static_cast<uint32_t>(blocks)), dim3(TileShape<W>::kThreads),
+                              rl, st>>>(
+      idx, w, N, sh.E, ntiles, tbase, plans, sh.lay.words, sh.lay.off[ULTRAEP_PLAN_INST_PTR],
+      sh.lay.off[ULTRAEP_PLAN_INST_END], sh.lay.off[ULTRAEP_PLAN_INST_PHYS],
+      sh.lay.off[ULTRAEP_PLAN_INST_BASE], sh.n_inst, phys_idx, pos, inv, w_perm);
+  return hipGetLastError();
+}
+
+template <bool LAYOUT>
+hipError_t launch_reroute_w(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
+                            int32_t N, int32_t ntiles, const int32_t* tbase,
+                            const int32_t* plans, int32_t* phys_idx, int32_t* pos, int32_t* inv,
+                            float* w_perm, hipStream_t st) {
+  switch (reroute_waves(sh, LAYOUT)) {
+    case 16:
+      return launch_reroute<LAYOUT, 16>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+                                        inv, w_perm, st);
+    case 8:
+      return launch_reroute<LAYOUT, 8>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+                                       inv, w_perm, st);
+    default:
+      return launch_reroute<LAYOUT, 4>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+                                       inv, w_perm, st);
+  }
+}
+
 }  // namespace
 
 size_t rerouting_lds_bytes(const Shape& sh, bool layout) {
-  return reroute_lds_bytes(sh.E, sh.n_inst, layout);
+  return reroute_lds_bytes(sh.E, sh.n_inst, layout, reroute_waves(sh, layout));
 }
 
 size_t plan_lds_bytes(const Shape& sh) {
@@ -1142,7 +1208,7 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   int32_t* hist = ws;
   int32_t* tbase = ws + static_cast<int64_t>(L) * ntiles * sh.E;
   if (blocks > 0) {
-    hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads),
+    hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(CountTile::kThreads),
                        sizeof(int32_t) * sh.E, st, idx, N, sh.E, ntiles, hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1174,32 +1240,12 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
     e = launch_plan_m<8>(sh.M, pp, L, lds, hist, tbase, plans, st);
   if (e != hipSuccess) return e;
   if (blocks > 0) {
-    const bool layout = inv != nullptr;
-    const size_t rl = reroute_lds_bytes(sh.E, sh.n_inst, layout);
-    if (layout) {
-      if (rl > 65536) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&reroute_kernel<true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
-        if (e != hipSuccess) return e;
-      }
-      reroute_kernel<true><<<dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads), rl, st>>>(
-          idx, w, N, sh.E, ntiles, tbase, plans, sh.lay.words,
-          sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
-          sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE], sh.n_inst,
-          phys_idx, pos, inv, w_perm);
-    } else {
-      if (rl > 65536) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&reroute_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
-        if (e != hipSuccess) return e;
-      }
-      reroute_kernel<false><<<dim3(static_cast<uint32_t>(blocks)), dim3(kTileThreads), rl, st>>>(
-          idx, w, N, sh.E, ntiles, tbase, plans, sh.lay.words,
-          sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
-          sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE], sh.n_inst,
-          phys_idx, pos, inv, w_perm);
-    }
-    e = hipGetLastError();
+    if (inv != nullptr)
+      e = launch_reroute_w<true>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos, inv,
+                                 w_perm, st);
+    else
+      e = launch_reroute_w<false>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+                                  nullptr, nullptr, st);
   }
   return e;
 }
