@@ -1,22 +1,39 @@
 """Benchmark of the exact-load rebalancing hot path on one MI355X.
 
-One step = one pass of the whole path over one layer of synthetic routing:
+One step = one pass of the whole path over one batch of synthetic routing:
   ultraep_balance          count + quota plan + reroute (phys_idx, pos) and the
-                           dispatch layout (inverse index, permuted weights)
+                           dispatch layout (inverse index, permuted weights),
+                           for every layer of the batch in one call
   ultraep_permute          bf16 rows of the most loaded rank's receive segment
-  ultraep_fold_grads       that rank's redundant-slot gradients into masters
+                           (first layer of the batch)
+  ultraep_fold_grads       that layer's redundant-slot gradients of the rank
+                           with the most filled slots, into their masters
 All inputs are resident in HBM before the timed region.  Each call is timed
 with HIP events on the stream it runs on; the permute kernel is the dominant
 one and its roofline is reported against the 8 TB/s HBM peak.
 
-The CPU oracle is timed on the host on the same workload (cpu_baseline).
-Prints ONE JSON line.
+Beside the timed steps, the balance call is timed warm (back to back on the
+same input) and cold (a 1 GiB scratch write before each repetition evicts the
+256 MB Infinity Cache and the L2s); permute and fold are timed cold the same
+way.  The CPU oracle is timed stage by stage on the host on the same workload
+(cpu_baseline).  Prints ONE JSON line.
+
+Workloads (--config):
+  2  single layer, E=128 R=64 S=2 D=64 T=8192 top-8 (the default)
+  3  61 layers, E=256 R=64 S=2 D=64 T=4096 top-8, balanced in one call;
+     per-layer figures are the call's time / 61
+  4  non-stationary stream, 32 layers x 16 microbatches of the single-layer
+     shape, one balance call per instance; the cold balance time is also
+     reported as median and p99 over the instances
+  5  topology-constrained prefill, E=160 R=40 S=3 D=8 T=16384 top-8
+  1  tiny (launch-bound; no roofline claim)
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import platform
 import sys
 import time
 
@@ -27,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "balance+reroute µs/layer; routed pairs/s; permute/fold HBM GB/s vs peak"
+FLUSH_MIB = 1024
 
 
 def parse():
@@ -35,6 +53,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = single layer, the headline)")
+    ap.add_argument("--cold-reps", type=int, default=20, help="repetitions of each cold / warm timing")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="workload 4: instances used (0 = all 32 x 16)")
+    ap.add_argument("--workers", type=int, default=16, help="host processes generating inputs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=1024,
@@ -42,7 +64,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "permute_kernel_traffic_single_layer.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_single_layer_E128_R64_T8192.md")
 KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_load_ultraep_amd", "csrc", "ultraep_kernels.hip")
 
 
@@ -56,11 +78,13 @@ def permute_source_sha256():
     return hashlib.sha256(text[start:end].encode()).hexdigest()
 
 
-def recorded_traffic():
+def recorded_traffic(config):
     """HBM bytes per permute launch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when the kernel source changed since."""
-    import hashlib
+    WRITE_SIZE summary, or None when the kernel source changed since or the
+    summary covers another workload."""
     import re
+    if config != 2:
+        return None
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
@@ -74,29 +98,102 @@ def recorded_traffic():
 
 
 def copy_ceiling(torch, dev, mib):
-    """Device-to-device copy rate (read + write bytes / time): the practical
-    HBM ceiling a streaming kernel is compared with."""
+    """Device-to-device copy rate (read + write bytes / time), the best of a
+    few relative placements of source and destination: the practical HBM
+    ceiling a streaming kernel is compared with.  (The rate of one copy
+    depends on how its two buffers fall on the memory channels.)"""
     n = mib << 20
-    a = torch.empty(n, dtype=torch.uint8, device=dev)
-    b = torch.empty_like(a)
-    a.fill_(1)
-    for _ in range(3):
-        b.copy_(a)
+    pad = 8 << 20
+    buf = torch.empty(2 * n + pad, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    a = buf[:n]
+    best = 0.0
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    reps = 10
-    torch.cuda.synchronize()
-    ev[0].record()
-    for _ in range(reps):
-        b.copy_(a)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / reps
-    del a, b
-    return 2 * n / (ms * 1e-3) / 1e9
+    for off in (0, 64 << 10, (1 << 20) + (4 << 10), (4 << 20) + (12 << 10)):
+        b = buf[n + off:2 * n + off]
+        for _ in range(2):
+            b.copy_(a)
+        reps = 8
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(reps):
+            b.copy_(a)
+        ev[1].record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * n / (ev[0].elapsed_time(ev[1]) / reps * 1e-3) / 1e9)
+    del buf, a, b
+    return best
 
 
-def cpu_baseline(w, idx, wt, hidden, seg, masters, reps, slots, budget_s):
-    """Time the oracle (unchanged) on the host: the same step on the same arrays."""
+def host_info():
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def _route(a):
+    import workload as W
+    cfg, layer, mb = a
+    idx, wt, _ = W.routing(W.CONFIGS[cfg], layer, mb)
+    return idx, wt
+
+
+def routing_instances(w, insts, workers):
+    """Routing of every (layer, microbatch) in insts, generated by a process
+    pool before the GPU is touched (the generator is seeded per instance, so
+    the result does not depend on the pool)."""
+    if workers <= 1 or len(insts) == 1:
+        return [_route((w.cfg_id, l, m)) for l, m in insts]
+    import multiprocessing as mp
+    with mp.get_context("fork").Pool(min(workers, len(insts))) as pool:
+        return pool.map(_route, [(w.cfg_id, l, m) for l, m in insts], chunksize=1)
+
+
+def quality(ctx, plans, w):
+    """Balance quality of decoded plan records: max/mean rank load before and
+    after, the domain floor, replicas, probes."""
+    rows = []
+    for pl in plans:
+        mean = pl["total"] / w.R
+        reps = np.bincount(pl["slot_expert"][pl["slot_expert"] >= 0], minlength=w.E)
+        rows.append({"before": pl["rank_before"].max() / mean, "after": pl["rank_after"].max() / mean,
+                     "floor": pl["floor"] / mean, "replicas": pl["replicas"],
+                     "max_per_expert": int(reps.max()), "grid_index": pl["grid_index"],
+                     "rounds": pl["rounds"]})
+    if len(rows) == 1:
+        r = rows[0]
+        return {"imbalance_before": r["before"], "imbalance_after": r["after"],
+                "domain_floor": r["floor"], "replicas": r["replicas"],
+                "replicas_max_per_expert": r["max_per_expert"], "grid_index": r["grid_index"],
+                "probe_rounds": r["rounds"]}
+    col = lambda k: np.array([r[k] for r in rows], dtype=np.float64)  # noqa: E731
+    return {"plans": len(rows),
+            "imbalance_before_min_median_max": [col("before").min(), float(np.median(col("before"))),
+                                                col("before").max()],
+            "imbalance_after_median_max": [float(np.median(col("after"))), col("after").max()],
+            "domain_floor_max": col("floor").max(),
+            "replicas_median_max": [float(np.median(col("replicas"))), int(col("replicas").max())],
+            "replicas_max_per_expert": int(col("max_per_expert").max()),
+            "grid_index_max": int(col("grid_index").max()), "probe_rounds_max": int(col("rounds").max())}
+
+
+def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s):
+    """Time the oracle (unchanged) on the host, stage by stage, on the same
+    arrays: count, plan, reroute and layout per layer (the batch's layers or
+    instances in order, as many as the budget allows), permute of the same
+    rank segment and fold of the same slots of the first layer.  The step
+    estimate is L layers of balance plus one permute and one fold, as on the
+    GPU."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_limits
@@ -105,24 +202,46 @@ def cpu_baseline(w, idx, wt, hidden, seg, masters, reps, slots, budget_s):
         limiter = None
     p_begin, p_end = seg
     s0, s1 = slots
-    times = []
+    st = {"count": [], "plan": [], "reroute": [], "layout": [], "permute": [], "fold": []}
     t_start = time.perf_counter()
+    i = 0
     while True:
+        idx, wt = routes[i % len(routes)]
         t0 = time.perf_counter()
-        pl, phys, pos = O.balance(idx, w.E, w.R, w.S, w.D)
-        inv, wp = O.layout(pos, wt, pl.total)
-        O.permute(hidden, inv, w.k, pl, p_begin, p_end)
-        O.fold(masters, reps, pl, s0, s1)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+        c, dropped = O.count(idx, w.E)
+        t1 = time.perf_counter()
+        pl = O.plan(c, w.E, w.R, w.S, w.D, dropped=dropped)
+        t2 = time.perf_counter()
+        phys, pos = O.reroute(idx, pl)
+        t3 = time.perf_counter()
+        inv, _ = O.layout(pos, wt, pl.total)
+        t4 = time.perf_counter()
+        st["count"].append(t1 - t0)
+        st["plan"].append(t2 - t1)
+        st["reroute"].append(t3 - t2)
+        st["layout"].append(t4 - t3)
+        if i == 0:
+            t5 = time.perf_counter()
+            O.permute(hidden, inv, w.k, pl, p_begin, p_end)
+            t6 = time.perf_counter()
+            O.fold(masters, reps, pl, s0, s1)
+            t7 = time.perf_counter()
+            st["permute"].append(t6 - t5)
+            st["fold"].append(t7 - t6)
+        i += 1
+        if time.perf_counter() - t_start > budget_s or i >= 20:
             break
     if limiter is not None:
         limiter.unregister()
-    t = float(np.median(times))
-    return {"value": w.N / t, "unit": "pairs/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(times)} full steps of the same workload (count, plan, reroute, layout, "
-                      f"permute of one rank segment, fold of one rank's slots), median "
-                      f"{t * 1e3:.0f} ms/step, NumPy single thread"}
+    med = {k: float(np.median(v)) for k, v in st.items()}
+    layer_s = med["count"] + med["plan"] + med["reroute"] + med["layout"]
+    step_s = L * layer_s + med["permute"] + med["fold"]
+    return {"value": L * w.N / step_s, "unit": "pairs/s", "cores": 1, "kind": "oracle",
+            "sample": f"{i} layer(s) of the same workload through count, plan, reroute and layout, "
+                      f"one permute of the same rank segment and one fold of the same slots; "
+                      f"medians combined as {L} layer(s) + permute + fold = {step_s * 1e3:.0f} ms "
+                      f"per step; NumPy, one thread",
+            "stage_ms": {k: v * 1e3 for k, v in med.items()}}
 
 
 def main():
@@ -132,98 +251,157 @@ def main():
               "single MI355X, so --gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
     import moe_expert_load_ultraep_amd as U
     import workload as W
 
+    w = W.CONFIGS[args.config]
+    # ---- inputs: generated on the host before the GPU is touched (untimed)
+    if args.config == 3:
+        insts = [(l, 0) for l in range(w.layers)]
+        L = w.layers
+    elif args.config == 4:
+        insts = [(l, m) for l in range(w.layers) for m in range(w.microbatches)]
+        if args.instances > 0:
+            insts = insts[:args.instances]
+        L = 1
+    else:
+        insts = [(0, 0)]
+        L = 1
+    routes = routing_instances(w, insts, args.workers)
+    hidden = W.hidden(w, workers=args.workers)
+
+    import torch
     if not os.path.exists(U.LIB_PATH):
         import __graft_entry__
         __graft_entry__.build()
     dev = torch.device("cuda:0")
-    w = W.CONFIGS[args.config]
-    L = 1
-
-    # ---- inputs (host generation is not timed) -------------------------
-    idx, wt, _ = W.routing(w)
-    hidden = W.hidden(w, workers=16)
     ctx = U.ultraep_create(w.E, w.R, w.S, w.D)
     buf = U.Buffers(ctx, L, w.T, w.k, dev)
-    d_idx = torch.from_numpy(idx).to(dev)
-    d_w = torch.from_numpy(wt).to(dev)
+    if args.config == 3:
+        d_idx = [torch.from_numpy(np.stack([r[0] for r in routes])).to(dev)]
+        d_w = [torch.from_numpy(np.stack([r[1] for r in routes])).to(dev)]
+    else:
+        d_idx = [torch.from_numpy(r[0]).to(dev) for r in routes]
+        d_w = [torch.from_numpy(r[1]).to(dev) for r in routes]
+    n_inst = len(d_idx)
     d_hid = torch.from_numpy(hidden.view(np.int16)).to(dev)
 
-    # one balance to size the permute / fold targets (outside the timing)
-    U.ultraep_balance(ctx, d_idx, w.T, w.k, buf.workspace, buf.plans, buf.phys_idx, buf.pos, L=L)
-    torch.cuda.synchronize()
-    plan = ctx.decode_plan(buf.plans[0].cpu().numpy())
+    def balance(i):
+        U.ultraep_balance(ctx, d_idx[i], w.T, w.k, buf.workspace, buf.plans, buf.phys_idx, buf.pos,
+                          topk_w=d_w[i], inv=buf.inv, w_perm=buf.w_perm, L=L)
+
+    # ---- sizing pass (untimed): every instance's plans, for the permute
+    # segment's capacity, the fold's masters and the quality figures
+    plans = []
+    for i in range(n_inst):
+        balance(i)
+        host = buf.plans.cpu().numpy()
+        plans.append([ctx.decode_plan(host[l]) for l in range(L)])
+    first = plans[0][0]
     P1 = w.M + w.S
-    r_max = int(np.argmax(plan["rank_after"]))
+    r_max = int(np.argmax(first["rank_after"]))
     seg = (r_max * P1, (r_max + 1) * P1)
-    seg_rows = int(plan["phys_off"][seg[1]] - plan["phys_off"][seg[0]])
-    out = torch.empty((seg_rows, w.H), dtype=torch.int16, device=dev)
+    seg_rows = [int(p[0]["phys_off"][seg[1]] - p[0]["phys_off"][seg[0]]) for p in plans]
+    out = torch.empty((max(seg_rows), w.H), dtype=torch.int16, device=dev)
     # fold unit: the redundant slots of the rank with the most filled slots
-    # (lowest such rank); each filled slot is one replica to fold
-    filled = (plan["slot_expert"].reshape(w.R, w.S) >= 0).sum(axis=1)
+    # (lowest such rank) in the first plan.  Every expert those slots hold in
+    # any instance gets a master buffer; the first plan's come from the seeded
+    # generator (the oracle folds those), the others copy the first one.
+    filled = (first["slot_expert"].reshape(w.R, w.S) >= 0).sum(axis=1)
     r_fold = int(np.argmax(filled))
     slots = (r_fold * w.S, (r_fold + 1) * w.S)
-    fold_experts = sorted({int(e) for e in plan["slot_expert"][slots[0]:slots[1]] if e >= 0})
-    n_fold_slots = int(filled[r_fold])
-    masters_h = W.grads(w, max(1, len(fold_experts)), stream=1)
+    held = [p[0]["slot_expert"][slots[0]:slots[1]] for p in plans]
+    first_experts = sorted({int(e) for e in held[0] if e >= 0})
+    all_experts = sorted({int(e) for h in held for e in h if e >= 0})
+    masters_h = W.grads(w, max(1, len(first_experts)), stream=1)
     reps_h = W.grads(w, w.S, stream=2)
-    d_m = torch.from_numpy(masters_h).to(dev)
+    d_m = {e: torch.from_numpy(masters_h[i]).to(dev) for i, e in enumerate(first_experts)}
+    for e in all_experts:
+        if e not in d_m:
+            d_m[e] = d_m[first_experts[0]].clone()
     d_r = torch.from_numpy(reps_h).to(dev)
     table = [0] * w.E
-    for i, e in enumerate(fold_experts):
-        table[e] = d_m[i].data_ptr()
+    for e, t in d_m.items():
+        table[e] = t.data_ptr()
     d_ptrs = torch.tensor(table, dtype=torch.int64, device=dev)
+    n_fold_slots = [int((h >= 0).sum()) for h in held]
+    n_fold_experts = [len({int(e) for e in h if e >= 0}) for h in held]
+    scratch = torch.empty(FLUSH_MIB << 20, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def permute():
+        U.ultraep_permute(ctx, buf.plans[0], buf.inv[0], w.k, d_hid, seg[0], seg[1], out)
+
+    def fold():
+        U.ultraep_fold_grads(ctx, buf.plans[0], d_ptrs, d_r, w.numel, slots[0], slots[1])
+
+    def step(i, ev=None):
         if ev is not None:
             ev[0].record(stream)
-        U.ultraep_balance(ctx, d_idx, w.T, w.k, buf.workspace, buf.plans, buf.phys_idx, buf.pos,
-                          topk_w=d_w, inv=buf.inv, w_perm=buf.w_perm, L=L)
+        balance(i)
         if ev is not None:
             ev[1].record(stream)
+        permute()
+        if ev is not None:
             ev[2].record(stream)
-        U.ultraep_permute(ctx, buf.plans[0], buf.inv[0], w.k, d_hid, seg[0], seg[1], out)
+        fold()
         if ev is not None:
             ev[3].record(stream)
-        U.ultraep_fold_grads(ctx, buf.plans[0], d_ptrs, d_r, w.numel, slots[0], slots[1])
-        if ev is not None:
-            ev[4].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    # ---- timed steps: K steps, synchronised on both sides
+    for s in range(args.warmup):
+        step(s % n_inst)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for s in range(args.steps):
+        step(s % n_inst, events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
 
-    def avg_ms(a, b):
-        return float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+    def ev_ms(evs, a, b):
+        return np.array([e[a].elapsed_time(e[b]) for e in evs])
 
-    t_bal, t_lay, t_perm, t_fold = avg_ms(0, 1), avg_ms(1, 2), avg_ms(2, 3), avg_ms(3, 4)
+    t_bal, t_perm, t_fold = ev_ms(events, 0, 1), ev_ms(events, 1, 2), ev_ms(events, 2, 3)
+    step_insts = [s % n_inst for s in range(args.steps)]
 
-    # algorithmic bytes
-    perm_bytes = seg_rows * (2 * 2 * w.H + 4)                       # read row, write row, read inv
-    fold_bytes = (len(fold_experts) * 2 + n_fold_slots) * w.numel * 4  # masters r+w, replicas r
-    bal_bytes = w.N * (4 + 4 + 4 + 16)   # idx read twice, w read; phys, pos, inv, w_perm written
-    gbps = lambda b, ms: b / (ms * 1e-3) / 1e9                       # noqa: E731
+    # ---- cold and warm repetitions, outside the timed steps
+    def timed(fn, reps, flush):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(reps)]
+        for r in range(reps):
+            if flush:
+                scratch.fill_(r & 0xFF)
+            evs[r][0].record(stream)
+            fn(r)
+            evs[r][1].record(stream)
+        torch.cuda.synchronize()
+        return ev_ms(evs, 0, 1)
 
-    total = plan["total"]
+    bal_cold = timed(lambda r: balance(r % n_inst), n_inst if args.config == 4 else args.cold_reps, True)
+    bal_warm = timed(lambda r: balance(0), args.cold_reps, False)
+    perm_cold = timed(lambda r: permute(), args.cold_reps, True)
+    fold_cold = timed(lambda r: fold(), args.cold_reps, True)
+    del scratch
+
+    # ---- algorithmic bytes
+    row_bytes = 2 * 2 * w.H + 4                            # read row, write row, read inv
+    fold_bytes = [(n_fold_experts[i] * 2 + n_fold_slots[i]) * w.numel * 4 for i in range(n_inst)]
+    bal_bytes = L * w.N * (4 + 4 + 4 + 16)   # idx read twice, w read; phys, pos, inv, w_perm written
+    gbps = lambda b, ms: b / (ms * 1e-3) / 1e9             # noqa: E731
+
+    perm_b = np.array([seg_rows[i] * row_bytes for i in step_insts], dtype=np.float64)
+    fold_b = np.array([fold_bytes[i] for i in step_insts], dtype=np.float64)
+    perm_gbps = float(perm_b.sum() / (t_perm.sum() * 1e-3) / 1e9)
+    fold_gbps = float(fold_b.sum() / (t_fold.sum() * 1e-3) / 1e9)
     ceiling = copy_ceiling(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
-    traffic = recorded_traffic()
+    bal_cold_us = float(np.mean(bal_cold)) * 1e3 / L
     result = {
         "metric": METRIC,
-        "value": w.N / (ms_step * 1e-3),
+        "value": L * w.N / (ms_step * 1e-3),
         "unit": "pairs/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -235,33 +413,41 @@ def main():
         "dtype": "int32+bf16+f32",
         "data": "synthetic",
         "config": {"workload": w.name, "E": w.E, "R": w.R, "S": w.S, "D": w.D, "top_k": w.k,
-                   "tokens_per_rank": w.T, "hidden": w.H, "layers_per_step": L,
-                   "permute_segment": f"rank {r_max} ({seg_rows} rows)",
-                   "fold": f"rank {r_fold} slots {slots[0]}..{slots[1] - 1} ({n_fold_slots} filled), "
+                   "tokens_per_rank": w.T, "hidden": w.H, "layers_per_step": L, "instances": n_inst,
+                   "permute_segment": f"rank {r_max} of the first layer ({seg_rows[0]} rows)",
+                   "fold": f"rank {r_fold} slots {slots[0]}..{slots[1] - 1} ({n_fold_slots[0]} filled), "
                            f"{w.fold_rows}x{w.fold_cols} fp32 per slot",
                    "parallelism": "1 GPU; EP group simulated as logical ranks"},
-        "balance_reroute_us_per_layer": (t_bal + t_lay) * 1e3 / L,
-        "routed_pairs_per_s_balance_layout": w.N / ((t_bal + t_lay) * 1e-3),
-        "balance_layout_GBps": gbps(bal_bytes, t_bal + t_lay),
-        "permute_us": t_perm * 1e3,
-        "permute_GBps": gbps(perm_bytes, t_perm),
-        "permute_frac_of_peak": gbps(perm_bytes, t_perm) / HBM_PEAK_GBPS,
-        "fold_us": t_fold * 1e3,
-        "fold_GBps": gbps(fold_bytes, t_fold),
-        "fold_frac_of_peak": gbps(fold_bytes, t_fold) / HBM_PEAK_GBPS,
-        "imbalance_before": plan["rank_before"].max() * w.R / total,
-        "imbalance_after": plan["rank_after"].max() * w.R / total,
-        "replicas": plan["replicas"],
+        "balance_reroute_us_per_layer": bal_cold_us,
+        "balance_reroute_us_per_layer_warm": float(np.mean(bal_warm)) * 1e3 / L,
+        "balance_reroute_us_per_layer_in_step": float(np.mean(t_bal)) * 1e3 / L,
+        "routed_pairs_per_s_balance_layout": w.N / (bal_cold_us * 1e-6),
+        "balance_layout_GBps": gbps(bal_bytes, float(np.mean(bal_cold))),
+        "permute_us": float(np.mean(t_perm)) * 1e3,
+        "permute_us_cold": float(np.mean(perm_cold)) * 1e3,
+        "permute_GBps": perm_gbps,
+        "permute_frac_of_peak": perm_gbps / HBM_PEAK_GBPS,
+        "fold_us": float(np.mean(t_fold)) * 1e3,
+        "fold_us_cold": float(np.mean(fold_cold)) * 1e3,
+        "fold_GBps": fold_gbps,
+        "fold_GBps_cold": gbps(fold_bytes[0], float(np.mean(fold_cold))),
+        "fold_frac_of_peak": fold_gbps / HBM_PEAK_GBPS,
         "hbm_copy_ceiling_GBps": ceiling,
-        "permute_frac_of_copy_ceiling": gbps(perm_bytes, t_perm) / ceiling if ceiling else None,
-        "roofline": {"bound": "hbm", "kernel": "permute_kernel", "achieved": gbps(perm_bytes, t_perm),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps(perm_bytes, t_perm) / HBM_PEAK_GBPS, "traffic": traffic,
-                     "algorithmic_bytes_per_launch": perm_bytes},
+        "permute_frac_of_copy_ceiling": perm_gbps / ceiling if ceiling else None,
+        "roofline": {"bound": "hbm", "kernel": "permute_kernel", "achieved": perm_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": perm_gbps / HBM_PEAK_GBPS,
+                     "traffic": recorded_traffic(args.config),
+                     "algorithmic_bytes_per_launch": float(perm_b.mean())},
+        "host": host_info(),
     }
+    if args.config == 4:
+        per = bal_cold * 1e3
+        result["balance_reroute_us_per_layer_cold_median_p99"] = [float(np.median(per)),
+                                                                  float(np.percentile(per, 99))]
+    result.update(quality(ctx, [p[l] for p in plans for l in range(L)], w))
     if not args.no_cpu_baseline:
-        masters = {e: masters_h[i] for i, e in enumerate(fold_experts)}
-        result["cpu_baseline"] = cpu_baseline(w, idx, wt, hidden, seg, masters, reps_h, slots,
+        masters = {e: masters_h[i] for i, e in enumerate(first_experts)}
+        result["cpu_baseline"] = cpu_baseline(w, L, routes, hidden, seg, masters, reps_h, slots,
                                               args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

@@ -38,7 +38,8 @@
  *   - Every call is ordered on the given stream (a hipStream_t passed as
  *     void*, NULL = the null stream), never synchronises the host, and reads
  *     data-dependent sizes from the device plan, so the sequence can be
- *     captured in a HIP graph ([README] principles: "CUDA graph" support).
+ *     captured in a HIP graph ([README] design principles: graph capture
+ *     is supported).
  *   - Return value: ULTRAEP_OK or a negative status (below).  Argument checks
  *     happen on the host before anything is launched; on error nothing is
  *     launched and outputs are untouched.  Data-dependent conditions that
@@ -89,10 +90,10 @@ typedef struct ultraep_options {
  * redundant slots per rank).
  * Rules: E % R == 0, R % D == 0, 1 <= E <= ULTRAEP_MAX_EXPERTS,
  * E/R <= ULTRAEP_MAX_MASTERS, 0 <= S <= ULTRAEP_MAX_SLOTS,
- * 1 <= D <= ULTRAEP_MAX_DOMAIN, R*S <= ULTRAEP_MAX_TOTAL_SLOTS, and the
- * per-workgroup tables (E experts, E + R*S instances) must fit one CU's
- * 160 KiB of LDS, which holds whenever E + R*S <= 1792 (EUNSUPPORTED
- * otherwise).
+ * 1 <= D <= ULTRAEP_MAX_DOMAIN, R*S <= ULTRAEP_MAX_TOTAL_SLOTS (EINVAL for a
+ * broken rule, EUNSUPPORTED beyond a limit).  Within these limits every
+ * kernel's per-workgroup tables fit one CU's 160 KiB of LDS; the check is
+ * still made and fails with EUNSUPPORTED.
  * opt may be NULL (defaults).  *out receives a host object the caller frees
  * with ultraep_destroy.  No HIP call is made. */
 int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,

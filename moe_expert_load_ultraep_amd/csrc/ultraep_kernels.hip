@@ -768,7 +768,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 // consecutive lanes on consecutive rows, instead of one 4-byte scatter per
 // pair.
 struct RerouteLds {
-  unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids
+  unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids (pass 1)
   int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
   int32_t* tcnt;   // [E] the tile's ordinal base of e, then the tile's pairs of e
   int32_t* kfirst; // [E] first instance of e that holds ordinals of this tile
@@ -781,12 +781,19 @@ struct RerouteLds {
   int32_t* tmp;    // [waves + 1]
   float* wt;       // [kTile] the tile's routing weights, in pair order
   uint32_t* sp;    // [kTile] staged slot: run index << 16 | pair index inside the tile
+                   // (pass 2; shares its words with peers, which pass 1 is done with)
 };
 
+// Words of the region that holds peers, and with the layout also sp.
+__host__ __device__ inline size_t reroute_shared_words(int E, bool layout, int waves) {
+  const size_t peers = 2ull * waves * (E + 1);
+  return layout && peers < static_cast<size_t>(kTile) ? kTile : peers;
+}
+
 __host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layout, int waves) {
-  size_t words = 2ull * waves * (E + 1) + static_cast<size_t>(waves) * E + 2ull * E + (E + 1) +
-                 3ull * n_inst;
-  if (layout) words += (n_inst + 1) + n_inst + (waves + 1) + 2ull * kTile;
+  size_t words = reroute_shared_words(E, layout, waves) + static_cast<size_t>(waves) * E + 2ull * E +
+                 (E + 1) + 3ull * n_inst;
+  if (layout) words += (n_inst + 1) + n_inst + (waves + 1) + kTile;
   return 4 * words;
 }
 
@@ -803,7 +810,9 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
   RerouteLds S;
   {
     int32_t* q = lds;
-    S.peers = reinterpret_cast<unsigned long long*>(q); q += 2 * W * (E + 1);
+    S.peers = reinterpret_cast<unsigned long long*>(q);
+    S.sp = reinterpret_cast<uint32_t*>(q);
+    q += reroute_shared_words(E, LAYOUT, W);
     S.cntw = q; q += W * E;
     S.tcnt = q; q += E;
     S.kfirst = q; q += E;
@@ -815,8 +824,7 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
       S.roff = q; q += n_inst + 1;
       S.ro0 = q; q += n_inst;
       S.tmp = q; q += W + 1;
-      S.wt = reinterpret_cast<float*>(q); q += kTile;
-      S.sp = reinterpret_cast<uint32_t*>(q);
+      S.wt = reinterpret_cast<float*>(q);
     }
   }
   const int64_t blk = blockIdx.x;

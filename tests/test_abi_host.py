@@ -48,7 +48,6 @@ def test_status_strings():
     (64, 64, 9, 64, -2),   # S beyond limit
     (256, 128, 1, 128, -2),  # D beyond one wave
     (1024, 1024, 2, 64, -2),  # R*S beyond limit
-    (1024, 1024, 1, 64, -2),  # E + R*S beyond one CU's LDS
 ])
 def test_create_rejects(E, R, S, D, code):
     with pytest.raises(U.UltraEPError) as ei:
@@ -56,7 +55,7 @@ def test_create_rejects(E, R, S, D, code):
     assert ei.value.status == code
 
 
-@pytest.mark.parametrize("E,R,S,D", [(1024, 512, 1, 64), (512, 512, 2, 64), (1024, 64, 8, 64),
+@pytest.mark.parametrize("E,R,S,D", [(1024, 1024, 1, 64), (1024, 512, 2, 64), (1024, 64, 8, 64),
                                      (256, 64, 2, 64), (160, 40, 3, 8), (8, 4, 1, 4)])
 def test_create_accepts_limits(E, R, S, D):
     U.ultraep_create(E, R, S, D).close()

@@ -106,6 +106,7 @@ def test_hand_worked_plans_on_gpu():
     (1024, 64, 8, 64, 512, 16, 0.0, False),    # M = 16, S = 8 (largest register tiles)
     (512, 512, 2, 64, 32, 8, 0.0, False),      # R*S = 1024 (slot limit), 8 domains
     (1024, 512, 1, 64, 32, 8, 0.0, False),     # E = 1024 with 512 slots
+    (1024, 1024, 1, 64, 16, 8, 0.0, False),    # E = 1024 and R*S = 1024 together
     (512, 512, 1, 8, 32, 8, 0.0, False),       # 64 domains: more items than waves
     (160, 40, 3, 8, 1000, 8, 0.0, False),
 ])
