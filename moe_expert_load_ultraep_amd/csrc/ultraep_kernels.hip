@@ -55,6 +55,26 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return max(max(readlane(x, 0), readlane(x, 16)), max(readlane(x, 32), readlane(x, 48)));
 }
 
+// Wave-wide max left in lane 63 and returned through one read-lane: the row
+// maxima are combined by DPP row broadcasts (lane 15 into rows 1 and 3, then
+// lane 31 into rows 2 and 3) instead of four read-lanes and scalar maxima,
+// which shortens the dependent chain.  Every lane must be active.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v),
+                                                           CTRL, ROWS, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t wave_max_bcast(uint32_t x) {
+  x = max(x, dpp<0xB1>(x));             // quad_perm [1,0,3,2]
+  x = max(x, dpp<0x4E>(x));             // quad_perm [2,3,0,1]
+  x = max(x, dpp<0x141>(x));            // row_half_mirror
+  x = max(x, dpp<0x140>(x));            // row_mirror: every lane holds its row's max
+  x = max(x, dpp_rows<0x142, 0xA>(x));  // row_bcast:15 -> rows 1, 3
+  x = max(x, dpp_rows<0x143, 0xC>(x));  // row_bcast:31 -> rows 2, 3
+  return readlane(x, 63);
+}
+
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
   x = min(x, dpp<0xB1>(x));
   x = min(x, dpp<0x4E>(x));
@@ -211,7 +231,7 @@ struct PlanParams {
 };
 
 enum Scalar {
-  kTotal = 0, kQmax, kFloor, kQlb, kTol, kK, kWin, kReplicas, kScalars = 16
+  kTotal = 0, kQmax, kFloor, kQlb, kTol, kK, kWin, kReplicas, kCmax, kScalars = 16
 };
 
 struct PlanLds {
@@ -281,16 +301,20 @@ __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
 //          filled and the rest queued;
 //  fail    else.
 // Each step fills a slot, so at most D*S steps run.
-template <int MMAX, int SMAX>
-__device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLds& L,
-                             int32_t* res_e, int32_t* res_q) {
-  const int lane = lane_id();
-  const int D = a.D, M = a.M, S = a.S;
-  const bool act = lane < D;
-  const int r = d * D + lane;
-  const int32_t Hr = act ? L.H[r] : 0;
+//
+// Two implementations of the same greedy follow.  greedy_probe_packed folds
+// each selection's value and its tie-break (lane, queue index) into one
+// 32-bit key, so a pick is one wave reduction; it needs every piece below
+// 2^(26 - log2 MMAX) pairs and Q below 2^25.  greedy_probe makes the same
+// picks with a value reduction followed by a ballot for the lowest tied
+// lane, for any size.
 
-  int32_t pa[MMAX], room[MMAX];
+// shed: the pieces rank r (lane) queues at quota Q and the room left on each
+// of its experts; false when some rank of the domain cannot shed enough.
+template <int MMAX>
+__device__ bool shed_pieces(int32_t Q, bool act, int r, int32_t Hr, const PlanParams& a,
+                            const PlanLds& L, int32_t (&pa)[MMAX], int32_t (&room)[MMAX]) {
+  const int M = a.M;
 #pragma unroll
   for (int j = 0; j < MMAX; ++j) {
     pa[j] = 0;
@@ -327,7 +351,19 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
     }
     fail = X > 0;
   }
-  if (ballot(fail)) return false;
+  return ballot(fail) == 0;
+}
+
+template <int MMAX, int SMAX>
+__device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLds& L,
+                             int32_t* res_e, int32_t* res_q) {
+  const int lane = lane_id();
+  const int D = a.D, M = a.M, S = a.S;
+  const bool act = lane < D;
+  const int r = d * D + lane;
+  const int32_t Hr = act ? L.H[r] : 0;
+  int32_t pa[MMAX], room[MMAX];
+  if (!shed_pieces<MMAX>(Q, act, r, Hr, a, L, pa, room)) return false;
 
   int32_t spare = act ? max(0, Q - Hr) : 0;
   int32_t nh = act ? 0 : S;  // filled slots; inactive lanes look full
@@ -447,6 +483,126 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
   return false;
 }
 
+constexpr int ilog2_c(int x) { return x <= 1 ? 0 : 1 + ilog2_c(x / 2); }
+
+template <int MMAX, int SMAX>
+__device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const PlanLds& L,
+                                    int32_t* res_e, int32_t* res_q) {
+  // queue keys: pairs << TB | (TMASK - (lane * MMAX + j)); the largest key
+  // is the largest piece, ties to the lowest expert id (lane, then j)
+  constexpr int TB = 6 + ilog2_c(MMAX);
+  constexpr uint32_t TMASK = (1u << TB) - 1;
+  // receiver keys: (fit ? 2^25 | (2^25 - 1 - spare) : spare) << 6 | (63 - lane)
+  constexpr uint32_t kFitBit = 1u << 25;
+  const int lane = lane_id();
+  const int D = a.D, M = a.M, S = a.S;
+  const bool act = lane < D;
+  const int r = d * D + lane;
+  const int32_t Hr = act ? L.H[r] : 0;
+  int32_t pa[MMAX], room[MMAX];
+  if (!shed_pieces<MMAX>(Q, act, r, Hr, a, L, pa, room)) return false;
+
+  const uint32_t tie0 = TMASK - static_cast<uint32_t>(lane * MMAX);
+  int32_t spare = act ? max(0, Q - Hr) : 0;
+  int32_t nh = act ? 0 : S;  // filled slots; inactive lanes look full
+  int32_t he[SMAX], hq[SMAX];
+#pragma unroll
+  for (int s = 0; s < SMAX; ++s) {
+    he[s] = -1;
+    hq[s] = 0;
+  }
+  auto place = [&](int who, int32_t e, int32_t x) {
+    const bool me = lane == who;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      const bool here = me && s == nh;
+      he[s] = here ? e : he[s];
+      hq[s] = here ? x : hq[s];
+    }
+    nh += me ? 1 : 0;
+  };
+
+  const int max_steps = D * S + 1;
+  for (int step = 0; step <= max_steps; ++step) {
+    uint32_t mk = 0;
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j)
+      mk = max(mk, pa[j] > 0 ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u);
+    const uint32_t km = wave_max_bcast(mk);
+    if (km == 0) {
+      if (act) {
+#pragma unroll
+        for (int s = 0; s < SMAX; ++s)
+          if (s < S) {
+            res_e[lane * S + s] = he[s];
+            res_q[lane * S + s] = hq[s];
+          }
+      }
+      return true;
+    }
+    const uint32_t t = TMASK - (km & TMASK);
+    const int owner = static_cast<int>(t / MMAX), jsel = static_cast<int>(t % MMAX);
+    const int32_t e = (d * D + owner) * M + jsel;
+    int32_t amt = static_cast<int32_t>(km >> TB);
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? 0 : pa[j];
+    bool hosts = false;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) hosts |= (he[s] == e);
+    const bool elig = lane != owner && nh < S && !hosts;
+    const uint32_t core = spare >= amt ? (kFitBit | (kFitBit - 1 - static_cast<uint32_t>(spare)))
+                                       : static_cast<uint32_t>(spare);
+    const uint32_t key = (elig && spare > 0) ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
+    uint32_t dk = 0;
+#pragma unroll
+    for (int j = 0; j < MMAX; ++j)
+      dk = max(dk, (elig && pa[j] > 0 && room[j] > 0)
+                       ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u);
+    const uint32_t kmax = wave_max_bcast(key);
+    const uint32_t dmax = wave_max_bcast(dk);
+    const int kl = 63 - static_cast<int>(kmax & 63);
+    if (kmax & (kFitBit << 6)) {  // fit
+      spare -= lane == kl ? amt : 0;
+      place(kl, e, amt);
+      continue;
+    }
+    const int32_t rmax = static_cast<int32_t>(kmax >> 6);  // roomiest spare (0: none)
+    if (dmax > 0) {  // chain through the donor's rank
+      const uint32_t dt = TMASK - (dmax & TMASK);
+      const int dl = static_cast<int>(dt / MMAX), djs = static_cast<int>(dt % MMAX);
+      if (rmax > 0) {
+        place(kl, e, rmax);
+        spare = lane == kl ? 0 : spare;
+        amt -= rmax;
+      }
+      int32_t myroom = 0;
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
+      const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
+      const int32_t x = min(amt, droom);
+      place(dl, e, x);
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j) {
+        const bool here = lane == dl && j == djs;
+        pa[j] += here ? x : 0;
+        room[j] -= here ? x : 0;
+      }
+      amt -= x;
+    } else if (rmax > 0) {  // fill the roomiest receiver
+      place(kl, e, rmax);
+      spare = lane == kl ? 0 : spare;
+      amt -= rmax;
+    } else {
+      return false;
+    }
+    if (amt > 0) {
+#pragma unroll
+      for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? amt : pa[j];
+    }
+  }
+  return false;
+}
+
 // Tile ordinal bases for the experts [e0, e0 + ew) of one layer: base[t][e]
 // = number of pairs of e in tiles before t.  Thread (el, ch) sums a
 // contiguous run of tiles of one expert, the runs are scanned in LDS, and the
@@ -551,7 +707,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   // -- phase 1: home loads, total, grid (wave 0, wave reductions only: LDS
   // atomics on one address would be serialised lane by lane).
   if (wave == 0) {
-    uint32_t total = 0, qmax = 0, floor = 0;
+    uint32_t total = 0, qmax = 0, floor = 0, cmax = 0;
+    for (int e0 = 0; e0 < E; e0 += 64)
+      cmax = max(cmax, wave_max(e0 + lane < E ? static_cast<uint32_t>(L.c[e0 + lane]) : 0u));
     for (int r0 = 0; r0 < R; r0 += 64) {
       const int r = r0 + lane;
       int32_t h = 0;
@@ -585,10 +743,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       L.scal[kTol] = tol;
       L.scal[kK] = static_cast<int32_t>(qmax) > qlb ? (static_cast<int32_t>(qmax) - qlb + tol - 1) / tol : 0;
       L.scal[kReplicas] = 0;
+      L.scal[kCmax] = static_cast<int32_t>(cmax);
     }
   }
   __syncthreads();
   const int32_t qlb = L.scal[kQlb], tol = L.scal[kTol], K = L.scal[kK], qmax = L.scal[kQmax];
+  const int32_t cmax = L.scal[kCmax];
 
   // -- phase 2: probe rounds; each wave takes (grid quota, domain) items.
   const bool no_moves = (S == 0 || D == 1);
@@ -602,8 +762,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       bool okv = false;
       if (g <= K) {
         const int32_t Q = g < K ? qlb + g * tol : qmax;
-        okv = greedy_probe<MMAX, SMAX>(Q, d, a, L, L.res + static_cast<size_t>(item) * D * S,
-                                       L.res + static_cast<size_t>(a.items + item) * D * S);
+        int32_t* re = L.res + static_cast<size_t>(item) * D * S;
+        int32_t* rq = L.res + static_cast<size_t>(a.items + item) * D * S;
+        constexpr uint32_t kPieceLimit = 1u << (26 - ilog2_c(MMAX));
+        okv = (static_cast<uint32_t>(cmax) < kPieceLimit && Q < (1 << 25))
+                  ? greedy_probe_packed<MMAX, SMAX>(Q, d, a, L, re, rq)
+                  : greedy_probe<MMAX, SMAX>(Q, d, a, L, re, rq);
       }
       if (lane == 0) L.ok[item] = okv ? 1 : 0;
     }

@@ -127,6 +127,24 @@ def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero, fused):
     check_plan_invariants(pl, pl.c, allow_zero)
 
 
+def test_large_counts_take_the_unpacked_probe():
+    """One expert with more than 2^22 pairs at 16 masters per rank: the
+    planner's packed selection keys cannot hold such pieces, so it takes its
+    general selection path; the plan must be the same."""
+    E, R, S, D, T, k = 64, 4, 1, 4, 1_200_000, 1
+    say(f"large counts E={E} R={R} T={T}")
+    rng = np.random.default_rng([64, 4, 1, 4, 1_200_000])
+    p = np.full(E, 0.1 / (E - 1))
+    p[5] = 0.9
+    idx = rng.choice(E, size=(R * T, k), p=p).astype(np.int32)
+    assert np.bincount(idx.ravel(), minlength=E).max() >= 1 << 22
+    wt = rng.random((R * T, k)).astype(np.float32)
+    ctx = U.ultraep_create(E, R, S, D)
+    got = run_balance(ctx, idx[None], wt[None], T, k)
+    pl, _, _ = assert_layer_equal(ctx, got, 0, idx, wt, E, R, S, D)
+    check_plan_invariants(pl, pl.c, False)
+
+
 def test_determinism_and_streams():
     """Two runs on different streams give bit-identical results."""
     w = W.SINGLE.with_(T=1024)
