@@ -3,5 +3,6 @@
 Only the test suite, the package smoke check and the benchmark's CPU
 baseline may import this package; the product path never does.
 """
-from .ultraep_oracle import (Plan, balance, count, feasible, fold, layout, ordinals,  # noqa: F401
-                             permute, plan, quota_grid, reroute)
+from .ultraep_oracle import (Plan, balance, bf16_bits_to_f64, combine, combine_backward,  # noqa: F401
+                             count, f64_to_bf16_bits, feasible, fold, layout, ordinals, permute,
+                             plan, quota_grid, reroute)

@@ -432,3 +432,87 @@ def balance(topk_idx: np.ndarray, E: int, R: int, S: int, D: int, **opts):
     pl = plan(c, E, R, S, D, dropped=dropped, **opts)
     phys, pos = reroute(topk_idx, pl)
     return pl, phys, pos
+
+
+# ---------------------------------------------------------------------------
+# combine, and the gradient gathers of the backward pass
+# ---------------------------------------------------------------------------
+# [README] Interface, "Forward and backward": after the experts run on the
+# dispatched rows, combine brings each token's k expert outputs back to the
+# token, weighted by its routing probabilities; in the backward pass reroute
+# gathers the gradients of the physical replicas back to the logical experts.
+# With routing held as (token, k) pairs the weights stay attached to their
+# pair, so the gradient of each pair's weight comes back in pair order; the
+# token gradient of the dispatch is the sum of its k rows' gradients.
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Values of bf16 bit patterns (a bf16 is the top half of an fp32)."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 (nearest, ties to even) in one step.
+
+    bf16 keeps 8 significand bits and fp32's exponent range: the spacing of
+    bf16 values around |x| in [2^e, 2^(e+1)) is 2^(e-7), and 2^-133 below the
+    smallest normal 2^-126.  Rounding happens on the exact fp64 value, never
+    through an intermediate fp32.  Finite inputs only; results beyond the
+    largest bf16 become infinities.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    mag = np.abs(x)
+    e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    spacing = np.exp2(np.maximum(e - 7, -133.0))
+    q = np.rint(x / spacing) * spacing           # rint: halves go to even
+    q32 = q.astype(np.float32)                   # exact: q has <= 8 significant bits
+    return (q32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def combine(rows_bits: np.ndarray, pos: np.ndarray, topk_w: Optional[np.ndarray], k: int,
+            token_begin: int, token_end: int) -> np.ndarray:
+    """y[g] = sum_j w[g, j] * rows[pos[g*k + j]] for g in [token_begin, token_end), in fp64.
+
+    rows_bits: the expert outputs in layout order, bf16 bit patterns
+    [layout_rows, H].  Pairs whose pos is outside [0, layout_rows) (dropped
+    pairs) add nothing.  With topk_w None every weight is 1: the sum of a
+    token's k row gradients, which is the backward of the dispatch gather.
+    """
+    rows = bf16_bits_to_f64(rows_bits)
+    nrows, H = rows.shape
+    p = np.asarray(pos).reshape(-1).astype(np.int64)
+    w = None if topk_w is None else np.asarray(topk_w, dtype=np.float64).reshape(-1)
+    out = np.zeros((token_end - token_begin, H), dtype=np.float64)
+    for g in range(token_begin, token_end):
+        for j in range(k):
+            n = g * k + j
+            if 0 <= p[n] < nrows:
+                out[g - token_begin] += (1.0 if w is None else w[n]) * rows[p[n]]
+    return out
+
+
+def combine_backward(rows_bits: np.ndarray, pos: np.ndarray, topk_w: np.ndarray, k: int,
+                     grad_out_bits: np.ndarray, token_begin: int, token_end: int):
+    """Gradients of combine for the tokens [token_begin, token_end), in fp64.
+
+    grad_out_bits: dL/dy as bf16 bit patterns [token_end - token_begin, H].
+    Returns (grad_rows, grad_w): grad_rows maps each layout row that a pair
+    of the range points to onto w[n] * dy[g] (the gradient of that expert
+    output row); grad_w[g - token_begin, j] = <dy[g], rows[pos[g*k + j]]>
+    (the gradient of the pair's routing weight, in logical pair order), 0
+    for a dropped pair.
+    """
+    rows = bf16_bits_to_f64(rows_bits)
+    nrows = rows.shape[0]
+    dy = bf16_bits_to_f64(grad_out_bits)
+    p = np.asarray(pos).reshape(-1).astype(np.int64)
+    w = np.asarray(topk_w, dtype=np.float64).reshape(-1)
+    grad_rows: Dict[int, np.ndarray] = {}
+    grad_w = np.zeros((token_end - token_begin, k), dtype=np.float64)
+    for g in range(token_begin, token_end):
+        for j in range(k):
+            n = g * k + j
+            if 0 <= p[n] < nrows:
+                grad_rows[int(p[n])] = w[n] * dy[g - token_begin]
+                grad_w[g - token_begin, j] = float(np.dot(dy[g - token_begin], rows[p[n]]))
+    return grad_rows, grad_w

@@ -14,6 +14,7 @@ import pytest
 
 import oracle
 import oracle.ultraep_oracle as base
+import test_oracle_combine as C
 import test_oracle_pins as P
 
 MUTATIONS = [
@@ -47,6 +48,16 @@ MUTATIONS = [
     ("fold in fp32", "acc = np.asarray(master[e], dtype=np.float64).copy()",
      "acc = np.asarray(master[e], dtype=np.float32).copy()"),
     ("fold drops range end", "for s in range(slot_begin, slot_end) if", "for s in range(slot_begin, slot_end - 1) if"),
+    ("combine ignores the weight", "out[g - token_begin] += (1.0 if w is None else w[n]) * rows[p[n]]",
+     "out[g - token_begin] += rows[p[n]]"),
+    ("combine keeps rows past the layout", "            if 0 <= p[n] < nrows:\n                out[",
+     "            if 0 <= p[n] <= nrows - 0 and p[n] != -1:\n                out["),
+    ("row gradient without the weight", "grad_rows[int(p[n])] = w[n] * dy[g - token_begin]",
+     "grad_rows[int(p[n])] = dy[g - token_begin]"),
+    ("weight gradient from the pair's own index", "float(np.dot(dy[g - token_begin], rows[p[n]]))",
+     "float(np.dot(dy[g - token_begin], rows[n % nrows]))"),
+    ("bf16 ties round up", "q = np.rint(x / spacing) * spacing", "q = np.floor(x / spacing + 0.5) * spacing"),
+    ("bf16 one bit short", "spacing = np.exp2(np.maximum(e - 7, -133.0))", "spacing = np.exp2(np.maximum(e - 6, -133.0))"),
 ]
 
 PIN_SUBSET = [
@@ -68,6 +79,12 @@ PIN_SUBSET = [
     (P.test_fold_rounds_once_from_fp64, {}),
     (P.test_plan_against_brute_force_optimum_tiny, {"seed": 0}),
     (P.test_topology_floor_is_reached, {}),
+    (C.test_bf16_rounding_fixed_cases, {}),
+    (C.test_combine_matches_dense_matrix_product, {"seed": 0}),
+    (C.test_dropped_pairs_add_nothing, {}),
+    (C.test_combine_backward_is_the_adjoint, {"seed": 0}),
+    (C.test_weight_gradient_is_a_finite_difference, {"seed": 0}),
+    (C.test_unweighted_combine_is_the_adjoint_of_the_dispatch_gather, {}),
 ]
 
 
