@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--workers", type=int, default=16, help="host processes generating inputs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-combine", action="store_true",
+                    help="skip the combine / combine-backward timing (needs two layout-sized buffers)")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size of the device-to-device copy that measures the HBM copy ceiling")
     return ap.parse_args()
@@ -244,6 +246,10 @@ def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s):
             "stage_ms": {k: v * 1e3 for k, v in med.items()}}
 
 
+def gbps_fn(b, ms):
+    return b / (ms * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -385,6 +391,46 @@ def main():
     bal_warm = timed(lambda r: balance(0), args.cold_reps, False)
     perm_cold = timed(lambda r: permute(), args.cold_reps, True)
     fold_cold = timed(lambda r: fold(), args.cold_reps, True)
+
+    # ---- combine and its backward (after the experts; not part of the step):
+    # the tokens of the permuted rank against the whole layout of the first
+    # layer, expert outputs and output gradients drawn on the GPU
+    comb = None
+    if not args.no_combine:
+        total0 = int(first["total"])
+        gen = torch.Generator(device=dev).manual_seed(7)
+        x_rows = torch.randn((total0, w.H), generator=gen, device=dev, dtype=torch.bfloat16).view(torch.int16)
+        g_rows = torch.empty_like(x_rows)
+        g0c, g1c = r_max * w.T, (r_max + 1) * w.T
+        dy = torch.randn((w.T, w.H), generator=gen, device=dev, dtype=torch.bfloat16).view(torch.int16)
+        y = torch.empty((w.T, w.H), dtype=torch.int16, device=dev)
+        gw = torch.empty((w.T, w.k), dtype=torch.float32, device=dev)
+        pos0, w0 = buf.pos[0], d_w[0].reshape(-1)
+        balance(0)
+
+        def comb_fwd(r):
+            U.ultraep_combine(ctx, pos0, w0, w.k, x_rows, g0c, g1c, y)
+
+        def comb_bwd(r):
+            U.ultraep_combine_backward(ctx, pos0, w0, w.k, x_rows, dy, g0c, g1c, g_rows, gw)
+
+        for _ in range(2):
+            comb_fwd(0)
+            comb_bwd(0)
+        t_cf = timed(comb_fwd, args.cold_reps, True)
+        t_cb = timed(comb_bwd, args.cold_reps, True)
+        ctok = g1c - g0c
+        cf_bytes = ctok * (w.k * 2 * w.H + 2 * w.H + w.k * 8)           # rows, out, pos + w
+        cb_bytes = ctok * (2 * w.H + 2 * w.k * 2 * w.H + w.k * 12)      # dy, rows r + w, pos + w + dw
+        comb = {"tokens": f"rank {r_max} ({ctok} tokens x {w.k} rows of the first layer)",
+                "combine_us": float(np.mean(t_cf)) * 1e3,
+                "combine_GBps": gbps_fn(cf_bytes, float(np.mean(t_cf))),
+                "combine_backward_us": float(np.mean(t_cb)) * 1e3,
+                "combine_backward_GBps": gbps_fn(cb_bytes, float(np.mean(t_cb))),
+                "combine_bytes": cf_bytes, "combine_backward_bytes": cb_bytes}
+        comb["combine_frac_of_peak"] = comb["combine_GBps"] / HBM_PEAK_GBPS
+        comb["combine_backward_frac_of_peak"] = comb["combine_backward_GBps"] / HBM_PEAK_GBPS
+        del x_rows, g_rows, dy, y, gw
     del scratch
 
     # ---- algorithmic bytes
@@ -444,6 +490,8 @@ def main():
         per = bal_cold * 1e3
         result["balance_reroute_us_per_layer_cold_median_p99"] = [float(np.median(per)),
                                                                   float(np.percentile(per, 99))]
+    if comb is not None:
+        result["combine"] = comb
     result.update(quality(ctx, [p[l] for p in plans for l in range(L)], w))
     if not args.no_cpu_baseline:
         masters = {e: masters_h[i] for i, e in enumerate(first_experts)}

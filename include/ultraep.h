@@ -8,6 +8,11 @@
  *                            and its row in the replica-contiguous layout
  *   ultraep_dispatch_layout  the layout's inverse index and permuted weights
  *   ultraep_permute          gather bf16 hidden rows into the layout
+ *   ultraep_combine          after the experts: each token's k output rows,
+ *                            weighted, back to the token (unweighted: the
+ *                            backward of ultraep_permute)
+ *   ultraep_combine_backward gradients of combine: expert-output rows and the
+ *                            routing weights in logical (token, k) order
  *   ultraep_fold_grads       fold replica gradients back into their masters
  *
  * Sources, cited by page title and section:
@@ -255,6 +260,48 @@ int ultraep_permute(const ultraep_ctx* ctx, const void* plan, const int32_t* inv
 int ultraep_fold_grads(const ultraep_ctx* ctx, const void* plan, float* const* master_grads,
                        const float* replica_grads, int64_t numel, int32_t slot_begin,
                        int32_t slot_end, void* stream);
+
+/* Combine: bring each token's k expert outputs back to the token, weighted
+ * by its routing weights ([README] Interface, "Forward and backward": the
+ * experts run on the dispatched rows, then combine returns their outputs to
+ * the tokens).  With topk_w NULL the rows are summed unweighted, which is the
+ * backward of ultraep_permute: a token's gradient is the sum of the gradients
+ * of its k dispatched rows.
+ * For every token g in [token_begin, token_end):
+ *   out[g - token_begin] = sum over j of w[g*k + j] * rows[pos[g*k + j]]
+ * summed in fp32 in ascending j and rounded to bf16 (nearest even); pairs
+ * whose pos is outside [0, layout_rows) (dropped pairs) add nothing.
+ * In:  pos [.][k] int32 of the layer (from ultraep_balance), topk_w fp32
+ *      [.][k] or NULL, rows [layout_rows][H] bf16 in layout order (the expert
+ *      outputs; layout_rows = total of the layer's plan, or N).
+ * Out: out [token_end - token_begin][H] bf16.
+ * Errors: EINVAL (null pointers, H <= 0, k outside [1, min(E, 64)], bad token
+ *      range, layout_rows < 0); EUNSUPPORTED (H % 8 != 0, layout_rows >= 2^31,
+ *      rows/out not 16-byte aligned, pos/topk_w not 4-byte aligned). */
+int ultraep_combine(const ultraep_ctx* ctx, const int32_t* pos, const float* topk_w, int32_t k,
+                    const uint16_t* rows, int64_t layout_rows, int32_t H, int64_t token_begin,
+                    int64_t token_end, uint16_t* out, void* stream);
+
+/* Backward of ultraep_combine ([README] Interface, "Forward and backward":
+ * reroute gathers the gradients of the physical replicas back to the logical
+ * experts).  For every pair n = g*k + j of the tokens [token_begin, token_end)
+ * with pos[n] in [0, layout_rows):
+ *   grad_rows[pos[n]]     = w[n] * grad_out[g - token_begin]   (bf16, nearest even)
+ *   grad_topk_w[(g - token_begin)*k + j] = <grad_out[g - token_begin], rows[pos[n]]>
+ * the dot product summed in fp32 (each lane over its columns in order, then
+ * across the wave in a fixed order); a dropped pair gets weight gradient 0
+ * and writes no row.  The weight gradients come back in logical (token, k)
+ * order, the order of topk_w.
+ * In:  pos, topk_w, rows as for ultraep_combine; grad_out
+ *      [token_end - token_begin][H] bf16.
+ * Out: grad_rows [layout_rows][H] bf16 (only the rows the range's pairs point
+ *      to are written), grad_topk_w [token_end - token_begin][k] fp32.
+ * Errors: as ultraep_combine, and EINVAL for a NULL topk_w, grad_out,
+ *      grad_rows or grad_topk_w with a non-empty range. */
+int ultraep_combine_backward(const ultraep_ctx* ctx, const int32_t* pos, const float* topk_w,
+                             int32_t k, const uint16_t* rows, int64_t layout_rows, int32_t H,
+                             const uint16_t* grad_out, int64_t token_begin, int64_t token_end,
+                             uint16_t* grad_rows, float* grad_topk_w, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* ultraep_status_string(int status);

@@ -58,6 +58,8 @@ _SIGNATURES = {
     "ultraep_dispatch_layout": (_I32, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P]),
     "ultraep_permute": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _I32, _I32, _P, _I64, _P]),
     "ultraep_fold_grads": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _P]),
+    "ultraep_combine": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _I64, _I64, _P, _P]),
+    "ultraep_combine_backward": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _P, _P]),
     "ultraep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -184,6 +186,23 @@ def ultraep_fold_grads(ctx: Context, plan, master_ptrs, replica_grads, numel: in
     st = lib().ultraep_fold_grads(ctx.handle, _ptr(plan), _ptr(master_ptrs), _ptr(replica_grads),
                                   numel, slot_begin, slot_end, _stream(stream))
     _check("ultraep_fold_grads", st)
+
+
+def ultraep_combine(ctx: Context, pos, topk_w, k: int, rows, token_begin: int, token_end: int,
+                    out, stream=None) -> None:
+    """out[g - token_begin] = sum_j w[g, j] * rows[pos[g*k + j]] (bf16; topk_w None: unweighted)."""
+    st = lib().ultraep_combine(ctx.handle, _ptr(pos), _ptr(topk_w), k, _ptr(rows), rows.shape[0],
+                               rows.shape[-1], token_begin, token_end, _ptr(out), _stream(stream))
+    _check("ultraep_combine", st)
+
+
+def ultraep_combine_backward(ctx: Context, pos, topk_w, k: int, rows, grad_out, token_begin: int,
+                             token_end: int, grad_rows, grad_topk_w, stream=None) -> None:
+    """grad_rows[pos[n]] = w[n] * grad_out[g]; grad_topk_w[g, j] = <grad_out[g], rows[pos[n]]>."""
+    st = lib().ultraep_combine_backward(ctx.handle, _ptr(pos), _ptr(topk_w), k, _ptr(rows),
+                                        rows.shape[0], rows.shape[-1], _ptr(grad_out), token_begin,
+                                        token_end, _ptr(grad_rows), _ptr(grad_topk_w), _stream(stream))
+    _check("ultraep_combine_backward", st)
 
 
 def status_string(status: int) -> str:

@@ -205,6 +205,48 @@ int ultraep_fold_grads(const ultraep_ctx* ctx, const void* plan, float* const* m
                                        static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// Shared checks of the combine calls: the token range and shapes.
+int combine_checks(const ultraep_ctx* ctx, const int32_t* pos, int32_t k, const uint16_t* rows,
+                   int64_t layout_rows, int32_t H, int64_t token_begin, int64_t token_end) {
+  if (!ctx || !pos) return ULTRAEP_EINVAL;
+  if (H <= 0 || k < 1 || k > ULTRAEP_MAX_TOPK || k > ctx->sh.E || layout_rows < 0) return ULTRAEP_EINVAL;
+  if (token_begin < 0 || token_end < token_begin) return ULTRAEP_EINVAL;
+  if (layout_rows > 0 && !rows) return ULTRAEP_EINVAL;
+  if (H % 8 != 0 || layout_rows >= (int64_t{1} << 31) || token_end > (int64_t{1} << 40) / k ||
+      !aligned(rows, 16) || !aligned(pos, 4))
+    return ULTRAEP_EUNSUPPORTED;
+  return ULTRAEP_OK;
+}
+}  // namespace
+
+int ultraep_combine(const ultraep_ctx* ctx, const int32_t* pos, const float* topk_w, int32_t k,
+                    const uint16_t* rows, int64_t layout_rows, int32_t H, int64_t token_begin,
+                    int64_t token_end, uint16_t* out, void* stream) {
+  const int st = combine_checks(ctx, pos, k, rows, layout_rows, H, token_begin, token_end);
+  if (st != ULTRAEP_OK) return st;
+  if (token_end > token_begin && !out) return ULTRAEP_EINVAL;
+  if (!aligned(out, 16) || !aligned(topk_w, 4)) return ULTRAEP_EUNSUPPORTED;
+  return from_hip(ultraep::launch_combine(pos, topk_w, k, rows, layout_rows, H, token_begin,
+                                          token_end, out, static_cast<hipStream_t>(stream)));
+}
+
+int ultraep_combine_backward(const ultraep_ctx* ctx, const int32_t* pos, const float* topk_w,
+                             int32_t k, const uint16_t* rows, int64_t layout_rows, int32_t H,
+                             const uint16_t* grad_out, int64_t token_begin, int64_t token_end,
+                             uint16_t* grad_rows, float* grad_topk_w, void* stream) {
+  const int st = combine_checks(ctx, pos, k, rows, layout_rows, H, token_begin, token_end);
+  if (st != ULTRAEP_OK) return st;
+  if (token_end > token_begin && (!topk_w || !grad_out || !grad_topk_w)) return ULTRAEP_EINVAL;
+  if (token_end > token_begin && layout_rows > 0 && !grad_rows) return ULTRAEP_EINVAL;
+  if (!aligned(grad_out, 16) || !aligned(grad_rows, 16) || !aligned(topk_w, 4) ||
+      !aligned(grad_topk_w, 4))
+    return ULTRAEP_EUNSUPPORTED;
+  return from_hip(ultraep::launch_combine_backward(pos, topk_w, k, rows, layout_rows, H, grad_out,
+                                                   token_begin, token_end, grad_rows, grad_topk_w,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 const char* ultraep_status_string(int status) {
   switch (status) {
     case ULTRAEP_OK: return "ok";

@@ -49,6 +49,15 @@ hipError_t launch_fold(const Shape& sh, const int32_t* plan, float* const* maste
                        const float* reps, int64_t numel, int32_t slot_begin, int32_t slot_end,
                        hipStream_t st);
 
+// Combine (w null: unweighted sum) and its backward over tokens [g0, g1).
+hipError_t launch_combine(const int32_t* pos, const float* w, int32_t k, const uint16_t* rows,
+                          int64_t layout_rows, int32_t H, int64_t g0, int64_t g1, uint16_t* out,
+                          hipStream_t st);
+hipError_t launch_combine_backward(const int32_t* pos, const float* w, int32_t k,
+                                   const uint16_t* rows, int64_t layout_rows, int32_t H,
+                                   const uint16_t* grad_out, int64_t g0, int64_t g1,
+                                   uint16_t* grad_rows, float* grad_w, hipStream_t st);
+
 // Bytes of dynamic LDS the plan solver / reroute kernel need for this shape.
 size_t plan_lds_bytes(const Shape& sh);
 size_t rerouting_lds_bytes(const Shape& sh, bool layout);

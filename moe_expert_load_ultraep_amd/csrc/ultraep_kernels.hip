@@ -14,89 +14,11 @@
 
 #include <cstdint>
 
+#include "ultraep_device.h"
 #include "ultraep_internal.h"
 
 namespace ultraep {
 namespace {
-
-// ------------------------------------------------------------------------
-// wave64 helpers
-// ------------------------------------------------------------------------
-__device__ __forceinline__ int lane_id() {
-  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-}
-
-__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
-
-// Number of set bits of m in lanes below the calling lane.
-__device__ __forceinline__ int count_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp(uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
-}
-
-__device__ __forceinline__ uint32_t readlane(uint32_t v, int l) {
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), l));
-}
-
-// Wave-wide max / min of an unsigned value; every lane must be active.  The
-// butterfly inside each 16-lane row uses DPP (quad swaps, half-row and row
-// mirrors); the four row results are combined through scalar registers.
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-  x = max(x, dpp<0xB1>(x));   // quad_perm [1,0,3,2]
-  x = max(x, dpp<0x4E>(x));   // quad_perm [2,3,0,1]
-  x = max(x, dpp<0x141>(x));  // row_half_mirror
-  x = max(x, dpp<0x140>(x));  // row_mirror
-  return max(max(readlane(x, 0), readlane(x, 16)), max(readlane(x, 32), readlane(x, 48)));
-}
-
-// Wave-wide max left in lane 63 and returned through one read-lane: the row
-// maxima are combined by DPP row broadcasts (lane 15 into rows 1 and 3, then
-// lane 31 into rows 2 and 3) instead of four read-lanes and scalar maxima,
-// which shortens the dependent chain.  Every lane must be active.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v),
-                                                           CTRL, ROWS, 0xF, false));
-}
-
-__device__ __forceinline__ uint32_t wave_max_bcast(uint32_t x) {
-  x = max(x, dpp<0xB1>(x));             // quad_perm [1,0,3,2]
-  x = max(x, dpp<0x4E>(x));             // quad_perm [2,3,0,1]
-  x = max(x, dpp<0x141>(x));            // row_half_mirror
-  x = max(x, dpp<0x140>(x));            // row_mirror: every lane holds its row's max
-  x = max(x, dpp_rows<0x142, 0xA>(x));  // row_bcast:15 -> rows 1, 3
-  x = max(x, dpp_rows<0x143, 0xC>(x));  // row_bcast:31 -> rows 2, 3
-  return readlane(x, 63);
-}
-
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-  x = min(x, dpp<0xB1>(x));
-  x = min(x, dpp<0x4E>(x));
-  x = min(x, dpp<0x141>(x));
-  x = min(x, dpp<0x140>(x));
-  return min(min(readlane(x, 0), readlane(x, 16)), min(readlane(x, 32), readlane(x, 48)));
-}
-
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-  x += dpp<0xB1>(x);
-  x += dpp<0x4E>(x);
-  x += dpp<0x141>(x);
-  x += dpp<0x140>(x);
-  return readlane(x, 0) + readlane(x, 16) + readlane(x, 32) + readlane(x, 48);
-}
-
-__device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(m); }
-
-// 16-byte vectors as native clang vectors (the nontemporal builtins take
-// these, not HIP's struct vector types).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Lanes of the wave holding the same value v: every lane ORs its lane bit
 // into an LDS word owned by its value, then reads the word back.  LDS
@@ -1164,13 +1086,6 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
 // HBM's channels busy than a few deep ones.
 constexpr int kPermThreads = 256;
 constexpr int kPermUnroll = 4;
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr int kNonTemporal = 2;           // cache policy bit: non-temporal
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                           kBufferWord3);
-}
 
 __device__ __forceinline__ int32_t perm_token(int32_t n, int32_t k, int64_t hidden_rows) {
   const int32_t t = n >= 0 ? n / k : -1;

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(U.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -137,3 +137,34 @@ def test_permute_and_fold_argument_checks():
     lay = U.lib().ultraep_dispatch_layout
     assert lay(ctx.handle, 1, 16, 2, None, FAKE, FAKE, FAKE, None) == -1
     assert lay(ctx.handle, 1, 16, 2, FAKE + 1, FAKE, FAKE, FAKE, None) == -2
+
+
+def test_combine_argument_checks():
+    ctx = U.ultraep_create(8, 4, 1, 4)
+    c = U.lib().ultraep_combine
+    F = FAKE
+    h = ctx.handle
+    #          ctx pos w  k  rows nrows H  g0 g1 out
+    assert c(h, F, F, 2, F, 10, 12, 0, 3, F, None) == -2        # H % 8
+    assert c(h, F, F, 2, F + 8, 10, 16, 0, 3, F, None) == -2    # rows not 16-B aligned
+    assert c(h, F, F, 2, F, 10, 16, 0, 3, F + 8, None) == -2    # out not 16-B aligned
+    assert c(h, F + 2, F, 2, F, 10, 16, 0, 3, F, None) == -2    # pos misaligned
+    assert c(h, F, F, 2, F, 1 << 31, 16, 0, 3, F, None) == -2   # layout rows >= 2^31
+    assert c(h, F, F, 0, F, 10, 16, 0, 3, F, None) == -1        # k = 0
+    assert c(h, F, F, 9, F, 10, 16, 0, 3, F, None) == -1        # k > E
+    assert c(h, F, F, 2, F, 10, 16, 3, 2, F, None) == -1        # empty range reversed
+    assert c(h, F, F, 2, F, 10, -16, 0, 3, F, None) == -1
+    assert c(h, None, F, 2, F, 10, 16, 0, 3, F, None) == -1
+    assert c(h, F, F, 2, None, 10, 16, 0, 3, F, None) == -1     # rows NULL with rows > 0
+    assert c(h, F, F, 2, F, 10, 16, 0, 3, None, None) == -1     # out NULL
+    assert c(h, F, None, 2, F, 10, 16, 3, 3, None, None) == 0   # empty range, unweighted: no-op
+    b = U.lib().ultraep_combine_backward
+    #          ctx pos w  k  rows nrows H  dy g0 g1 grows gw
+    assert b(h, F, None, 2, F, 10, 16, F, 0, 3, F, F, None) == -1   # weights required
+    assert b(h, F, F, 2, F, 10, 16, None, 0, 3, F, F, None) == -1
+    assert b(h, F, F, 2, F, 10, 16, F, 0, 3, None, F, None) == -1
+    assert b(h, F, F, 2, F, 10, 16, F, 0, 3, F, None, None) == -1
+    assert b(h, F, F, 2, F, 10, 16, F + 8, 0, 3, F, F, None) == -2  # grad_out misaligned
+    assert b(h, F, F, 2, F, 10, 16, F, 0, 3, F + 8, F, None) == -2  # grad_rows misaligned
+    assert b(h, F, F, 2, F, 10, 16, F, 0, 3, F, F + 2, None) == -2  # grad_topk_w misaligned
+    assert b(h, F, F, 2, F, 10, 16, F, 4, 4, F, F, None) == 0       # empty range: no-op
