@@ -424,6 +424,86 @@ def fold(master: Dict[int, np.ndarray], replica_grads: np.ndarray, pl: Plan,
 
 
 # ---------------------------------------------------------------------------
+# weight_sync: master weights into the replica slots
+# ---------------------------------------------------------------------------
+RELAY_DIRECT, RELAY_ADAPTIVE, RELAY_FORCE = 0, 1, 2
+
+
+def weight_sync(master: Dict[int, np.ndarray], pl: Plan, slot_begin: int,
+                slot_end: int) -> Dict[int, np.ndarray]:
+    """Replica weights of the slots [slot_begin, slot_end).
+
+    [README] Interface, "Forward and backward": weight_sync materialises the
+    plan by distributing master weights to the replica slots.  Slot s holding
+    expert e receives a bit copy of e's master weights; empty slots get
+    nothing.  Returns {slot: weights}.
+    """
+    return {s: np.array(master[int(pl.slot_expert[s])], copy=True)
+            for s in range(slot_begin, slot_end) if pl.slot_expert[s] >= 0}
+
+
+def replica_slots(pl: Plan, e: int) -> List[int]:
+    """Redundant slots holding expert e, in ascending physical id."""
+    out = []
+    for p, _, _ in pl.instances(e):
+        r, j = divmod(p, pl.M + pl.S)
+        if j >= pl.M:
+            out.append(r * pl.S + (j - pl.M))
+    return out
+
+
+def relay_plan(pl: Plan, mode: int = RELAY_ADAPTIVE, min_replicas: int = 4, max_relays: int = 8,
+               min_gain: int = 2, domain_gpus: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Where each replica slot's weights come from, and in which stage.
+
+    [README] "Performance Tuning", "Expert communication": the weight
+    distribution plan is direct, adaptive or forced relay; adaptive relay
+    needs a minimum replica count per expert, uses at most a maximum number
+    of relays and is taken only for a minimum fan-out gain; plans are direct
+    when the scale-up domain has at most 8 GPUs.  [NEWS] "What problem does
+    UltraEP solve": the relay keeps the master's fan-out from overloading.
+
+    Reading (the pages give the switches, not the schedule): an expert with
+    n replicas either copies all of them from its master in one stage
+    (fan-out n) or picks m relays -- its m lowest-physical-id replicas --
+    that copy from the master in stage 1 while the other n - m copy from the
+    relays in stage 2, relay (i - m) mod m serving the i-th replica.  The
+    critical fan-out is then m + ceil((n - m) / m); m is the smallest value in
+    [1, min(max_relays, n - 1)] that minimises it, and the gain is n over it.
+    Relay is used under RELAY_FORCE (n >= 2), or under RELAY_ADAPTIVE when
+    n >= min_replicas and n >= min_gain * critical fan-out; never when the
+    domain has at most 8 GPUs (domain_gpus defaults to D, one GPU per rank).
+
+    Returns (src, stage), each [R*S]: src -1 = the master, >= 0 = the relay
+    slot, -2 = empty slot; stage 1 or 2, 0 for an empty slot.
+    """
+    if domain_gpus is None:
+        domain_gpus = pl.D
+    nslots = pl.R * pl.S
+    src = np.full(nslots, -2, dtype=np.int64)
+    stage = np.zeros(nslots, dtype=np.int64)
+    for e in range(pl.E):
+        reps = replica_slots(pl, e)
+        n = len(reps)
+        relay = False
+        m = 0
+        if mode != RELAY_DIRECT and domain_gpus > 8 and n >= 2 and max_relays >= 1:
+            best = None
+            for cand in range(1, min(max_relays, n - 1) + 1):
+                cost = cand + _ceil_div(n - cand, cand)
+                if best is None or cost < best[0]:
+                    best = (cost, cand)
+            cost, m = best
+            relay = mode == RELAY_FORCE or (n >= min_replicas and n >= min_gain * cost)
+        for i, s in enumerate(reps):
+            if not relay or i < m:
+                src[s], stage[s] = -1, 1
+            else:
+                src[s], stage[s] = reps[(i - m) % m], 2
+    return src, stage
+
+
+# ---------------------------------------------------------------------------
 # the whole path for one layer
 # ---------------------------------------------------------------------------
 def balance(topk_idx: np.ndarray, E: int, R: int, S: int, D: int, **opts):

@@ -6,6 +6,7 @@ module, swaps it in for ``oracle`` and runs a fast subset of the pins.  The
 test passes only if at least one pin fails on the broken copy.
 """
 import inspect
+import json
 import sys
 import types
 
@@ -15,6 +16,7 @@ import pytest
 import oracle
 import oracle.ultraep_oracle as base
 import test_oracle_combine as C
+import test_oracle_weight_sync as WS
 import test_oracle_pins as P
 
 MUTATIONS = [
@@ -47,7 +49,8 @@ MUTATIONS = [
      "lo, hi = int(pl.phys_off[p_begin]), int(pl.phys_off[p_end - 1])"),
     ("fold in fp32", "acc = np.asarray(master[e], dtype=np.float64).copy()",
      "acc = np.asarray(master[e], dtype=np.float32).copy()"),
-    ("fold drops range end", "for s in range(slot_begin, slot_end) if", "for s in range(slot_begin, slot_end - 1) if"),
+    ("fold drops range end", "slots = [s for s in range(slot_begin, slot_end) if",
+     "slots = [s for s in range(slot_begin, slot_end - 1) if"),
     ("combine ignores the weight", "out[g - token_begin] += (1.0 if w is None else w[n]) * rows[p[n]]",
      "out[g - token_begin] += rows[p[n]]"),
     ("combine keeps rows past the layout", "            if 0 <= p[n] < nrows:\n                out[",
@@ -58,6 +61,12 @@ MUTATIONS = [
      "float(np.dot(dy[g - token_begin], rows[n % nrows]))"),
     ("bf16 ties round up", "q = np.rint(x / spacing) * spacing", "q = np.floor(x / spacing + 0.5) * spacing"),
     ("bf16 one bit short", "spacing = np.exp2(np.maximum(e - 7, -133.0))", "spacing = np.exp2(np.maximum(e - 6, -133.0))"),
+    ("relay count ties to the larger", "if best is None or cost < best[0]:", "if best is None or cost <= best[0]:"),
+    ("relays are the highest-id replicas", "            if not relay or i < m:", "            if not relay or i >= n - m:"),
+    ("relay gain not checked", "(n >= min_replicas and n >= min_gain * cost)", "(n >= min_replicas)"),
+    ("relay ignores the domain size", "domain_gpus > 8 and n >= 2", "domain_gpus > 0 and n >= 2"),
+    ("weight sync from the wrong master", "{s: np.array(master[int(pl.slot_expert[s])], copy=True)",
+     "{s: np.array(master[int(pl.slot_expert[s]) ^ 1], copy=True)"),
 ]
 
 PIN_SUBSET = [
@@ -85,6 +94,9 @@ PIN_SUBSET = [
     (C.test_combine_backward_is_the_adjoint, {"seed": 0}),
     (C.test_weight_gradient_is_a_finite_difference, {"seed": 0}),
     (C.test_unweighted_combine_is_the_adjoint_of_the_dispatch_gather, {}),
+    *[(WS.test_relay_costs_hand_worked, {"case": c}) for c in json.load(open(WS.GOLDEN))["cases"]],
+    (WS.test_relay_schedule_structure_on_workload_plans, {}),
+    (WS.test_weight_sync_copies_bits, {}),
 ]
 
 
