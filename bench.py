@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--workers", type=int, default=16, help="host processes generating inputs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-weight-sync", action="store_true",
+                    help="skip the weight_sync timing (needs master and replica weight buffers)")
     ap.add_argument("--no-combine", action="store_true",
                     help="skip the combine / combine-backward timing (needs two layout-sized buffers)")
     ap.add_argument("--copy-mib", type=int, default=1024,
@@ -431,6 +433,54 @@ def main():
         comb["combine_frac_of_peak"] = comb["combine_GBps"] / HBM_PEAK_GBPS
         comb["combine_backward_frac_of_peak"] = comb["combine_backward_GBps"] / HBM_PEAK_GBPS
         del x_rows, g_rows, dy, y, gw
+
+    # ---- weight_sync: master fc1 / fc2 bf16 weights into the replica slots
+    # of the first layer's plan: the fold rank's slots (one GPU's share) and
+    # every slot of the group, direct and with the adaptive relay plan
+    wsync = None
+    if not args.no_weight_sync and w.ffn > 0:
+        balance(0)
+        numels = (2 * w.H * w.ffn, w.H * w.ffn)
+        gen = torch.Generator(device=dev).manual_seed(11)
+        mast = [torch.randint(-32768, 32767, (w.E, n), generator=gen, dtype=torch.int16, device=dev)
+                for n in numels]
+        ptrs = [torch.tensor([m[e].data_ptr() for e in range(w.E)], dtype=torch.int64, device=dev)
+                for m in mast]
+        nslot = w.R * w.S
+        reps_w = [torch.empty((nslot, n), dtype=torch.int16, device=dev) for n in numels]
+        relay = torch.empty((2, nslot), dtype=torch.int32, device=dev)
+        U.ultraep_weight_sync_plan(ctx, buf.plans[0], relay)
+        slot_e = first["slot_expert"]
+
+        def ws(s0, s1, rl):
+            for q in range(2):
+                U.ultraep_weight_sync(ctx, buf.plans[0], ptrs[q], reps_w[q][s0:s1] if rl is None else reps_w[q],
+                                      numels[q], s0, s1, relay=rl)
+
+        def ws_bytes(s0, s1):
+            held = [int(e) for e in slot_e[s0:s1] if e >= 0]
+            return sum(n * 2 * (len(held) + len(set(held))) for n in numels)
+
+        for _ in range(2):
+            ws(slots[0], slots[1], None)
+            ws(0, nslot, None)
+            ws(0, nslot, relay)
+        t_rank = timed(lambda r: ws(slots[0], slots[1], None), args.cold_reps, True)
+        t_all = timed(lambda r: ws(0, nslot, None), args.cold_reps, True)
+        t_rel = timed(lambda r: ws(0, nslot, relay), args.cold_reps, True)
+        rel = relay.cpu().numpy()
+        b_rank, b_all = ws_bytes(slots[0], slots[1]), ws_bytes(0, nslot)
+        wsync = {"expert_weights": f"fc1 2x{w.H}x{w.ffn} + fc2 {w.H}x{w.ffn} bf16 per expert",
+                 "rank_slots_us": float(np.mean(t_rank)) * 1e3,
+                 "rank_slots_GBps": gbps_fn(b_rank, float(np.mean(t_rank))),
+                 "all_slots_us": float(np.mean(t_all)) * 1e3,
+                 "all_slots_GBps": gbps_fn(b_all, float(np.mean(t_all))),
+                 "all_slots_relay_us": float(np.mean(t_rel)) * 1e3,
+                 "relayed_slots": int((rel[1] == 2).sum()), "filled_slots": int((rel[1] > 0).sum()),
+                 "rank_slots_bytes": b_rank, "all_slots_bytes": b_all}
+        wsync["all_slots_frac_of_peak"] = wsync["all_slots_GBps"] / HBM_PEAK_GBPS
+        wsync["rank_slots_frac_of_peak"] = wsync["rank_slots_GBps"] / HBM_PEAK_GBPS
+        del mast, ptrs, reps_w, relay
     del scratch
 
     # ---- algorithmic bytes
@@ -492,6 +542,8 @@ def main():
                                                                   float(np.percentile(per, 99))]
     if comb is not None:
         result["combine"] = comb
+    if wsync is not None:
+        result["weight_sync"] = wsync
     result.update(quality(ctx, [p[l] for p in plans for l in range(L)], w))
     if not args.no_cpu_baseline:
         masters = {e: masters_h[i] for i, e in enumerate(first_experts)}

@@ -13,6 +13,8 @@
  *                            backward of ultraep_permute)
  *   ultraep_combine_backward gradients of combine: expert-output rows and the
  *                            routing weights in logical (token, k) order
+ *   ultraep_weight_sync_plan the relay schedule of the master -> replica copies
+ *   ultraep_weight_sync      copy master weights into the replica slots
  *   ultraep_fold_grads       fold replica gradients back into their masters
  *
  * Sources, cited by page title and section:
@@ -88,6 +90,25 @@ typedef struct ultraep_options {
   int32_t allow_zero_master;
   int32_t reserved[5]; /* must be zero */
 } ultraep_options;
+
+/* Weight-distribution plan of ultraep_weight_sync_plan ([README]
+ * "Performance Tuning", "Expert communication": the plan mode is direct,
+ * adaptive or forced relay; adaptive relay needs a minimum replica count per
+ * expert and a minimum fan-out gain and uses at most a maximum number of
+ * relays; plans are direct when the scale-up domain has at most 8 GPUs).
+ * NULL options mean: adaptive, min_replicas 4, max_relays 8, min_gain 2,
+ * domain_gpus = D. */
+#define ULTRAEP_RELAY_DIRECT 0
+#define ULTRAEP_RELAY_ADAPTIVE 1
+#define ULTRAEP_RELAY_FORCE 2
+typedef struct ultraep_relay_options {
+  int32_t mode;         /* ULTRAEP_RELAY_* */
+  int32_t min_replicas; /* adaptive: relay only experts with at least this many replicas */
+  int32_t max_relays;   /* at most this many relays per expert (>= 1 to relay at all) */
+  int32_t min_gain;     /* adaptive: relay only if replicas >= min_gain * relayed fan-out */
+  int32_t domain_gpus;  /* GPUs of the scale-up domain; <= 8 forces direct */
+  int32_t reserved[3];  /* must be zero */
+} ultraep_relay_options;
 
 /* Create a planning context for E experts over R ranks with S redundant slots
  * per rank and scale-up domains of D ranks ([README] Interface,
@@ -302,6 +323,50 @@ int ultraep_combine_backward(const ultraep_ctx* ctx, const int32_t* pos, const f
                              int32_t k, const uint16_t* rows, int64_t layout_rows, int32_t H,
                              const uint16_t* grad_out, int64_t token_begin, int64_t token_end,
                              uint16_t* grad_rows, float* grad_topk_w, void* stream);
+
+/* The relay schedule of the plan's replica slots (see ultraep_relay_options).
+ * Reading of the pages' switches: an expert with n replicas either copies
+ * all of them from its master in one stage (fan-out n) or names its m
+ * lowest-physical-id replicas relays, which copy from the master in stage 1,
+ * while the i-th of the others (i >= m, ascending physical id) copies from
+ * relay (i - m) mod m in stage 2; m is the smallest value in
+ * [1, min(max_relays, n - 1)] minimising the critical fan-out
+ * m + ceil((n - m) / m).  Relay is used under FORCE (n >= 2), or under
+ * ADAPTIVE when n >= min_replicas and n >= min_gain * that fan-out, and never
+ * when domain_gpus <= 8.
+ * In:  plan (one record from ultraep_balance).
+ * Out: relay int32 [2][R*S]: relay[s] = -1 (copy from the master), a slot
+ *      id (copy from that relay slot) or -2 (empty slot); relay[R*S + s] =
+ *      the stage, 1 or 2 (0 for an empty slot).
+ * Errors: EINVAL (null pointers, mode outside 0..2, negative counts, reserved
+ *      fields not zero); EUNSUPPORTED (pointers not 4-byte aligned). */
+int ultraep_weight_sync_plan(const ultraep_ctx* ctx, const void* plan, const ultraep_relay_options* opt,
+                             int32_t* relay, void* stream);
+
+/* weight_sync: copy master weights into the redundant slots of the plan
+ * ([README] Interface, "Forward and backward": weight_sync materialises the
+ * plan by distributing master weights to the replica slots; "Initialization":
+ * redundant weight buffers of expert_fc1_numel / expert_fc2_numel elements,
+ * one call per tensor).
+ * For every slot s in [slot_begin, slot_end) that holds expert e:
+ *   replica_weights[s - slot_begin][0, numel) = master_weights[e][0, numel)
+ * as a bit copy (any 16-bit element type).  Each source is read once per call
+ * and written to all of its target slots.  With relay (from
+ * ultraep_weight_sync_plan) the copy runs in its two stages, stage-2 slots
+ * copying from their relay slots; the result is the same bits.
+ * In:  plan (one record); master_weights: DEVICE array of E device pointers
+ *      (entries of experts without a replica in the range may be NULL; a
+ *      NULL entry of a touched expert leaves its slots untouched);
+ *      relay NULL or the [2][R*S] table (then the range must be all slots,
+ *      [0, R*S), since relays may sit anywhere).
+ * Out: replica_weights [slot_end - slot_begin][numel]; empty slots untouched.
+ * Errors: EINVAL (null pointers, numel < 0, bad slot range, relay with a
+ *      partial range); EUNSUPPORTED (master table not 8-byte aligned).  Any
+ *      data alignment works; 16-byte aligned buffers with numel % 8 == 0
+ *      take the vector path. */
+int ultraep_weight_sync(const ultraep_ctx* ctx, const void* plan, const uint16_t* const* master_weights,
+                        uint16_t* replica_weights, int64_t numel, int32_t slot_begin, int32_t slot_end,
+                        const int32_t* relay, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* ultraep_status_string(int status);

@@ -8,7 +8,9 @@ status.  There is no fallback: if ``libultraep.so`` is missing the first call
 raises, telling the user to build it.
 
 Names follow the C ABI: ``ultraep_create``, ``ultraep_balance``,
-``ultraep_dispatch_layout``, ``ultraep_permute``, ``ultraep_fold_grads``.
+``ultraep_dispatch_layout``, ``ultraep_permute``, ``ultraep_combine``,
+``ultraep_combine_backward``, ``ultraep_weight_sync_plan``,
+``ultraep_weight_sync``, ``ultraep_fold_grads``.
 """
 from __future__ import annotations
 
@@ -45,6 +47,14 @@ class _Options(ctypes.Structure):
                 ("allow_zero_master", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
+class _RelayOptions(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("min_replicas", ctypes.c_int32),
+                ("max_relays", ctypes.c_int32), ("min_gain", ctypes.c_int32),
+                ("domain_gpus", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+RELAY_DIRECT, RELAY_ADAPTIVE, RELAY_FORCE = 0, 1, 2
+
 _lib = None
 
 _I32, _I64, _P, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
@@ -60,6 +70,8 @@ _SIGNATURES = {
     "ultraep_fold_grads": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _P]),
     "ultraep_combine": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _I64, _I64, _P, _P]),
     "ultraep_combine_backward": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _P, _I64, _I64, _P, _P, _P]),
+    "ultraep_weight_sync_plan": (_I32, [_P, _P, ctypes.POINTER(_RelayOptions), _P, _P]),
+    "ultraep_weight_sync": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _P, _P]),
     "ultraep_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -203,6 +215,23 @@ def ultraep_combine_backward(ctx: Context, pos, topk_w, k: int, rows, grad_out, 
                                         rows.shape[0], rows.shape[-1], _ptr(grad_out), token_begin,
                                         token_end, _ptr(grad_rows), _ptr(grad_topk_w), _stream(stream))
     _check("ultraep_combine_backward", st)
+
+
+def ultraep_weight_sync_plan(ctx: Context, plan, relay, mode: int = RELAY_ADAPTIVE, min_replicas: int = 4,
+                             max_relays: int = 8, min_gain: int = 2, domain_gpus: Optional[int] = None,
+                             stream=None) -> None:
+    """relay: int32 device tensor [2, R*S] (source slot / -1 master / -2 empty; stage)."""
+    o = _RelayOptions(mode, min_replicas, max_relays, min_gain, ctx.D if domain_gpus is None else domain_gpus)
+    st = lib().ultraep_weight_sync_plan(ctx.handle, _ptr(plan), ctypes.byref(o), _ptr(relay), _stream(stream))
+    _check("ultraep_weight_sync_plan", st)
+
+
+def ultraep_weight_sync(ctx: Context, plan, master_ptrs, replica_weights, numel: int, slot_begin: int,
+                        slot_end: int, relay=None, stream=None) -> None:
+    """master_ptrs: int64 device tensor [E] of master-weight pointers (16-bit elements)."""
+    st = lib().ultraep_weight_sync(ctx.handle, _ptr(plan), _ptr(master_ptrs), _ptr(replica_weights), numel,
+                                   slot_begin, slot_end, _ptr(relay), _stream(stream))
+    _check("ultraep_weight_sync", st)
 
 
 def status_string(status: int) -> str:

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libultraep.so")
-SOURCES = ["ultraep_kernels.hip", "ultraep_combine.hip", "ultraep_abi.hip"]
+SOURCES = ["ultraep_kernels.hip", "ultraep_combine.hip", "ultraep_weights.hip", "ultraep_abi.hip"]
 
 
 def hipcc() -> str:

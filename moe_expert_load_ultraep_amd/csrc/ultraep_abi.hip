@@ -247,6 +247,40 @@ int ultraep_combine_backward(const ultraep_ctx* ctx, const int32_t* pos, const f
                                                    static_cast<hipStream_t>(stream)));
 }
 
+int ultraep_weight_sync_plan(const ultraep_ctx* ctx, const void* plan, const ultraep_relay_options* opt,
+                             int32_t* relay, void* stream) {
+  if (!ctx || !plan || !relay) return ULTRAEP_EINVAL;
+  ultraep_relay_options o{ULTRAEP_RELAY_ADAPTIVE, 4, 8, 2, ctx->sh.D, {0, 0, 0}};
+  if (opt) {
+    o = *opt;
+    for (int32_t r : o.reserved)
+      if (r != 0) return ULTRAEP_EINVAL;
+  }
+  if (o.mode < ULTRAEP_RELAY_DIRECT || o.mode > ULTRAEP_RELAY_FORCE || o.min_replicas < 0 ||
+      o.max_relays < 0 || o.min_gain < 0 || o.domain_gpus < 0)
+    return ULTRAEP_EINVAL;
+  if (!aligned(plan, 4) || !aligned(relay, 4)) return ULTRAEP_EUNSUPPORTED;
+  return from_hip(ultraep::launch_relay_plan(ctx->sh, static_cast<const int32_t*>(plan), o.mode,
+                                             o.min_replicas, o.max_relays, o.min_gain, o.domain_gpus,
+                                             relay, static_cast<hipStream_t>(stream)));
+}
+
+int ultraep_weight_sync(const ultraep_ctx* ctx, const void* plan, const uint16_t* const* master_weights,
+                        uint16_t* replica_weights, int64_t numel, int32_t slot_begin, int32_t slot_end,
+                        const int32_t* relay, void* stream) {
+  if (!ctx || !plan || !master_weights || numel < 0) return ULTRAEP_EINVAL;
+  const int32_t all = ctx->sh.R * ctx->sh.S;
+  if (slot_begin < 0 || slot_end < slot_begin || slot_end > all) return ULTRAEP_EINVAL;
+  if (slot_end > slot_begin && numel > 0 && !replica_weights) return ULTRAEP_EINVAL;
+  if (relay && (slot_begin != 0 || slot_end != all)) return ULTRAEP_EINVAL;
+  if (!aligned(plan, 4) || !aligned(master_weights, 8) || !aligned(replica_weights, 2) ||
+      !aligned(relay, 4))
+    return ULTRAEP_EUNSUPPORTED;
+  return from_hip(ultraep::launch_weight_sync(ctx->sh, static_cast<const int32_t*>(plan), master_weights,
+                                              replica_weights, numel, slot_begin, slot_end, relay,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 const char* ultraep_status_string(int status) {
   switch (status) {
     case ULTRAEP_OK: return "ok";

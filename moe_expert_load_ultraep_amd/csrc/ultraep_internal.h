@@ -58,6 +58,14 @@ hipError_t launch_combine_backward(const int32_t* pos, const float* w, int32_t k
                                    const uint16_t* grad_out, int64_t g0, int64_t g1,
                                    uint16_t* grad_rows, float* grad_w, hipStream_t st);
 
+// weight_sync: the relay table [2][R*S] and the copy (relay may be null).
+hipError_t launch_relay_plan(const Shape& sh, const int32_t* plan, int32_t mode, int32_t min_replicas,
+                             int32_t max_relays, int32_t min_gain, int32_t domain_gpus, int32_t* relay,
+                             hipStream_t st);
+hipError_t launch_weight_sync(const Shape& sh, const int32_t* plan, const uint16_t* const* masters,
+                              uint16_t* reps, int64_t numel, int32_t slot_begin, int32_t slot_end,
+                              const int32_t* relay, hipStream_t st);
+
 // Bytes of dynamic LDS the plan solver / reroute kernel need for this shape.
 size_t plan_lds_bytes(const Shape& sh);
 size_t rerouting_lds_bytes(const Shape& sh, bool layout);

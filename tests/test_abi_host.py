@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(U.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -168,3 +168,29 @@ def test_combine_argument_checks():
     assert b(h, F, F, 2, F, 10, 16, F, 0, 3, F + 8, F, None) == -2  # grad_rows misaligned
     assert b(h, F, F, 2, F, 10, 16, F, 0, 3, F, F + 2, None) == -2  # grad_topk_w misaligned
     assert b(h, F, F, 2, F, 10, 16, F, 4, 4, F, F, None) == 0       # empty range: no-op
+
+
+def test_weight_sync_argument_checks():
+    ctx = U.ultraep_create(8, 4, 1, 4)
+    F = FAKE
+    p = U.lib().ultraep_weight_sync_plan
+    o = U._RelayOptions(1, 4, 8, 2, 4)
+    assert p(ctx.handle, None, ctypes.byref(o), F, None) == -1
+    assert p(ctx.handle, F, ctypes.byref(o), None, None) == -1
+    assert p(ctx.handle, F, ctypes.byref(U._RelayOptions(3, 4, 8, 2, 4)), F, None) == -1   # mode
+    assert p(ctx.handle, F, ctypes.byref(U._RelayOptions(1, -1, 8, 2, 4)), F, None) == -1
+    bad = U._RelayOptions(1, 4, 8, 2, 4)
+    bad.reserved[1] = 5
+    assert p(ctx.handle, F, ctypes.byref(bad), F, None) == -1                             # reserved
+    assert p(ctx.handle, F, ctypes.byref(o), F + 2, None) == -2                            # misaligned
+    s = U.lib().ultraep_weight_sync
+    #          ctx plan masters reps numel s0 s1 relay
+    assert s(ctx.handle, F, F, F, 16, 0, 5, None, None) == -1       # slot_end > R*S
+    assert s(ctx.handle, F, F, F, 16, 2, 1, None, None) == -1
+    assert s(ctx.handle, F, F, F, -1, 0, 1, None, None) == -1
+    assert s(ctx.handle, F, None, F, 16, 0, 1, None, None) == -1
+    assert s(ctx.handle, F, F, None, 16, 0, 1, None, None) == -1
+    assert s(ctx.handle, F, F, F, 16, 0, 2, F, None) == -1          # relay needs every slot
+    assert s(ctx.handle, F, F + 4, F, 16, 0, 1, None, None) == -2   # pointer table misaligned
+    assert s(ctx.handle, F, F, F + 1, 16, 0, 1, None, None) == -2   # odd element address
+    assert s(ctx.handle, F, F, F, 0, 0, 4, None, None) == 0         # numel 0: no-op

@@ -59,6 +59,7 @@ class Workload:
     microbatches: int
     fold_rows: int    # one slot's gradient is fold_rows x fold_cols fp32
     fold_cols: int
+    ffn: int = 0      # expert FFN width: fc1 holds 2*H*ffn weights, fc2 H*ffn
 
     @property
     def M(self) -> int:
@@ -87,19 +88,19 @@ class Workload:
 # The five workloads.  T is per rank for all of them.
 TINY = Workload(1, "tiny: T=256/rank E=8 top-2 R=4 S=1 D=4 H=64",
                 E=8, R=4, S=1, D=4, k=2, T=256, H=64, layers=1, microbatches=1,
-                fold_rows=64, fold_cols=64)
+                fold_rows=64, fold_cols=64, ffn=64)
 SINGLE = Workload(2, "single layer 235B-class: E=128 top-8 R=64 S=2 D=64 T=8192 H=4096 Dirichlet(0.3)",
                   E=128, R=64, S=2, D=64, k=8, T=8192, H=4096, layers=1, microbatches=1,
-                  fold_rows=2048, fold_cols=4096)
+                  fold_rows=2048, fold_cols=4096, ffn=1536)
 DEEP = Workload(3, "671B-class 61 layers: E=256 top-8 R=64 S=2 D=64 T=4096 H=7168 Zipf s~U[0.6,1.4]",
                 E=256, R=64, S=2, D=64, k=8, T=4096, H=7168, layers=61, microbatches=1,
-                fold_rows=2048, fold_cols=7168)
+                fold_rows=2048, fold_cols=7168, ffn=2048)
 STREAM = Workload(4, "non-stationary stream 32 layers x 16 mb: E=128 top-8 R=64 S=2 D=64 T=8192 H=4096",
                   E=128, R=64, S=2, D=64, k=8, T=8192, H=4096, layers=32, microbatches=16,
-                  fold_rows=2048, fold_cols=4096)
+                  fold_rows=2048, fold_cols=4096, ffn=1536)
 TOPO = Workload(5, "topology-constrained prefill: E=160 top-8 R=40 S=3 D=8 T=16384 H=5120 hot in 2 domains",
                 E=160, R=40, S=3, D=8, k=8, T=16384, H=5120, layers=1, microbatches=1,
-                fold_rows=2048, fold_cols=5120)
+                fold_rows=2048, fold_cols=5120, ffn=1536)
 
 CONFIGS = {w.cfg_id: w for w in (TINY, SINGLE, DEEP, STREAM, TOPO)}
 
