@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--workers", type=int, default=16, help="host processes generating inputs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the oracle timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--threshold", default="1/1",
+                    help="early-stop target of the quota search as num/den (the pages' default 1.0)")
     ap.add_argument("--no-weight-sync", action="store_true",
                     help="skip the weight_sync timing (needs master and replica weight buffers)")
     ap.add_argument("--no-combine", action="store_true",
@@ -191,7 +193,31 @@ def quality(ctx, plans, w):
             "grid_index_max": int(col("grid_index").max()), "probe_rounds_max": int(col("rounds").max())}
 
 
-def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s):
+def stale_plan_imbalance(prev, cur, w):
+    """Max/mean rank load when an instance is served by the previous
+    instance's placement, every expert's pairs split evenly over the ranks
+    that hold it (a history-based balancer's view), against the exact
+    counts of the current instance."""
+    P1 = w.M + w.S
+    counts = cur["counts"].astype(np.float64)
+    load = np.zeros(w.R)
+    ptr, phys = prev["inst_ptr"], prev["inst_phys"]
+    for e in range(w.E):
+        ranks = phys[ptr[e]:ptr[e + 1]] // P1
+        load[ranks] += counts[e] / len(ranks)
+    return float(load.max() * w.R / counts.sum())
+
+
+# The pages' EP64 test table ([README] "Tests"), for the workloads at its shape.
+PAGES_TABLE = {6: {"initial": 1.51, "final": 1.01, "replicas_max_per_expert": 4, "replicas_total": 38,
+                   "update_placement_ms": 0.067, "reroute_ms": 0.039},
+               7: {"initial": 2.01, "final": 1.01, "replicas_max_per_expert": 5, "replicas_total": 46,
+                   "update_placement_ms": 0.072, "reroute_ms": 0.037},
+               8: {"initial": 3.03, "final": 1.01, "replicas_max_per_expert": 6, "replicas_total": 51,
+                   "update_placement_ms": 0.078, "reroute_ms": 0.036}}
+
+
+def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s, thr=(1, 1)):
     """Time the oracle (unchanged) on the host, stage by stage, on the same
     arrays: count, plan, reroute and layout per layer (the batch's layers or
     instances in order, as many as the budget allows), permute of the same
@@ -214,7 +240,7 @@ def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s):
         t0 = time.perf_counter()
         c, dropped = O.count(idx, w.E)
         t1 = time.perf_counter()
-        pl = O.plan(c, w.E, w.R, w.S, w.D, dropped=dropped)
+        pl = O.plan(c, w.E, w.R, w.S, w.D, dropped=dropped, thr_num=thr[0], thr_den=thr[1])
         t2 = time.perf_counter()
         phys, pos = O.reroute(idx, pl)
         t3 = time.perf_counter()
@@ -283,7 +309,8 @@ def main():
         import __graft_entry__
         __graft_entry__.build()
     dev = torch.device("cuda:0")
-    ctx = U.ultraep_create(w.E, w.R, w.S, w.D)
+    thr = tuple(int(x) for x in args.threshold.split("/"))
+    ctx = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr)
     buf = U.Buffers(ctx, L, w.T, w.k, dev)
     if args.config == 3:
         d_idx = [torch.from_numpy(np.stack([r[0] for r in routes])).to(dev)]
@@ -545,10 +572,16 @@ def main():
     if wsync is not None:
         result["weight_sync"] = wsync
     result.update(quality(ctx, [p[l] for p in plans for l in range(L)], w))
+    result["threshold"] = f"{thr[0]}/{thr[1]}"
+    if args.config == 4 and n_inst > 1:
+        stale = [stale_plan_imbalance(plans[i - 1][0], plans[i][0], w) for i in range(1, n_inst)]
+        result["stale_plan_imbalance_median_max"] = [float(np.median(stale)), float(np.max(stale))]
+    if args.config in PAGES_TABLE:
+        result["pages_table_context"] = PAGES_TABLE[args.config]
     if not args.no_cpu_baseline:
         masters = {e: masters_h[i] for i, e in enumerate(first_experts)}
         result["cpu_baseline"] = cpu_baseline(w, L, routes, hidden, seg, masters, reps_h, slots,
-                                              args.cpu_seconds)
+                                              args.cpu_seconds, thr)
     print(json.dumps(result), flush=True)
 
 

@@ -83,12 +83,19 @@ typedef struct ultraep_ctx ultraep_ctx;
  * eps_num/eps_den: the balancing tolerance eps (default 1/100, the pages'
  *   default 0.01).  The quota grid steps by floor(total*eps/R), at least 1.
  * allow_zero_master: 0 (default) = a master with load keeps at least one
- *   pair; 1 = a master may give all of its load to replicas. */
+ *   pair; 1 = a master may give all of its load to replicas.
+ * threshold_num/threshold_den: the early-stop target of the balancing search
+ *   (the pages' default 1.0; 0/0 means 1/1), read as the lowest max/mean the
+ *   plan aims at: the quota grid starts at min(max(ceil(total * threshold /
+ *   R), domain floor), max home load).  Must be >= 1 (num >= den >= 1) and
+ *   at most 64. */
 typedef struct ultraep_options {
   int32_t eps_num;
   int32_t eps_den;
   int32_t allow_zero_master;
-  int32_t reserved[5]; /* must be zero */
+  int32_t threshold_num;
+  int32_t threshold_den;
+  int32_t reserved[3]; /* must be zero */
 } ultraep_options;
 
 /* Weight-distribution plan of ultraep_weight_sync_plan ([README]
@@ -204,8 +211,9 @@ int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_
  * Per layer:
  *  1. c[e] = number of pairs with id e.
  *  2. Quota grid: Q_lb = max over domains of ceil(domain load / D) (never
- *     below ceil(total/R)), step tol = max(1, floor(total*eps/R)), up to the
- *     max home load Q_max; Q* = the first grid quota the greedy reaches.
+ *     below ceil(total * threshold / R), never above Q_max), step
+ *     tol = max(1, floor(total*eps/R)), up to the max home load Q_max;
+ *     Q* = the first grid quota the greedy reaches.
  *  3. The greedy, per domain: ranks above Q shed their excess from their
  *     hottest experts first (pairs desc, id asc), each master keeping one
  *     pair unless allow_zero_master; the largest shed piece (ties: lower id)

@@ -44,7 +44,8 @@ class UltraEPError(RuntimeError):
 
 class _Options(ctypes.Structure):
     _fields_ = [("eps_num", ctypes.c_int32), ("eps_den", ctypes.c_int32),
-                ("allow_zero_master", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("allow_zero_master", ctypes.c_int32), ("threshold_num", ctypes.c_int32),
+                ("threshold_den", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class _RelayOptions(ctypes.Structure):
@@ -111,8 +112,10 @@ def _ptr(t) -> Optional[int]:
 class Context:
     """An ``ultraep_ctx``: the shape (E, R, S, D) and planning options."""
 
-    def __init__(self, E: int, R: int, S: int, D: int, eps=(1, 100), allow_zero_master=False):
-        opt = _Options(int(eps[0]), int(eps[1]), int(bool(allow_zero_master)), (ctypes.c_int32 * 5)())
+    def __init__(self, E: int, R: int, S: int, D: int, eps=(1, 100), allow_zero_master=False,
+                 threshold=(1, 1)):
+        opt = _Options(int(eps[0]), int(eps[1]), int(bool(allow_zero_master)), int(threshold[0]),
+                       int(threshold[1]), (ctypes.c_int32 * 3)())
         h = _P()
         _check("ultraep_create", lib().ultraep_create(E, R, S, D, ctypes.byref(opt), ctypes.byref(h)))
         self.handle = h
@@ -156,8 +159,8 @@ class Context:
 
 
 def ultraep_create(E: int, R: int, slots_per_rank: int, D: int, eps=(1, 100),
-                   allow_zero_master: bool = False) -> Context:
-    return Context(E, R, slots_per_rank, D, eps, allow_zero_master)
+                   allow_zero_master: bool = False, threshold=(1, 1)) -> Context:
+    return Context(E, R, slots_per_rank, D, eps, allow_zero_master, threshold)
 
 
 def ultraep_balance(ctx: Context, topk_idx, T: int, k: int, workspace, plans, phys_idx, pos,

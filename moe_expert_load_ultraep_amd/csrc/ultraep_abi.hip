@@ -73,12 +73,16 @@ int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
   if (E > ULTRAEP_MAX_EXPERTS || E / R > ULTRAEP_MAX_MASTERS || slots_per_rank > ULTRAEP_MAX_SLOTS ||
       D > ULTRAEP_MAX_DOMAIN || static_cast<int64_t>(R) * slots_per_rank > ULTRAEP_MAX_TOTAL_SLOTS)
     return ULTRAEP_EUNSUPPORTED;
-  ultraep_options o{1, 100, 0, {0, 0, 0, 0, 0}};
+  ultraep_options o{1, 100, 0, 1, 1, {0, 0, 0}};
   if (opt) {
     o = *opt;
-    for (int i = 0; i < 5; ++i)
+    for (int i = 0; i < 3; ++i)
       if (o.reserved[i] != 0) return ULTRAEP_EINVAL;
     if (o.eps_num < 0 || o.eps_den < 1 || (o.allow_zero_master != 0 && o.allow_zero_master != 1))
+      return ULTRAEP_EINVAL;
+    if (o.threshold_num == 0 && o.threshold_den == 0) o.threshold_num = o.threshold_den = 1;
+    if (o.threshold_den < 1 || o.threshold_num < o.threshold_den ||
+        static_cast<int64_t>(o.threshold_num) > 64ll * o.threshold_den)
       return ULTRAEP_EINVAL;
   }
   ultraep_ctx* c = new (std::nothrow) ultraep_ctx;
@@ -95,6 +99,8 @@ int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
   sh.eps_num = o.eps_num;
   sh.eps_den = o.eps_den;
   sh.allow_zero = o.allow_zero_master;
+  sh.thr_num = o.threshold_num;
+  sh.thr_den = o.threshold_den;
   build_layout(&sh);
   if (ultraep::plan_lds_bytes(sh) > 160 * 1024 || ultraep::rerouting_lds_bytes(sh, true) > 160 * 1024) {
     delete c;

@@ -28,6 +28,7 @@ struct Shape {
   int32_t E, R, S, D, M, P, ndom;
   int32_t n_inst;                        // E + R*S instance entries
   int32_t eps_num, eps_den, allow_zero;
+  int32_t thr_num, thr_den;              // early-stop target of the quota search
   PlanLayout lay;
 };
 

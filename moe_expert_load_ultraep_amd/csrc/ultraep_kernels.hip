@@ -144,6 +144,7 @@ struct PlanParams {
   int32_t E, R, S, D, M, P, ndom, n_inst;
   int32_t N, ntiles;
   int32_t eps_num, eps_den, allow_zero;
+  int32_t thr_num, thr_den;
   int32_t rec_words;
   int32_t G, items;  // grid quotas per probe round, (quota, domain) items per round
   int32_t scan_wgs;  // workgroups per layer that build the tile ordinal bases
@@ -653,8 +654,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       floor = max(floor, wave_max(fl));
     }
     if (lane == 0) {
-      const int32_t qmean = (static_cast<int32_t>(total) + R - 1) / R;
-      const int32_t qlb = max(qmean, static_cast<int32_t>(floor));
+      // lowest quota aimed at: the early-stop target times the mean (at
+      // least the domain floor, at most the max home load)
+      const int64_t tden = static_cast<int64_t>(R) * a.thr_den;
+      const int64_t qmean = (static_cast<int64_t>(total) * a.thr_num + tden - 1) / tden;
+      const int64_t qlb64 = min(max(qmean, static_cast<int64_t>(floor)), static_cast<int64_t>(qmax));
+      const int32_t qlb = static_cast<int32_t>(qlb64);
       const int64_t tol64 = (static_cast<int64_t>(total) * a.eps_num) /
                             (static_cast<int64_t>(R) * a.eps_den);
       const int32_t tol = static_cast<int32_t>(tol64 < 1 ? 1 : tol64);
@@ -1304,6 +1309,7 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   pp.E = sh.E; pp.R = sh.R; pp.S = sh.S; pp.D = sh.D; pp.M = sh.M; pp.P = sh.P;
   pp.ndom = sh.ndom; pp.n_inst = sh.n_inst; pp.N = N; pp.ntiles = ntiles;
   pp.eps_num = sh.eps_num; pp.eps_den = sh.eps_den; pp.allow_zero = sh.allow_zero;
+  pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den;
   pp.rec_words = sh.lay.words;
   plan_rounds(sh, &pp.G, &pp.items);
   // scan workgroups: enough that each thread's run of tiles is about one

@@ -116,7 +116,8 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
-def quota_grid(total: int, H: List[int], R: int, D: int, eps_num: int, eps_den: int):
+def quota_grid(total: int, H: List[int], R: int, D: int, eps_num: int, eps_den: int,
+               thr_num: int = 1, thr_den: int = 1):
     """The quota values a plan may settle on, in the order they are tried.
 
     [README] "Performance Tuning / Replication planning": the balancing ratio
@@ -128,11 +129,16 @@ def quota_grid(total: int, H: List[int], R: int, D: int, eps_num: int, eps_den: 
     eps * mean until the no-replication load max H is reached; that last
     quota is always feasible.  (The domain term is never below the global
     mean, so it alone sets the start; the mean is kept for readability.)
+
+    The early-stop target (default 1.0) is read as the lowest max/mean the
+    search aims at: with a target thr = thr_num / thr_den the grid starts at
+    ceil(thr * total / R) instead of the mean, so a plan stops replicating
+    once every rank is within thr of the mean (R26).
     """
-    Q_mean = _ceil_div(total, R)
+    Q_mean = _ceil_div(total * thr_num, R * thr_den)
     floor = max(_ceil_div(sum(H[d * D:(d + 1) * D]), D) for d in range(R // D))
-    Q_lb = max(Q_mean, floor)
     Q_max = max(H)
+    Q_lb = min(max(Q_mean, floor), Q_max)   # the clamp only acts for a target above 1
     tol = max(1, (total * eps_num) // (R * eps_den))
     grid = []
     q = Q_lb
@@ -246,7 +252,8 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
 
 
 def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
-         eps_num: int = 1, eps_den: int = 100, allow_zero_master: bool = False) -> Plan:
+         eps_num: int = 1, eps_den: int = 100, allow_zero_master: bool = False,
+         thr_num: int = 1, thr_den: int = 1) -> Plan:
     """Replication plan from the exact per-expert load ([README] Interface /
     "Forward and backward": ``update_placement``).
 
@@ -262,7 +269,7 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     c = [int(x) for x in c]
     total = sum(c)
     H = [sum(c[r * M:(r + 1) * M]) for r in range(R)]
-    grid, Q_lb, Q_max, tol, floor = quota_grid(total, H, R, D, eps_num, eps_den)
+    grid, Q_lb, Q_max, tol, floor = quota_grid(total, H, R, D, eps_num, eps_den, thr_num, thr_den)
     for gi, Q in enumerate(grid):
         hosted = feasible(c, Q, E, R, S, D, allow_zero_master)
         if hosted is not None:

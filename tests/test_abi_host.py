@@ -64,6 +64,11 @@ def test_create_accepts_limits(E, R, S, D):
 def test_create_rejects_bad_options():
     with pytest.raises(U.UltraEPError):
         U.ultraep_create(8, 4, 1, 4, eps=(1, 0))
+    for thr in ((1, 2), (65, 1), (1, 0), (-1, 1)):     # below 1, above 64, zero denominator
+        with pytest.raises(U.UltraEPError):
+            U.ultraep_create(8, 4, 1, 4, threshold=thr)
+    U.ultraep_create(8, 4, 1, 4, threshold=(0, 0)).close()   # 0/0: the default 1
+    U.ultraep_create(8, 4, 1, 4, threshold=(64, 1)).close()
 
 
 def test_plan_layout_fields():

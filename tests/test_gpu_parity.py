@@ -83,7 +83,8 @@ def test_hand_worked_plans_on_gpu():
         k = 1
         idx = np.full(R * T * k, -1, dtype=np.int32)
         idx[:ids.size] = np.random.default_rng(0).permutation(ids)
-        ctx = U.ultraep_create(E, R, S, D, allow_zero_master=case.get("allow_zero_master", False))
+        ctx = U.ultraep_create(E, R, S, D, allow_zero_master=case.get("allow_zero_master", False),
+                               threshold=tuple(case.get("threshold", (1, 1))))
         got = run_balance(ctx, idx.reshape(1, R * T, k), None, T, k)
         g = ctx.decode_plan(got["plans"][0])
         assert g["Q_star"] == case["Q_star"] and g["grid_index"] == case["grid_index"], case["name"]
@@ -125,6 +126,17 @@ def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero, fused):
     got = run_balance(ctx, idx[None], wt[None], T, k, fused=fused)
     pl, phys, pos = assert_layer_equal(ctx, got, 0, idx, wt, E, R, S, D, allow_zero_master=allow_zero)
     check_plan_invariants(pl, pl.c, allow_zero)
+
+
+@pytest.mark.parametrize("thr", [(101, 100), (105, 100), (3, 2)])
+def test_threshold_single_layer(thr):
+    """The early-stop target above 1 on the single-layer workload (1024
+    tokens per rank) and the pages' EP64 table shape."""
+    w = W.SINGLE.with_(T=1024)
+    idx, wt = routing_cached(2, 0, 0, 1024)
+    ctx = _ctx(w, threshold=thr)
+    got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
+    assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D, thr_num=thr[0], thr_den=thr[1])
 
 
 def test_large_counts_take_the_unpacked_probe():

@@ -24,7 +24,8 @@ MUTATIONS = [
      "valid = (ids >= 0) & (ids <= E)\n    c = np.bincount"),
     ("ordinal off by one", 'run_start = np.searchsorted(key[order], key[order], side="left")',
      'run_start = np.searchsorted(key[order], key[order], side="right")'),
-    ("no domain floor", "Q_lb = max(Q_mean, floor)", "Q_lb = Q_mean"),
+    ("no domain floor", "Q_lb = min(max(Q_mean, floor), Q_max)", "Q_lb = min(Q_mean, Q_max)"),
+    ("target ignored", "Q_mean = _ceil_div(total * thr_num, R * thr_den)", "Q_mean = _ceil_div(total, R)"),
     ("tolerance not per rank", "tol = max(1, (total * eps_num) // (R * eps_den))",
      "tol = max(1, (total * eps_num) // eps_den)"),
     ("shed coldest first", "key=lambda f: (-c[f], f)", "key=lambda f: (c[f], f)"),
@@ -78,6 +79,7 @@ PIN_SUBSET = [
     (P.test_plan_single_hot_expert_wraps, {"N": 77, "R": 5, "M": 3, "S": 1}),
     (P.test_plan_two_ranks_closed_form, {"seed": 1}),
     (P.test_plan_uniform_home_load, {}),
+    (P.test_plan_threshold_stops_at_the_target, {"which": 1, "thr": (105, 100)}),
     (P.test_plan_no_replication_possible, {"seed": 0, "S": 0, "D": 4}),
     (P.test_plan_invariants_random_shapes, {"seed": 3}),
     (P.test_layout_properties_workloads, {"cfg": 1, "layer": 0}),

@@ -48,8 +48,9 @@ HAND = load_golden("hand_plans.json")["cases"]
 
 @pytest.mark.parametrize("case", HAND, ids=[c["name"] for c in HAND])
 def test_plan_hand_worked(case):
+    thr = case.get("threshold", [1, 1])
     pl = O.plan(np.array(case["c"]), case["E"], case["R"], case["S"], case["D"],
-                allow_zero_master=case.get("allow_zero_master", False))
+                allow_zero_master=case.get("allow_zero_master", False), thr_num=thr[0], thr_den=thr[1])
     assert pl.Q_star == case["Q_star"] and pl.grid_index == case["grid_index"]
     for key in ("slot_expert", "slot_quota", "master_quota", "phys_load", "phys_off",
                 "inst_ptr", "inst_phys", "inst_end", "rank_after"):
@@ -374,3 +375,26 @@ def test_fold_rounds_once_from_fp64():
     reps[slots[0]] = reps[slots[1]] = np.float32(2.0 ** -24)
     out = O.fold({0: np.array([1.0], np.float32)}, reps, pl, 0, 8)
     assert out[0][0] == np.float32(1 + 2.0 ** -23)
+
+
+@pytest.mark.parametrize("which", [0, 1, 2])
+@pytest.mark.parametrize("thr", [(101, 100), (105, 100), (5, 4)])
+def test_plan_threshold_stops_at_the_target(which, thr):
+    """With an early-stop target above 1 the plan aims at target x mean: the
+    grid starts at ceil(target * total / R) (capped by the max home load),
+    the result stays within the first feasible grid quota, and a target at
+    or above the initial max/mean replicates nothing."""
+    g = load_golden("pages_ep64_table.json")
+    sh = g["shape"]
+    rng = np.random.default_rng([78, which])
+    N = sh["R"] * sh["tokens_per_rank"] * sh["k"]
+    c = _zipf_counts_at(g["initial_imbalance"][which], sh["E"], sh["R"], N, rng)
+    pl = _plan_of(c, sh["E"], sh["R"], sh["S"], sh["D"], thr_num=thr[0], thr_den=thr[1])
+    want_lb = min(max(-(-pl.total * thr[0] // (sh["R"] * thr[1])), pl.floor), pl.Q_max)
+    assert pl.Q_lb == want_lb
+    assert pl.rank_after.max() <= pl.Q_star < want_lb + pl.tol * (pl.grid_index + 1) or pl.Q_star == pl.Q_max
+    base = _plan_of(c, sh["E"], sh["R"], sh["S"], sh["D"])
+    assert pl.Q_star >= base.Q_star
+    top = _plan_of(c, sh["E"], sh["R"], sh["S"], sh["D"], thr_num=int(pl.imbalance_before() * 1000) + 1,
+                   thr_den=1000)
+    assert top.n_replicas == 0 and top.Q_star == top.Q_max

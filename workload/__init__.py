@@ -102,7 +102,17 @@ TOPO = Workload(5, "topology-constrained prefill: E=160 top-8 R=40 S=3 D=8 T=163
                 E=160, R=40, S=3, D=8, k=8, T=16384, H=5120, layers=1, microbatches=1,
                 fold_rows=2048, fold_cols=5120, ffn=1536)
 
-CONFIGS = {w.cfg_id: w for w in (TINY, SINGLE, DEEP, STREAM, TOPO)}
+# The project README's EP64 test table ("Tests"): 256 experts, 4 masters and
+# 2 redundant slots per rank, top-8, 8k tokens per rank, loads synthesized
+# at initial max/mean 1.51, 2.01 and 3.03 (hidden and FFN widths of the
+# 256-expert model class, which the table does not give).
+TABLE_IMBALANCE = {6: 1.51, 7: 2.01, 8: 3.03}
+TABLE = [Workload(cid, f"pages' EP64 table shape: E=256 top-8 R=64 S=2 D=64 T=8192, initial max/mean {r}",
+                  E=256, R=64, S=2, D=64, k=8, T=8192, H=7168, layers=1, microbatches=1,
+                  fold_rows=2048, fold_cols=7168, ffn=2048)
+         for cid, r in TABLE_IMBALANCE.items()]
+
+CONFIGS = {w.cfg_id: w for w in (TINY, SINGLE, DEEP, STREAM, TOPO, *TABLE)}
 
 
 def _zipf(E: int, s: float) -> np.ndarray:
@@ -134,9 +144,46 @@ def hot_domains(w: Workload) -> np.ndarray:
     return np.sort(rng.choice(w.R // w.D, size=2, replace=False))
 
 
+def zipf_at_imbalance(target: float, E: int, R: int, rng: np.random.Generator) -> np.ndarray:
+    """Zipf popularity over a seeded permutation of the experts, its exponent
+    bisected so that the expected max/mean home-rank load is ``target``."""
+    perm = rng.permutation(E)
+
+    def law(s):
+        z = _zipf(E, s)
+        q = np.empty(E)
+        q[perm] = z / z.sum()
+        return q.reshape(R, -1).sum(axis=1).max() * R, q
+
+    lo, hi = 0.0, 4.0
+    for _ in range(60):
+        mid = (lo + hi) / 2
+        if law(mid)[0] < target:
+            lo = mid
+        else:
+            hi = mid
+    return law(lo)[1]
+
+
+def dealt_topk(rng: np.random.Generator, counts: np.ndarray, ntok: int, k: int) -> np.ndarray:
+    """A top-k routing with exactly ``counts`` pairs per expert.
+
+    The pairs, sorted by expert, are dealt column by column: pair i goes to
+    token i mod ntok, slot i div ntok.  No expert has more pairs than there
+    are tokens, so two pairs of one expert never meet in a token.  Tokens and
+    the slots inside each token are then shuffled."""
+    assert counts.sum() == ntok * k and counts.max() <= ntok
+    ids = np.repeat(np.arange(counts.size), counts)
+    out = ids.reshape(k, ntok).T.copy()
+    out = out[rng.permutation(ntok)]
+    return np.take_along_axis(out, rng.random((ntok, k)).argsort(axis=1), axis=1)
+
+
 def popularity(w: Workload, layer: int, mb: int, rng: np.random.Generator) -> np.ndarray:
     """Expert popularity p (sums to 1, every entry >= 1e-30) for one instance."""
     E = w.E
+    if w.cfg_id in TABLE_IMBALANCE:         # Zipf tuned to the table's initial max/mean
+        return zipf_at_imbalance(TABLE_IMBALANCE[w.cfg_id], E, w.R, rng)
     if w.cfg_id == 1:                       # Zipf(1.2), seeded permutation
         z = _zipf(E, 1.2)
         p = np.empty(E)
@@ -200,7 +247,11 @@ def routing(w: Workload, layer: int = 0, mb: int = 0):
     """(topk_idx int32 [R*T, k], topk_w fp32 [R*T, k], p float64 [E]) for one instance."""
     rng = np.random.default_rng([w.cfg_id, layer, mb])
     p = popularity(w, layer, mb, rng)
-    idx = sample_topk(rng, p, w.tokens, w.k).astype(np.int32)
+    if w.cfg_id in TABLE_IMBALANCE:         # exact multinomial counts, dealt to tokens
+        counts = rng.multinomial(w.N, p)
+        idx = dealt_topk(rng, counts, w.tokens, w.k).astype(np.int32)
+    else:
+        idx = sample_topk(rng, p, w.tokens, w.k).astype(np.int32)
     logits = rng.standard_normal((w.tokens, w.k))
     e = np.exp(logits - logits.max(axis=1, keepdims=True))
     wts = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
