@@ -373,6 +373,96 @@ def reroute(topk_idx: np.ndarray, pl: Plan) -> Tuple[np.ndarray, np.ndarray]:
     return phys, pos
 
 
+def local_takes(pl: Plan, rank_counts: np.ndarray) -> np.ndarray:
+    """Pairs each instance takes from its own rank's pairs of its expert.
+
+    [README] "Replication planning": the locality-aware per-rank quota
+    decomposition cuts remote traffic.  Read as (R31): instance i of expert e,
+    hosted on rank h_i with quota q_i, first serves min(q_i, pairs of e whose
+    token lives on h_i).  rank_counts[r, e] = pairs of e from rank r.
+    Returns one value per instance entry (inst_phys order).
+    """
+    a = np.zeros(len(pl.inst_phys), dtype=np.int64)
+    for e in range(pl.E):
+        start = 0
+        for i in range(pl.inst_ptr[e], pl.inst_ptr[e + 1]):
+            q = int(pl.inst_end[i]) - start
+            start = int(pl.inst_end[i])
+            h = int(pl.inst_phys[i]) // (pl.M + pl.S)
+            a[i] = min(q, int(rank_counts[h, e]))
+    return a
+
+
+def reroute_local(topk_idx: np.ndarray, pl: Plan, interleave: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Physical expert and dispatch row of every pair, locality first.
+
+    [README] "Replication planning": locality-aware per-rank quota
+    decomposition to cut remote traffic, and reroute interleave to spread
+    the token order over the replicas against congestion in the dispatch
+    that follows.  Reading (R31, R32):
+      - the pairs of expert e split by the rank of their token into R
+        blocks, each in pair order;
+      - instance i (host rank h_i, quota q_i) first takes the first a_i =
+        min(q_i, |block h_i|) pairs of block h_i (``local_takes``);
+      - the remaining pairs of all blocks, in pair order, form e's pool;
+        the instances' remaining quotas q_i - a_i take the pool
+        contiguously in instance order, or, with interleave, round by
+        round: in round t every instance with more than t remaining pairs
+        takes the next pool pair, in instance order;
+      - instance i's rows hold its local pairs first (in pair order), then
+        its pool pairs in pool order.
+    The token's rank is n // (N / R): pairs are rank-major.
+    """
+    ids = np.asarray(topk_idx).reshape(-1).astype(np.int64)
+    N = ids.size
+    E, R = pl.E, pl.R
+    TK = N // R if R else 0
+    valid = (ids >= 0) & (ids < E)
+    src = np.arange(N) // max(TK, 1)
+    rank_counts = np.zeros((R, E), dtype=np.int64)
+    np.add.at(rank_counts, (src[valid], ids[valid]), 1)
+    a = local_takes(pl, rank_counts)
+    phys = np.full(N, -1, dtype=np.int64)
+    pos = np.full(N, -1, dtype=np.int64)
+    for e in range(E):
+        insts = list(range(pl.inst_ptr[e], pl.inst_ptr[e + 1]))
+        host = {int(pl.inst_phys[i]) // (pl.M + pl.S): i for i in insts}
+        start = 0
+        rem = {}
+        for i in insts:
+            rem[i] = int(pl.inst_end[i]) - start - int(a[i])
+            start = int(pl.inst_end[i])
+        # the pool's owner sequence
+        owner: List[int] = []
+        if interleave:
+            left = dict(rem)
+            while any(left[i] > 0 for i in insts):
+                for i in insts:
+                    if left[i] > 0:
+                        owner.append(i)
+                        left[i] -= 1
+        else:
+            for i in insts:
+                owner += [i] * rem[i]
+        taken = {i: 0 for i in insts}     # local pairs handed out so far
+        pool_seen = {i: 0 for i in insts}  # pool pairs handed out so far
+        u = 0
+        for n in np.nonzero(ids == e)[0]:
+            r = int(src[n])
+            i = host.get(r)
+            if i is not None and taken[i] < a[i]:
+                row = taken[i]
+                taken[i] += 1
+            else:
+                i = owner[u]
+                u += 1
+                row = int(a[i]) + pool_seen[i]
+                pool_seen[i] += 1
+            phys[n] = pl.inst_phys[i]
+            pos[n] = pl.phys_off[pl.inst_phys[i]] + row
+    return phys, pos
+
+
 def layout(pos: np.ndarray, topk_w: np.ndarray, total: int) -> Tuple[np.ndarray, np.ndarray]:
     """Inverse index and permuted weights of the dispatch layout.
 

@@ -16,6 +16,7 @@ import pytest
 import oracle
 import oracle.ultraep_oracle as base
 import test_oracle_combine as C
+import test_oracle_locality as LC
 import test_oracle_weight_sync as WS
 import test_oracle_pins as P
 
@@ -66,6 +67,10 @@ MUTATIONS = [
     ("relays are the highest-id replicas", "            if not relay or i < m:", "            if not relay or i >= n - m:"),
     ("relay gain not checked", "(n >= min_replicas and n >= min_gain * cost)", "(n >= min_replicas)"),
     ("relay ignores the domain size", "domain_gpus > 8 and n >= 2", "domain_gpus > 0 and n >= 2"),
+    ("local take not capped by the quota", "a[i] = min(q, int(rank_counts[h, e]))", "a[i] = int(rank_counts[h, e])"),
+    ("pool rows before local rows", "row = int(a[i]) + pool_seen[i]", "row = pool_seen[i]"),
+    ("interleave in reverse instance order", "                for i in insts:\n                    if left[i] > 0:",
+     "                for i in reversed(insts):\n                    if left[i] > 0:"),
     ("weight sync from the wrong master", "{s: np.array(master[int(pl.slot_expert[s])], copy=True)",
      "{s: np.array(master[int(pl.slot_expert[s]) ^ 1], copy=True)"),
 ]
@@ -99,6 +104,9 @@ PIN_SUBSET = [
     *[(WS.test_relay_costs_hand_worked, {"case": c}) for c in json.load(open(WS.GOLDEN))["cases"]],
     (WS.test_relay_schedule_structure_on_workload_plans, {}),
     (WS.test_weight_sync_copies_bits, {}),
+    *[(LC.test_locality_hand_worked, {"case": c}) for c in LC.CASES],
+    (LC.test_locality_structure_on_workloads, {"cfg": 1, "T": None, "interleave": True}),
+    (LC.test_locality_random_shapes_with_dropped, {"seed": 0}),
 ]
 
 
