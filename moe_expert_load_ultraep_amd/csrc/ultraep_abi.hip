@@ -134,7 +134,7 @@ int ultraep_workspace_bytes(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_
   int32_t N = 0;
   const int st = pairs_per_layer(ctx, T, k, &N);
   if (st != ULTRAEP_OK) return st;
-  const size_t ntiles = static_cast<size_t>(ultraep::ntiles_of(N));
+  const size_t ntiles = static_cast<size_t>(ultraep::ntiles_of(ctx->sh.R, static_cast<int64_t>(T) * k));
   *out = 2 * sizeof(int32_t) * static_cast<size_t>(L) * ntiles * static_cast<size_t>(ctx->sh.E);
   if (*out == 0) *out = 256;
   return ULTRAEP_OK;
@@ -160,7 +160,7 @@ int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
   st = ultraep_workspace_bytes(ctx, L, T, k, &need);
   if (st != ULTRAEP_OK) return st;
   if (workspace_bytes < need) return ULTRAEP_EWORKSPACE;
-  return from_hip(ultraep::launch_balance(ctx->sh, L, topk_idx, topk_w, N,
+  return from_hip(ultraep::launch_balance(ctx->sh, L, topk_idx, topk_w, static_cast<int32_t>(T * k),
                                           static_cast<int32_t*>(workspace),
                                           static_cast<int32_t*>(plans), phys_idx, pos,
                                           layout ? inv : nullptr, w_perm,

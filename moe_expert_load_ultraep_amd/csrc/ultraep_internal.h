@@ -32,13 +32,18 @@ struct Shape {
   PlanLayout lay;
 };
 
-inline int64_t ntiles_of(int64_t N) { return (N + kTile - 1) / kTile; }
+// Tiles never straddle two ranks: each rank's TK = T*k pairs split into
+// ceil(TK / kTile) tiles, the last one ragged, so a tile's pairs all come
+// from one rank's tokens.
+inline int64_t tiles_per_rank(int64_t TK) { return (TK + kTile - 1) / kTile; }
+inline int64_t ntiles_of(int64_t R, int64_t TK) { return R * tiles_per_rank(TK); }
 
 // Launchers.  All work is queued on `st`; none of them synchronises.
-// ws: 2*L*ntiles*E int32 (tile histograms, tile ordinal bases).  With inv
-// non-null the dispatch layout (inv, w_perm from w) is written too.
+// ws: 2*L*ntiles*E int32 (tile histograms, tile ordinal bases); TK = T*k
+// pairs per rank, N = R*TK per layer.  With inv non-null the dispatch
+// layout (inv, w_perm from w) is written too.
 hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const float* w,
-                          int32_t N, int32_t* ws, int32_t* plans, int32_t* phys_idx, int32_t* pos,
+                          int32_t TK, int32_t* ws, int32_t* plans, int32_t* phys_idx, int32_t* pos,
                           int32_t* inv, float* w_perm, hipStream_t st);
 hipError_t launch_layout(int32_t L, int32_t N, const int32_t* pos, const float* w,
                          int32_t* inv, float* w_perm, hipStream_t st);

@@ -42,6 +42,28 @@ struct TileShape {
   static_assert(kChunks * 64 * W == kTile, "tile must split into whole chunks");
 };
 
+// The tiling of one launch: N = R*TK pairs per layer, tpr tiles per rank,
+// ntiles = R*tpr tiles per layer.
+struct Tiling {
+  int32_t N, TK, tpr, ntiles;
+};
+
+// Where tile `tile` of a layer lies: tiles are numbered rank by rank, TK
+// pairs per rank in tiles of kTile (the last one of a rank ragged).  tile0
+// is the layer-relative index of its first pair.
+struct TileSpan {
+  int64_t first;  // index of the first pair in the [L][N] arrays
+  int32_t tile0;  // index of the first pair inside the layer
+  int32_t n;      // pairs in the tile
+};
+
+__device__ __forceinline__ TileSpan tile_span(int64_t layer, int32_t tile, int32_t N, int32_t TK,
+                                              int32_t tpr) {
+  const int32_t r = tile / tpr, q = tile % tpr;
+  const int32_t tile0 = r * TK + q * kTile;
+  return {layer * N + tile0, tile0, min(kTile, TK - q * kTile)};
+}
+
 // Expert ids of one wave's stretch of a tile: chunk c, lane l holds pair
 // base + 64c + l.  Every load is issued unconditionally (indices past the
 // tile are clamped to its last pair and masked afterwards) so all C loads
@@ -116,7 +138,7 @@ __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
 using CountTile = TileShape<16>;
 
 __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
-    const int32_t* __restrict__ idx, int32_t N, int32_t E, int32_t ntiles,
+    const int32_t* __restrict__ idx, int32_t N, int32_t TK, int32_t tpr, int32_t E, int32_t ntiles,
     int32_t* __restrict__ hist) {
   using T = CountTile;
   extern __shared__ __align__(16) int32_t s_cnt[];
@@ -124,8 +146,9 @@ __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
   const int32_t layer = static_cast<int32_t>(blk / ntiles);
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
   for (int i = threadIdx.x; i < E; i += T::kThreads) s_cnt[i] = 0;
-  const int32_t* src = idx + static_cast<int64_t>(layer) * N + static_cast<int64_t>(tile) * kTile;
-  const int n_here = min(kTile, N - tile * kTile);
+  const TileSpan sp = tile_span(layer, tile, N, TK, tpr);
+  const int32_t* src = idx + sp.first;
+  const int n_here = sp.n;
   uint32_t v[T::kChunks];
   load_tile_ids(src, (threadIdx.x >> 6) * T::kWavePairs, n_here, lane_id(), E, v);
   __syncthreads();
@@ -890,8 +913,8 @@ __host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layo
 
 template <bool LAYOUT, int W>
 __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
-    const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t E,
-    int32_t ntiles, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans,
+    const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t TK, int32_t tpr,
+    int32_t E, int32_t ntiles, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans,
     int32_t rec_words, int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase,
     int32_t n_inst, int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos,
     int32_t* __restrict__ inv, float* __restrict__ w_perm) {
@@ -923,8 +946,9 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
   const int32_t* plan = plans + static_cast<int64_t>(layer) * rec_words;
   const int64_t lb = static_cast<int64_t>(layer) * N;
-  const int64_t first = lb + static_cast<int64_t>(tile) * kTile;
-  const int n_here = min(kTile, N - tile * kTile);
+  const TileSpan span = tile_span(layer, tile, N, TK, tpr);
+  const int64_t first = span.first;
+  const int n_here = span.n;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int base = wave * T::kWavePairs;
@@ -1042,7 +1066,7 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
     // at most n_here valid pairs; the clamp and the row check only matter for
     // a corrupted plan record.
     const int nt = min(S.roff[n_inst], n_here);
-    const int32_t tile0 = tile * kTile;
+    const int32_t tile0 = span.tile0;
     for (int j = threadIdx.x; j < nt; j += NT) {
       const uint32_t sp = S.sp[j];
       const int r = static_cast<int>(sp >> 16), n = static_cast<int>(sp & 0xFFFFu);
@@ -1243,7 +1267,7 @@ int reroute_waves(const Shape& sh, bool layout) {
 
 template <bool LAYOUT, int W>
 hipError_t launch_reroute(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
-                          int32_t N, int32_t ntiles, const int32_t* tbase, const int32_t* plans,
+                          const Tiling& tl, const int32_t* tbase, const int32_t* plans,
                           int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
                           hipStream_t st) {
   const size_t rl = reroute_lds_bytes(sh.E, sh.n_inst, LAYOUT, W);
@@ -1255,7 +1279,7 @@ hipError_t launch_reroute(const Shape& sh, int64_t blocks, const int32_t* idx, c
   }
   reroute_kernel<LAYOUT, W><<<dim3(static_cast<uint32_t>(blocks)), dim3(TileShape<W>::kThreads),
                               rl, st>>>(
-      idx, w, N, sh.E, ntiles, tbase, plans, sh.lay.words, sh.lay.off[ULTRAEP_PLAN_INST_PTR],
+      idx, w, tl.N, tl.TK, tl.tpr, sh.E, tl.ntiles, tbase, plans, sh.lay.words, sh.lay.off[ULTRAEP_PLAN_INST_PTR],
       sh.lay.off[ULTRAEP_PLAN_INST_END], sh.lay.off[ULTRAEP_PLAN_INST_PHYS],
       sh.lay.off[ULTRAEP_PLAN_INST_BASE], sh.n_inst, phys_idx, pos, inv, w_perm);
   return hipGetLastError();
@@ -1263,18 +1287,18 @@ hipError_t launch_reroute(const Shape& sh, int64_t blocks, const int32_t* idx, c
 
 template <bool LAYOUT>
 hipError_t launch_reroute_w(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
-                            int32_t N, int32_t ntiles, const int32_t* tbase,
+                            const Tiling& tl, const int32_t* tbase,
                             const int32_t* plans, int32_t* phys_idx, int32_t* pos, int32_t* inv,
                             float* w_perm, hipStream_t st) {
   switch (reroute_waves(sh, LAYOUT)) {
     case 16:
-      return launch_reroute<LAYOUT, 16>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+      return launch_reroute<LAYOUT, 16>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos,
                                         inv, w_perm, st);
     case 8:
-      return launch_reroute<LAYOUT, 8>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+      return launch_reroute<LAYOUT, 8>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos,
                                        inv, w_perm, st);
     default:
-      return launch_reroute<LAYOUT, 4>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+      return launch_reroute<LAYOUT, 4>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos,
                                        inv, w_perm, st);
   }
 }
@@ -1292,16 +1316,18 @@ size_t plan_lds_bytes(const Shape& sh) {
 }
 
 hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const float* w,
-                          int32_t N, int32_t* ws, int32_t* plans, int32_t* phys_idx, int32_t* pos,
+                          int32_t TK, int32_t* ws, int32_t* plans, int32_t* phys_idx, int32_t* pos,
                           int32_t* inv, float* w_perm, hipStream_t st) {
   if (L <= 0) return hipSuccess;
-  const int32_t ntiles = static_cast<int32_t>(ntiles_of(N));
+  const int32_t N = sh.R * TK;
+  const int32_t ntiles = static_cast<int32_t>(ntiles_of(sh.R, TK));
+  const Tiling tl{N, TK, static_cast<int32_t>(tiles_per_rank(TK)), ntiles};
   const int64_t blocks = static_cast<int64_t>(L) * ntiles;
   int32_t* hist = ws;
   int32_t* tbase = ws + static_cast<int64_t>(L) * ntiles * sh.E;
   if (blocks > 0) {
     hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(CountTile::kThreads),
-                       sizeof(int32_t) * sh.E, st, idx, N, sh.E, ntiles, hist);
+                       sizeof(int32_t) * sh.E, st, idx, N, TK, tl.tpr, sh.E, ntiles, hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1334,10 +1360,10 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   if (e != hipSuccess) return e;
   if (blocks > 0) {
     if (inv != nullptr)
-      e = launch_reroute_w<true>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos, inv,
+      e = launch_reroute_w<true>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos, inv,
                                  w_perm, st);
     else
-      e = launch_reroute_w<false>(sh, blocks, idx, w, N, ntiles, tbase, plans, phys_idx, pos,
+      e = launch_reroute_w<false>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos,
                                   nullptr, nullptr, st);
   }
   return e;
