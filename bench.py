@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threshold", default="1/1",
                     help="early-stop target of the quota search as num/den (the pages' default 1.0)")
+    ap.add_argument("--reroute-mode", type=int, default=0, choices=(0, 1, 2),
+                    help="0: ordinal ranges; 1: locality-aware; 2: locality-aware with interleave")
     ap.add_argument("--no-weight-sync", action="store_true",
                     help="skip the weight_sync timing (needs master and replica weight buffers)")
     ap.add_argument("--no-combine", action="store_true",
@@ -193,6 +195,22 @@ def quality(ctx, plans, w):
             "grid_index_max": int(col("grid_index").max()), "probe_rounds_max": int(col("rounds").max())}
 
 
+def dispatch_traffic(phys, w):
+    """Where the first layer's pairs travel: the fraction served on their
+    own token's rank, and the R x R matrix of pairs sent from each token's
+    rank to each serving rank (off the diagonal) as max over mean."""
+    ids = np.asarray(phys).reshape(-1)
+    ok = ids >= 0
+    src = (np.arange(ids.size) // (w.T * w.k))[ok]
+    dst = ids[ok] // (w.M + w.S)
+    m = np.bincount(src * w.R + dst, minlength=w.R * w.R).reshape(w.R, w.R).astype(np.float64)
+    off = m[~np.eye(w.R, dtype=bool)]
+    return {"local_fraction": float(np.trace(m) / m.sum()),
+            "remote_pairs": int(off.sum()),
+            "remote_matrix_max_over_mean": float(off.max() / off.mean()) if off.mean() > 0 else None,
+            "max_remote_pairs_received_by_a_rank": int((m.sum(axis=0) - np.diag(m)).max())}
+
+
 def stale_plan_imbalance(prev, cur, w):
     """Max/mean rank load when an instance is served by the previous
     instance's placement, every expert's pairs split evenly over the ranks
@@ -310,7 +328,7 @@ def main():
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     thr = tuple(int(x) for x in args.threshold.split("/"))
-    ctx = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr)
+    ctx = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr, reroute_mode=args.reroute_mode)
     buf = U.Buffers(ctx, L, w.T, w.k, dev)
     if args.config == 3:
         d_idx = [torch.from_numpy(np.stack([r[0] for r in routes])).to(dev)]
@@ -573,6 +591,10 @@ def main():
         result["weight_sync"] = wsync
     result.update(quality(ctx, [p[l] for p in plans for l in range(L)], w))
     result["threshold"] = f"{thr[0]}/{thr[1]}"
+    result["reroute_mode"] = args.reroute_mode
+    balance(0)
+    torch.cuda.synchronize()
+    result["dispatch_traffic"] = dispatch_traffic(buf.phys_idx[0].cpu().numpy(), w)
     if args.config == 4 and n_inst > 1:
         stale = [stale_plan_imbalance(plans[i - 1][0], plans[i][0], w) for i in range(1, n_inst)]
         result["stale_plan_imbalance_median_max"] = [float(np.median(stale)), float(np.max(stale))]

@@ -88,14 +88,31 @@ typedef struct ultraep_ctx ultraep_ctx;
  *   (the pages' default 1.0; 0/0 means 1/1), read as the lowest max/mean the
  *   plan aims at: the quota grid starts at min(max(ceil(total * threshold /
  *   R), domain floor), max home load).  Must be >= 1 (num >= den >= 1) and
- *   at most 64. */
+ *   at most 64.
+ * reroute_mode: which pairs an instance serves ([README] "Replication
+ *   planning": locality-aware per-rank quota decomposition; reroute
+ *   interleave).  ULTRAEP_REROUTE_RANGES (0, default): instance i of an
+ *   expert serves the contiguous range [start_i, end_i) of the expert's
+ *   pairs in pair order.  ULTRAEP_REROUTE_LOCAL (1): instance i first
+ *   serves the first INST_LOCAL[i] pairs of its expert whose tokens live on
+ *   its own rank; the expert's other pairs, in pair order, fill the
+ *   instances' remaining quotas contiguously in instance order.
+ *   ULTRAEP_REROUTE_INTERLEAVE (2): as LOCAL, but the remaining pairs are
+ *   dealt round by round: in round t every instance with more than t pairs
+ *   still to take gets the next one, in instance order.  In modes 1 and 2 an
+ *   instance's layout rows hold its local pairs (pair order), then the rest
+ *   (in the order dealt), and a fused layout is written by a scatter pass. */
+#define ULTRAEP_REROUTE_RANGES 0
+#define ULTRAEP_REROUTE_LOCAL 1
+#define ULTRAEP_REROUTE_INTERLEAVE 2
 typedef struct ultraep_options {
   int32_t eps_num;
   int32_t eps_den;
   int32_t allow_zero_master;
   int32_t threshold_num;
   int32_t threshold_den;
-  int32_t reserved[3]; /* must be zero */
+  int32_t reroute_mode;
+  int32_t reserved[2]; /* must be zero */
 } ultraep_options;
 
 /* Weight-distribution plan of ultraep_weight_sync_plan ([README]
@@ -155,7 +172,9 @@ enum ultraep_plan_field_id {
   ULTRAEP_PLAN_INST_BASE = 10,   /* [E+R*S] layout row of ordinal o is INST_BASE + o */
   ULTRAEP_PLAN_RANK_BEFORE = 11, /* [R] home load before balancing */
   ULTRAEP_PLAN_RANK_AFTER = 12,  /* [R] load after balancing */
-  ULTRAEP_PLAN_NUM_FIELDS = 13
+  ULTRAEP_PLAN_INST_LOCAL = 13,  /* [E+R*S] pairs the instance takes from its own rank's tokens:
+                                    min(its quota, pairs of its expert from its host rank) */
+  ULTRAEP_PLAN_NUM_FIELDS = 14
 };
 
 /* Header words (ULTRAEP_PLAN_HEADER). */

@@ -26,7 +26,8 @@ LIB_PATH = os.path.join(_PKG, "libultraep.so")
 # Plan record fields, in the order of enum ultraep_plan_field_id.
 PLAN_FIELDS = ("header", "counts", "master_quota", "slot_expert", "slot_quota", "phys_load",
                "phys_off", "inst_ptr", "inst_phys", "inst_end", "inst_base", "rank_before",
-               "rank_after")
+               "rank_after", "inst_local")
+REROUTE_RANGES, REROUTE_LOCAL, REROUTE_INTERLEAVE = 0, 1, 2
 # Header words, in the order of enum ultraep_header_word.
 HEADER_WORDS = ("magic", "E", "R", "S", "D", "M", "P", "N", "total", "dropped", "Q_star", "Q_lb",
                 "Q_max", "tol", "grid_index", "floor", "replicas", "rounds")
@@ -45,7 +46,8 @@ class UltraEPError(RuntimeError):
 class _Options(ctypes.Structure):
     _fields_ = [("eps_num", ctypes.c_int32), ("eps_den", ctypes.c_int32),
                 ("allow_zero_master", ctypes.c_int32), ("threshold_num", ctypes.c_int32),
-                ("threshold_den", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("threshold_den", ctypes.c_int32), ("reroute_mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class _RelayOptions(ctypes.Structure):
@@ -113,9 +115,10 @@ class Context:
     """An ``ultraep_ctx``: the shape (E, R, S, D) and planning options."""
 
     def __init__(self, E: int, R: int, S: int, D: int, eps=(1, 100), allow_zero_master=False,
-                 threshold=(1, 1)):
+                 threshold=(1, 1), reroute_mode: int = 0):
         opt = _Options(int(eps[0]), int(eps[1]), int(bool(allow_zero_master)), int(threshold[0]),
-                       int(threshold[1]), (ctypes.c_int32 * 3)())
+                       int(threshold[1]), int(reroute_mode), (ctypes.c_int32 * 2)())
+        self.reroute_mode = int(reroute_mode)
         h = _P()
         _check("ultraep_create", lib().ultraep_create(E, R, S, D, ctypes.byref(opt), ctypes.byref(h)))
         self.handle = h
@@ -159,8 +162,8 @@ class Context:
 
 
 def ultraep_create(E: int, R: int, slots_per_rank: int, D: int, eps=(1, 100),
-                   allow_zero_master: bool = False, threshold=(1, 1)) -> Context:
-    return Context(E, R, slots_per_rank, D, eps, allow_zero_master, threshold)
+                   allow_zero_master: bool = False, threshold=(1, 1), reroute_mode: int = 0) -> Context:
+    return Context(E, R, slots_per_rank, D, eps, allow_zero_master, threshold, reroute_mode)
 
 
 def ultraep_balance(ctx: Context, topk_idx, T: int, k: int, workspace, plans, phys_idx, pos,

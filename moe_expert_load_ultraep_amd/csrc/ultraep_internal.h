@@ -29,6 +29,7 @@ struct Shape {
   int32_t n_inst;                        // E + R*S instance entries
   int32_t eps_num, eps_den, allow_zero;
   int32_t thr_num, thr_den;              // early-stop target of the quota search
+  int32_t reroute_mode;                  // ULTRAEP_REROUTE_*
   PlanLayout lay;
 };
 

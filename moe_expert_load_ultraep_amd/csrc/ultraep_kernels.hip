@@ -165,7 +165,7 @@ __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
 // ------------------------------------------------------------------------
 struct PlanParams {
   int32_t E, R, S, D, M, P, ndom, n_inst;
-  int32_t N, ntiles;
+  int32_t N, ntiles, tpr;
   int32_t eps_num, eps_den, allow_zero;
   int32_t thr_num, thr_den;
   int32_t rec_words;
@@ -791,6 +791,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   int32_t* inst_phys = rec + a.off[ULTRAEP_PLAN_INST_PHYS];
   int32_t* inst_end = rec + a.off[ULTRAEP_PLAN_INST_END];
   int32_t* inst_base = rec + a.off[ULTRAEP_PLAN_INST_BASE];
+  int32_t* inst_local = rec + a.off[ULTRAEP_PLAN_INST_LOCAL];
   for (int e = tid; e < E; e += kPlanThreads) {
     const int home = e / M, d = home / D;
     const uint64_t in_domain = D == 64 ? ~0ull : ((1ull << D) - 1);
@@ -813,6 +814,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       inst_phys[i] = p;
       inst_end[i] = end;
       inst_base[i] = L.pload[p] - (end - q);
+      // local take: min(quota, pairs of e from rank r's tiles)
+      int32_t own = 0;
+      for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * E + e];
+      inst_local[i] = min(q, own);
       ++i;
     }
   }
@@ -822,6 +827,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     inst_phys[i] = -1;
     inst_end[i] = 0;
     inst_base[i] = 0;
+    inst_local[i] = 0;
   }
   for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
     const int end = f + 1 < ULTRAEP_PLAN_NUM_FIELDS ? a.off[f + 1] : a.rec_words;
@@ -1080,6 +1086,232 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
 }
 
 // ------------------------------------------------------------------------
+// reroute, locality first ([README] "Replication planning": locality-aware
+// per-rank quota decomposition; reroute interleave)
+// ------------------------------------------------------------------------
+// A tile's pairs all come from one source rank r (tiles never straddle
+// ranks).  Pass 1 is the same grouping as reroute_kernel and gives every
+// pair its ordinal o among its expert's pairs; t = o - (pairs of e from ranks
+// before r) is its place in rank r's block of e.  If e has an instance on
+// rank r and t is below that instance's local take, the pair is local (row
+// t of the instance).  Otherwise it is pool pair u = (pool pairs of e from
+// ranks before r) + t - local take; the pool fills the instances' remaining
+// quotas contiguously, or (INTERLEAVE) round by round: in round tau every
+// instance with rho_i > tau takes one pool pair, in instance order.  With
+// the distinct positive rho sorted, 0 = lam_0 < lam_1 < ... < lam_m, phase j
+// holds rounds [lam_{j-1}, lam_j) with act_j = #{rho_i >= lam_j} instances
+// and starts at pool pair P_j = sum over earlier phases of their rounds x
+// act; pool pair u of phase j is round lam_{j-1} + (u - P_j) / act_j of the
+// ((u - P_j) mod act_j)-th instance with rho_i >= lam_j.
+struct LocalLds {
+  unsigned long long* peers;  // [waves][E+1]
+  int32_t* cntw;   // [waves][E]
+  int32_t* blk;    // [E] pairs of e from ranks before r (block base)
+  int32_t* loc;    // [E] instance of e on rank r, or -1
+  int32_t* pbase;  // [E] pool pairs of e from ranks before r
+  int32_t* iptr;   // [E+1]
+  int32_t* iphys;  // [n_inst]
+  int32_t* irow;   // [n_inst] first layout row of the instance
+  int32_t* ia;     // [n_inst] local take
+  int32_t* ipool;  // [n_inst] pool pairs before the instance's (contiguous order)
+  int32_t* irho;   // [n_inst] remaining quota after the local take
+  int32_t* lev;    // [n_inst] INTERLEAVE: phase levels lam_j of each expert (its instance slots)
+  int32_t* pst;    // [n_inst] INTERLEAVE: pool pair at which phase j starts
+  int32_t* nph;    // [E] INTERLEAVE: phases of each expert
+};
+
+__host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, int waves) {
+  return 4 * (2ull * waves * (E + 1) + static_cast<size_t>(waves) * E + 4ull * E + (E + 1) +
+              7ull * n_inst);
+}
+
+template <bool INTERLEAVE, int W>
+__global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
+    const int32_t* __restrict__ idx, int32_t N, int32_t TK, int32_t tpr, int32_t E, int32_t M,
+    int32_t S, int32_t ntiles, const int32_t* __restrict__ tile_base,
+    const int32_t* __restrict__ plans, int32_t rec_words, int32_t off_iptr, int32_t off_iend,
+    int32_t off_iphys, int32_t off_ibase, int32_t off_ilocal, int32_t n_inst,
+    int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos) {
+  using T = TileShape<W>;
+  constexpr int NT = T::kThreads;
+  extern __shared__ __align__(16) int32_t lds[];
+  LocalLds S_;
+  {
+    int32_t* q = lds;
+    S_.peers = reinterpret_cast<unsigned long long*>(q); q += 2 * W * (E + 1);
+    S_.cntw = q; q += W * E;
+    S_.blk = q; q += E;
+    S_.loc = q; q += E;
+    S_.pbase = q; q += E;
+    S_.iptr = q; q += E + 1;
+    S_.iphys = q; q += n_inst;
+    S_.irow = q; q += n_inst;
+    S_.ia = q; q += n_inst;
+    S_.ipool = q; q += n_inst;
+    S_.irho = q; q += n_inst;
+    S_.lev = q; q += n_inst;
+    S_.pst = q; q += n_inst;
+    S_.nph = q;
+  }
+  const int64_t blkid = blockIdx.x;
+  const int32_t layer = static_cast<int32_t>(blkid / ntiles);
+  const int32_t tile = static_cast<int32_t>(blkid % ntiles);
+  const int32_t src_rank = tile / tpr;
+  const int32_t* plan = plans + static_cast<int64_t>(layer) * rec_words;
+  const TileSpan span = tile_span(layer, tile, N, TK, tpr);
+  const int64_t first = span.first;
+  const int n_here = span.n;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int base = wave * T::kWavePairs;
+  const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
+  const int32_t* rb = tile_base + (static_cast<int64_t>(layer) * ntiles + src_rank * tpr) * E;
+
+  uint32_t v[T::kChunks];
+  load_tile_ids(idx + first, base, n_here, lane, E, v);
+  for (int i = threadIdx.x; i < W * (E + 1); i += NT) S_.peers[i] = 0;
+  for (int i = threadIdx.x; i < W * E; i += NT) S_.cntw[i] = 0;
+  for (int i = threadIdx.x; i <= E; i += NT) S_.iptr[i] = plan[off_iptr + i];
+  for (int e = threadIdx.x; e < E; e += NT) {
+    S_.cntw[e] = 0;
+    S_.blk[e] = rb[e];
+  }
+  __syncthreads();
+
+  // per expert: its instances' rows, local takes and pool ranges, and the
+  // instance on this tile's rank
+  for (int e = threadIdx.x; e < E; e += NT) {
+    int32_t start = 0, pool = 0, before = 0, loc = -1;
+    for (int i = S_.iptr[e]; i < S_.iptr[e + 1]; ++i) {
+      const int32_t p = plan[off_iphys + i];
+      const int32_t end = plan[off_iend + i];
+      const int32_t a = plan[off_ilocal + i];
+      const int32_t h = p / (M + S);
+      S_.iphys[i] = p;
+      S_.irow[i] = plan[off_ibase + i] + start;  // phys_off of the instance
+      S_.ia[i] = a;
+      S_.ipool[i] = pool;
+      S_.irho[i] = end - start - a;
+      pool += end - start - a;
+      if (h < src_rank) before += a;
+      if (h == src_rank) loc = i;
+      start = end;
+    }
+    S_.loc[e] = loc;
+    S_.pbase[e] = S_.blk[e] - before;
+    if (INTERLEAVE) {
+      // distinct positive remaining quotas, ascending (insertion into the
+      // expert's own instance slots), then each phase's first pool pair
+      const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
+      int m = 0;
+      for (int i = i0; i < i1; ++i) {
+        const int32_t x = S_.irho[i];
+        if (x <= 0) continue;
+        int j = m;
+        bool dup = false;
+        for (int k = 0; k < m; ++k) dup |= S_.lev[i0 + k] == x;
+        if (dup) continue;
+        while (j > 0 && S_.lev[i0 + j - 1] > x) {
+          S_.lev[i0 + j] = S_.lev[i0 + j - 1];
+          --j;
+        }
+        S_.lev[i0 + j] = x;
+        ++m;
+      }
+      int32_t prev = 0, at = 0;
+      for (int j = 0; j < m; ++j) {
+        int act = 0;
+        for (int i = i0; i < i1; ++i) act += S_.irho[i] >= S_.lev[i0 + j] ? 1 : 0;
+        S_.pst[i0 + j] = at;
+        at += (S_.lev[i0 + j] - prev) * act;
+        prev = S_.lev[i0 + j];
+      }
+      S_.nph[e] = m;
+    }
+  }
+  __syncthreads();
+
+  // pass 1: rank of each pair among the wave's earlier pairs of its expert
+  int32_t* my = S_.cntw + wave * E;
+  unsigned long long* mw = S_.peers + wave * (E + 1);
+  int32_t lr[T::kChunks];
+#pragma unroll
+  for (int c = 0; c < T::kChunks; ++c) {
+    const uint64_t peers = match_peers_lds(mw, v[c], lane);
+    const bool valid = v[c] < static_cast<uint32_t>(E);
+    const int32_t old = valid ? my[v[c]] : 0;
+    if (lane == lowest_lane(peers)) {
+      if (valid) my[v[c]] = old + __builtin_popcountll(peers);
+      mw[v[c]] = 0;
+    }
+    lr[c] = old + count_below(peers);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += NT) {
+    int32_t run = tb[e];
+#pragma unroll
+    for (int q = 0; q < W; ++q) {
+      const int32_t x = S_.cntw[q * E + e];
+      S_.cntw[q * E + e] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+
+  // pass 2
+#pragma unroll
+  for (int c = 0; c < T::kChunks; ++c) {
+    const int i = base + c * 64 + lane;
+    int32_t p = -1, row = -1;
+    if (v[c] < static_cast<uint32_t>(E)) {
+      const int e = static_cast<int>(v[c]);
+      const int32_t t = my[e] + lr[c] - S_.blk[e];
+      const int32_t L = S_.loc[e];
+      const int32_t aL = L >= 0 ? S_.ia[L] : 0;
+      if (t < aL) {
+        p = S_.iphys[L];
+        row = S_.irow[L] + t;
+      } else {
+        const int32_t u = S_.pbase[e] + t - aL;
+        const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
+        int k = i0;
+        int32_t rank_in = 0;
+        if (!INTERLEAVE) {
+          while (k < i1 - 1 && u >= S_.ipool[k] + S_.irho[k]) ++k;
+          rank_in = u - S_.ipool[k];
+        } else {
+          // the phase holding pool pair u, then its round and instance
+          const int m = S_.nph[e];
+          int j = 0;
+          while (j < m - 1 && u >= S_.pst[i0 + j + 1]) ++j;
+          const int32_t lam = m > 0 ? S_.lev[i0 + j] : 0;
+          const int32_t lam0 = j > 0 ? S_.lev[i0 + j - 1] : 0;
+          int act = 0;
+          for (int x = i0; x < i1; ++x) act += S_.irho[x] >= lam ? 1 : 0;
+          const int32_t off = u - (m > 0 ? S_.pst[i0 + j] : 0);
+          const int32_t round = lam0 + off / max(act, 1);
+          int slot = off % max(act, 1);
+          k = i1 - 1;
+          for (int x = i0; x < i1; ++x) {
+            if (S_.irho[x] >= lam) {
+              if (slot == 0) { k = x; break; }
+              --slot;
+            }
+          }
+          rank_in = round;
+        }
+        p = S_.iphys[k];
+        row = S_.irow[k] + S_.ia[k] + rank_in;
+      }
+    }
+    if (i < n_here) {
+      phys_idx[first + i] = p;
+      pos[first + i] = row;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
 // layout: inverse index and permuted weights
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__ pos,
@@ -1303,10 +1535,49 @@ hipError_t launch_reroute_w(const Shape& sh, int64_t blocks, const int32_t* idx,
   }
 }
 
+int local_waves(const Shape& sh) {
+  for (int waves : {16, 8})
+    if (local_lds_bytes(sh.E, sh.n_inst, waves) <= kLdsBytes) return waves;
+  return 4;
+}
+
+template <bool INTERLEAVE, int W>
+hipError_t launch_reroute_local_w(const Shape& sh, int64_t blocks, const int32_t* idx, const Tiling& tl,
+                                  const int32_t* tbase, const int32_t* plans, int32_t* phys_idx,
+                                  int32_t* pos, hipStream_t st) {
+  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, W);
+  const void* fn = reinterpret_cast<const void*>(&reroute_local_kernel<INTERLEAVE, W>);
+  if (rl > 65536) {
+    const hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
+    if (e != hipSuccess) return e;
+  }
+  reroute_local_kernel<INTERLEAVE, W><<<dim3(static_cast<uint32_t>(blocks)), dim3(TileShape<W>::kThreads),
+                                        rl, st>>>(
+      idx, tl.N, tl.TK, tl.tpr, sh.E, sh.M, sh.S, tl.ntiles, tbase, plans, sh.lay.words,
+      sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
+      sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE],
+      sh.lay.off[ULTRAEP_PLAN_INST_LOCAL], sh.n_inst, phys_idx, pos);
+  return hipGetLastError();
+}
+
+template <bool INTERLEAVE>
+hipError_t launch_reroute_local(const Shape& sh, int64_t blocks, const int32_t* idx, const Tiling& tl,
+                                const int32_t* tbase, const int32_t* plans, int32_t* phys_idx,
+                                int32_t* pos, hipStream_t st) {
+  switch (local_waves(sh)) {
+    case 16: return launch_reroute_local_w<INTERLEAVE, 16>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
+    case 8: return launch_reroute_local_w<INTERLEAVE, 8>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
+    default: return launch_reroute_local_w<INTERLEAVE, 4>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
+  }
+}
+
 }  // namespace
 
 size_t rerouting_lds_bytes(const Shape& sh, bool layout) {
-  return reroute_lds_bytes(sh.E, sh.n_inst, layout, reroute_waves(sh, layout));
+  const size_t a = reroute_lds_bytes(sh.E, sh.n_inst, layout, reroute_waves(sh, layout));
+  const size_t b = local_lds_bytes(sh.E, sh.n_inst, local_waves(sh));
+  return a > b ? a : b;
 }
 
 size_t plan_lds_bytes(const Shape& sh) {
@@ -1333,7 +1604,7 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   }
   PlanParams pp{};
   pp.E = sh.E; pp.R = sh.R; pp.S = sh.S; pp.D = sh.D; pp.M = sh.M; pp.P = sh.P;
-  pp.ndom = sh.ndom; pp.n_inst = sh.n_inst; pp.N = N; pp.ntiles = ntiles;
+  pp.ndom = sh.ndom; pp.n_inst = sh.n_inst; pp.N = N; pp.ntiles = ntiles; pp.tpr = tl.tpr;
   pp.eps_num = sh.eps_num; pp.eps_den = sh.eps_den; pp.allow_zero = sh.allow_zero;
   pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den;
   pp.rec_words = sh.lay.words;
@@ -1359,12 +1630,18 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
     e = launch_plan_m<8>(sh.M, pp, L, lds, hist, tbase, plans, st);
   if (e != hipSuccess) return e;
   if (blocks > 0) {
-    if (inv != nullptr)
+    if (sh.reroute_mode != ULTRAEP_REROUTE_RANGES) {
+      e = sh.reroute_mode == ULTRAEP_REROUTE_INTERLEAVE
+              ? launch_reroute_local<true>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st)
+              : launch_reroute_local<false>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
+      if (e == hipSuccess && inv != nullptr) e = launch_layout(L, N, pos, w, inv, w_perm, st);
+    } else if (inv != nullptr) {
       e = launch_reroute_w<true>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos, inv,
                                  w_perm, st);
-    else
+    } else {
       e = launch_reroute_w<false>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos,
                                   nullptr, nullptr, st);
+    }
   }
   return e;
 }

@@ -84,11 +84,28 @@ def assert_plan_equal(ctx, words: np.ndarray, pl: O.Plan, N: int):
     return g
 
 
+def rank_counts(idx: np.ndarray, R: int, E: int) -> np.ndarray:
+    """Pairs of each expert from each rank's tokens (pairs are rank-major)."""
+    ids = np.asarray(idx).reshape(-1).astype(np.int64)
+    src = np.arange(ids.size) // max(1, ids.size // R)
+    ok = (ids >= 0) & (ids < E)
+    rc = np.zeros((R, E), dtype=np.int64)
+    np.add.at(rc, (src[ok], ids[ok]), 1)
+    return rc
+
+
 def assert_layer_equal(ctx, got: dict, layer: int, idx: np.ndarray, wt: np.ndarray | None,
                        E: int, R: int, S: int, D: int, **opts):
     pl, phys, pos = O.balance(idx, E, R, S, D, **opts)
+    mode = getattr(ctx, "reroute_mode", 0)
+    if mode:
+        phys, pos = O.reroute_local(idx, pl, interleave=(mode == 2))
     N = idx.size
     assert_plan_equal(ctx, got["plans"][layer], pl, N)
+    g = ctx.decode_plan(got["plans"][layer])
+    n = int(pl.inst_ptr[-1])
+    assert np.array_equal(g["inst_local"][:n].astype(np.int64), O.local_takes(pl, rank_counts(idx, R, E)))
+    assert (g["inst_local"][n:] == 0).all()
     assert np.array_equal(got["phys"][layer].astype(np.int64), phys)
     assert np.array_equal(got["pos"][layer].astype(np.int64), pos)
     if wt is not None:

@@ -69,6 +69,11 @@ def test_create_rejects_bad_options():
             U.ultraep_create(8, 4, 1, 4, threshold=thr)
     U.ultraep_create(8, 4, 1, 4, threshold=(0, 0)).close()   # 0/0: the default 1
     U.ultraep_create(8, 4, 1, 4, threshold=(64, 1)).close()
+    for mode in (0, 1, 2):
+        U.ultraep_create(8, 4, 1, 4, reroute_mode=mode).close()
+    for mode in (-1, 3):
+        with pytest.raises(U.UltraEPError):
+            U.ultraep_create(8, 4, 1, 4, reroute_mode=mode)
 
 
 def test_plan_layout_fields():
@@ -76,7 +81,8 @@ def test_plan_layout_fields():
     E, R, S, P = 256, 64, 2, ctx.P
     want = {"header": 64, "counts": E, "master_quota": E, "slot_expert": R * S, "slot_quota": R * S,
             "phys_load": P, "phys_off": P + 1, "inst_ptr": E + 1, "inst_phys": E + R * S,
-            "inst_end": E + R * S, "inst_base": E + R * S, "rank_before": R, "rank_after": R}
+            "inst_end": E + R * S, "inst_base": E + R * S, "rank_before": R, "rank_after": R,
+            "inst_local": E + R * S}
     end = 0
     for name in U.PLAN_FIELDS:
         off, cnt = ctx.fields[name]

@@ -306,3 +306,50 @@ def test_fold_full_size(cfg_id, numel):
         scale = np.abs(masters[i].astype(np.float64)) + sum(
             np.abs(reps[s - s0].astype(np.float64)) for s in range(s0, s1) if pl.slot_expert[s] == e)
         assert (np.abs(gm[i].astype(np.float64) - want[e]) <= 1e-6 * scale).all(), e
+
+
+# ------------------------------------------- locality-aware reroute -------
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("cfg,T", [(1, None), (2, 512), (3, 256), (5, 256)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_locality_reroute_workloads(mode, cfg, T, fused):
+    """Locality-aware reroute (mode 1) and its interleave (mode 2) against
+    the oracle's reroute_local, with the layout fused or separate."""
+    w = W.CONFIGS[cfg] if T is None else W.CONFIGS[cfg].with_(T=T)
+    say(f"locality mode={mode} cfg={cfg} T={w.T} fused={fused}")
+    idx, wt = routing_cached(cfg, 0, 0, T)
+    ctx = _ctx(w, reroute_mode=mode)
+    got = run_balance(ctx, idx[None], wt[None], w.T, w.k, fused=fused)
+    assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("E,R,S,D,T,k,invalid,allow_zero", [
+    (12, 4, 2, 2, 333, 3, 0.05, False),   # ragged tiles, dropped ids, two domains
+    (16, 4, 0, 4, 500, 2, 0.0, False),    # no slots: every instance is a master
+    (32, 8, 3, 4, 2049, 4, 0.01, True),   # zero-quota masters allowed
+    (1024, 64, 8, 64, 256, 16, 0.0, False),  # M = 16, S = 8
+    (64, 64, 1, 64, 20000, 1, 0.0, False),   # several tiles per rank (T*k > 8192)
+])
+def test_locality_reroute_edge_shapes(mode, E, R, S, D, T, k, invalid, allow_zero):
+    say(f"locality edge mode={mode} E={E} R={R} S={S} D={D} T={T} k={k}")
+    rng = np.random.default_rng([E, R, S, D, T, k, 7])
+    p = rng.dirichlet(np.full(E, 0.2))
+    N = R * T * k
+    idx = rng.choice(E, size=N, p=p).astype(np.int32)
+    if invalid:
+        idx = np.where(rng.random(N) < invalid, rng.choice([-1, E, 1 << 30], size=N), idx).astype(np.int32)
+    idx = idx.reshape(R * T, k)
+    wt = rng.random((R * T, k)).astype(np.float32)
+    ctx = U.ultraep_create(E, R, S, D, allow_zero_master=allow_zero, reroute_mode=mode)
+    got = run_balance(ctx, idx[None], wt[None], T, k)
+    assert_layer_equal(ctx, got, 0, idx, wt, E, R, S, D, allow_zero_master=allow_zero)
+
+
+def test_locality_interleave_single_layer_full_size():
+    """Mode 2 on the full single-layer workload (4,194,304 pairs)."""
+    w = W.SINGLE
+    idx, wt = routing_cached(2, 0, 0)
+    ctx = _ctx(w, reroute_mode=2)
+    got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
+    assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D)
