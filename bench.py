@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--threshold", default="1/1",
                     help="early-stop target of the quota search as num/den (the pages' default 1.0)")
+    ap.add_argument("--min-tokens", type=int, default=1,
+                    help="smallest replica quota the plan keeps (the pages' default is 1024)")
     ap.add_argument("--reroute-mode", type=int, default=0, choices=(0, 1, 2),
                     help="0: ordinal ranges; 1: locality-aware; 2: locality-aware with interleave")
     ap.add_argument("--no-weight-sync", action="store_true",
@@ -235,7 +237,7 @@ PAGES_TABLE = {6: {"initial": 1.51, "final": 1.01, "replicas_max_per_expert": 4,
                    "update_placement_ms": 0.078, "reroute_ms": 0.036}}
 
 
-def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s, thr=(1, 1)):
+def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s, thr=(1, 1), min_tokens=1):
     """Time the oracle (unchanged) on the host, stage by stage, on the same
     arrays: count, plan, reroute and layout per layer (the batch's layers or
     instances in order, as many as the budget allows), permute of the same
@@ -258,7 +260,8 @@ def cpu_baseline(w, L, routes, hidden, seg, masters, reps, slots, budget_s, thr=
         t0 = time.perf_counter()
         c, dropped = O.count(idx, w.E)
         t1 = time.perf_counter()
-        pl = O.plan(c, w.E, w.R, w.S, w.D, dropped=dropped, thr_num=thr[0], thr_den=thr[1])
+        pl = O.plan(c, w.E, w.R, w.S, w.D, dropped=dropped, thr_num=thr[0], thr_den=thr[1],
+                    min_tokens=min_tokens)
         t2 = time.perf_counter()
         phys, pos = O.reroute(idx, pl)
         t3 = time.perf_counter()
@@ -328,7 +331,8 @@ def main():
         __graft_entry__.build()
     dev = torch.device("cuda:0")
     thr = tuple(int(x) for x in args.threshold.split("/"))
-    ctx = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr, reroute_mode=args.reroute_mode)
+    ctx = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr, reroute_mode=args.reroute_mode,
+                           min_tokens=args.min_tokens)
     buf = U.Buffers(ctx, L, w.T, w.k, dev)
     if args.config == 3:
         d_idx = [torch.from_numpy(np.stack([r[0] for r in routes])).to(dev)]
@@ -592,6 +596,7 @@ def main():
     result.update(quality(ctx, [p[l] for p in plans for l in range(L)], w))
     result["threshold"] = f"{thr[0]}/{thr[1]}"
     result["reroute_mode"] = args.reroute_mode
+    result["min_tokens_per_replica"] = args.min_tokens
     balance(0)
     torch.cuda.synchronize()
     result["dispatch_traffic"] = dispatch_traffic(buf.phys_idx[0].cpu().numpy(), w)
@@ -603,7 +608,7 @@ def main():
     if not args.no_cpu_baseline:
         masters = {e: masters_h[i] for i, e in enumerate(first_experts)}
         result["cpu_baseline"] = cpu_baseline(w, L, routes, hidden, seg, masters, reps_h, slots,
-                                              args.cpu_seconds, thr)
+                                              args.cpu_seconds, thr, args.min_tokens)
     print(json.dumps(result), flush=True)
 
 

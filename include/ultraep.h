@@ -101,7 +101,11 @@ typedef struct ultraep_ctx ultraep_ctx;
  *   dealt round by round: in round t every instance with more than t pairs
  *   still to take gets the next one, in instance order.  In modes 1 and 2 an
  *   instance's layout rows hold its local pairs (pair order), then the rest
- *   (in the order dealt), and a fused layout is written by a scatter pass. */
+ *   (in the order dealt), and a fused layout is written by a scatter pass.
+ * min_tokens_per_replica ([README] "Replication planning": the minimal load
+ *   allocated to a replica; 0 means 1): a replica the greedy gives fewer
+ *   pairs is not created, its slot stays empty and its pairs stay with the
+ *   expert's master (whose rank may then end above Q*). */
 #define ULTRAEP_REROUTE_RANGES 0
 #define ULTRAEP_REROUTE_LOCAL 1
 #define ULTRAEP_REROUTE_INTERLEAVE 2
@@ -112,7 +116,8 @@ typedef struct ultraep_options {
   int32_t threshold_num;
   int32_t threshold_den;
   int32_t reroute_mode;
-  int32_t reserved[2]; /* must be zero */
+  int32_t min_tokens_per_replica;
+  int32_t reserved[1]; /* must be zero */
 } ultraep_options;
 
 /* Weight-distribution plan of ultraep_weight_sync_plan ([README]

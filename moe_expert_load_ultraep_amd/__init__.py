@@ -47,7 +47,7 @@ class _Options(ctypes.Structure):
     _fields_ = [("eps_num", ctypes.c_int32), ("eps_den", ctypes.c_int32),
                 ("allow_zero_master", ctypes.c_int32), ("threshold_num", ctypes.c_int32),
                 ("threshold_den", ctypes.c_int32), ("reroute_mode", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2)]
+                ("min_tokens_per_replica", ctypes.c_int32), ("reserved", ctypes.c_int32 * 1)]
 
 
 class _RelayOptions(ctypes.Structure):
@@ -115,9 +115,9 @@ class Context:
     """An ``ultraep_ctx``: the shape (E, R, S, D) and planning options."""
 
     def __init__(self, E: int, R: int, S: int, D: int, eps=(1, 100), allow_zero_master=False,
-                 threshold=(1, 1), reroute_mode: int = 0):
+                 threshold=(1, 1), reroute_mode: int = 0, min_tokens: int = 1):
         opt = _Options(int(eps[0]), int(eps[1]), int(bool(allow_zero_master)), int(threshold[0]),
-                       int(threshold[1]), int(reroute_mode), (ctypes.c_int32 * 2)())
+                       int(threshold[1]), int(reroute_mode), int(min_tokens), (ctypes.c_int32 * 1)())
         self.reroute_mode = int(reroute_mode)
         h = _P()
         _check("ultraep_create", lib().ultraep_create(E, R, S, D, ctypes.byref(opt), ctypes.byref(h)))
@@ -162,8 +162,9 @@ class Context:
 
 
 def ultraep_create(E: int, R: int, slots_per_rank: int, D: int, eps=(1, 100),
-                   allow_zero_master: bool = False, threshold=(1, 1), reroute_mode: int = 0) -> Context:
-    return Context(E, R, slots_per_rank, D, eps, allow_zero_master, threshold, reroute_mode)
+                   allow_zero_master: bool = False, threshold=(1, 1), reroute_mode: int = 0,
+                   min_tokens: int = 1) -> Context:
+    return Context(E, R, slots_per_rank, D, eps, allow_zero_master, threshold, reroute_mode, min_tokens)
 
 
 def ultraep_balance(ctx: Context, topk_idx, T: int, k: int, workspace, plans, phys_idx, pos,

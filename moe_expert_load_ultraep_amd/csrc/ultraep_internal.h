@@ -30,6 +30,7 @@ struct Shape {
   int32_t eps_num, eps_den, allow_zero;
   int32_t thr_num, thr_den;              // early-stop target of the quota search
   int32_t reroute_mode;                  // ULTRAEP_REROUTE_*
+  int32_t min_tokens;                    // smallest replica quota kept
   PlanLayout lay;
 };
 

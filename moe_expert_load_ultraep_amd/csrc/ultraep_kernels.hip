@@ -168,6 +168,7 @@ struct PlanParams {
   int32_t N, ntiles, tpr;
   int32_t eps_num, eps_den, allow_zero;
   int32_t thr_num, thr_den;
+  int32_t min_tokens;
   int32_t rec_words;
   int32_t G, items;  // grid quotas per probe round, (quota, domain) items per round
   int32_t scan_wgs;  // workgroups per layer that build the tile ordinal bases
@@ -745,6 +746,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       const int item = (winner - wg0) * a.ndom + d;
       e = L.res[static_cast<size_t>(item) * D * S + lr * S + j];
       q = L.res[static_cast<size_t>(a.items + item) * D * S + lr * S + j];
+      // a replica below the minimum is not created: its pairs stay with
+      // the master (the master quota below is what the slots leave)
+      if (e >= 0 && q < a.min_tokens) e = -1;
     }
     L.slotE[s] = e;
     L.slotQ[s] = e >= 0 ? q : 0;
@@ -1606,7 +1610,7 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   pp.E = sh.E; pp.R = sh.R; pp.S = sh.S; pp.D = sh.D; pp.M = sh.M; pp.P = sh.P;
   pp.ndom = sh.ndom; pp.n_inst = sh.n_inst; pp.N = N; pp.ntiles = ntiles; pp.tpr = tl.tpr;
   pp.eps_num = sh.eps_num; pp.eps_den = sh.eps_den; pp.allow_zero = sh.allow_zero;
-  pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den;
+  pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den; pp.min_tokens = sh.min_tokens;
   pp.rec_words = sh.lay.words;
   plan_rounds(sh, &pp.G, &pp.items);
   // scan workgroups: enough that each thread's run of tiles is about one

@@ -253,7 +253,7 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
 
 def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
          eps_num: int = 1, eps_den: int = 100, allow_zero_master: bool = False,
-         thr_num: int = 1, thr_den: int = 1) -> Plan:
+         thr_num: int = 1, thr_den: int = 1, min_tokens: int = 1) -> Plan:
     """Replication plan from the exact per-expert load ([README] Interface /
     "Forward and backward": ``update_placement``).
 
@@ -261,6 +261,12 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     Each expert's instances are its master and its replicas, ordered by
     ascending physical id (R10); instance i serves the ordinals
     [start_i, start_i + quota_i) of that expert's pairs, cumulatively.
+
+    [README] "Replication planning": a minimal load is allocated to a
+    replica (default 1024 there).  Read as (R34): a replica the greedy gives
+    fewer than ``min_tokens`` pairs is not created; its slot stays empty and
+    its pairs stay with the expert's master (so that rank may end above Q*).
+    The default 1 changes nothing.
     """
     if E % R or R % D or S < 0:
         raise ValueError("bad shape")
@@ -280,6 +286,8 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     slot_quota = np.zeros(R * S, dtype=np.int64)
     for r in range(R):
         for s, (e, x) in enumerate(hosted[r]):
+            if x < min_tokens:
+                continue
             slot_expert[r * S + s] = e
             slot_quota[r * S + s] = x
     master_quota = np.array(c, dtype=np.int64)

@@ -74,6 +74,10 @@ def test_create_rejects_bad_options():
     for mode in (-1, 3):
         with pytest.raises(U.UltraEPError):
             U.ultraep_create(8, 4, 1, 4, reroute_mode=mode)
+    U.ultraep_create(8, 4, 1, 4, min_tokens=0).close()       # 0: the default 1
+    U.ultraep_create(8, 4, 1, 4, min_tokens=1024).close()
+    with pytest.raises(U.UltraEPError):
+        U.ultraep_create(8, 4, 1, 4, min_tokens=-1)
 
 
 def test_plan_layout_fields():

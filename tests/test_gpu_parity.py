@@ -84,7 +84,8 @@ def test_hand_worked_plans_on_gpu():
         idx = np.full(R * T * k, -1, dtype=np.int32)
         idx[:ids.size] = np.random.default_rng(0).permutation(ids)
         ctx = U.ultraep_create(E, R, S, D, allow_zero_master=case.get("allow_zero_master", False),
-                               threshold=tuple(case.get("threshold", (1, 1))))
+                               threshold=tuple(case.get("threshold", (1, 1))),
+                               min_tokens=case.get("min_tokens", 1))
         got = run_balance(ctx, idx.reshape(1, R * T, k), None, T, k)
         g = ctx.decode_plan(got["plans"][0])
         assert g["Q_star"] == case["Q_star"] and g["grid_index"] == case["grid_index"], case["name"]
@@ -137,6 +138,17 @@ def test_threshold_single_layer(thr):
     ctx = _ctx(w, threshold=thr)
     got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
     assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D, thr_num=thr[0], thr_den=thr[1])
+
+
+@pytest.mark.parametrize("cfg,T,mt", [(2, 1024, 1024), (2, None, 1024), (6, None, 1024), (8, None, 4096)])
+def test_minimum_tokens_per_replica(cfg, T, mt):
+    """Replicas below the minimum are not created (the pages' default 1024)."""
+    w = W.CONFIGS[cfg] if T is None else W.CONFIGS[cfg].with_(T=T)
+    idx, wt = routing_cached(cfg, 0, 0, T)
+    ctx = _ctx(w, min_tokens=mt)
+    got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
+    pl, _, _ = assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D, min_tokens=mt)
+    check_plan_invariants(pl, pl.c, False, mt)
 
 
 def test_large_counts_take_the_unpacked_probe():

@@ -26,6 +26,7 @@ MUTATIONS = [
     ("ordinal off by one", 'run_start = np.searchsorted(key[order], key[order], side="left")',
      'run_start = np.searchsorted(key[order], key[order], side="right")'),
     ("no domain floor", "Q_lb = min(max(Q_mean, floor), Q_max)", "Q_lb = min(Q_mean, Q_max)"),
+    ("minimum tokens ignored", "            if x < min_tokens:\n                continue", "            if x < 0:\n                continue"),
     ("target ignored", "Q_mean = _ceil_div(total * thr_num, R * thr_den)", "Q_mean = _ceil_div(total, R)"),
     ("tolerance not per rank", "tol = max(1, (total * eps_num) // (R * eps_den))",
      "tol = max(1, (total * eps_num) // eps_den)"),
@@ -85,6 +86,7 @@ PIN_SUBSET = [
     (P.test_plan_two_ranks_closed_form, {"seed": 1}),
     (P.test_plan_uniform_home_load, {}),
     (P.test_plan_threshold_stops_at_the_target, {"which": 1, "thr": (105, 100)}),
+    (P.test_plan_minimum_tokens_per_replica, {"cfg": 2, "mt": 1024}),
     (P.test_plan_no_replication_possible, {"seed": 0, "S": 0, "D": 4}),
     (P.test_plan_invariants_random_shapes, {"seed": 3}),
     (P.test_layout_properties_workloads, {"cfg": 1, "layer": 0}),

@@ -50,13 +50,14 @@ HAND = load_golden("hand_plans.json")["cases"]
 def test_plan_hand_worked(case):
     thr = case.get("threshold", [1, 1])
     pl = O.plan(np.array(case["c"]), case["E"], case["R"], case["S"], case["D"],
-                allow_zero_master=case.get("allow_zero_master", False), thr_num=thr[0], thr_den=thr[1])
+                allow_zero_master=case.get("allow_zero_master", False), thr_num=thr[0], thr_den=thr[1],
+                min_tokens=case.get("min_tokens", 1))
     assert pl.Q_star == case["Q_star"] and pl.grid_index == case["grid_index"]
     for key in ("slot_expert", "slot_quota", "master_quota", "phys_load", "phys_off",
                 "inst_ptr", "inst_phys", "inst_end", "rank_after"):
         if key in case:
             assert getattr(pl, key).tolist() == case[key], key
-    check_plan_invariants(pl, case["c"], case.get("allow_zero_master", False))
+    check_plan_invariants(pl, case["c"], case.get("allow_zero_master", False), case.get("min_tokens", 1))
 
 
 def test_plan_hand_layout_example():
@@ -398,3 +399,26 @@ def test_plan_threshold_stops_at_the_target(which, thr):
     top = _plan_of(c, sh["E"], sh["R"], sh["S"], sh["D"], thr_num=int(pl.imbalance_before() * 1000) + 1,
                    thr_den=1000)
     assert top.n_replicas == 0 and top.Q_star == top.Q_max
+
+
+@pytest.mark.parametrize("cfg", [2, 6, 8])
+@pytest.mark.parametrize("mt", [1024, 4096])
+def test_plan_minimum_tokens_per_replica(cfg, mt):
+    """Every replica carries at least the minimum; the replicas kept are the
+    unconstrained plan's replicas that reach it, in the same slots; the rest
+    of their expert's pairs stay with its master; a minimum above every
+    replica's quota replicates nothing."""
+    w = W.CONFIGS[cfg]
+    idx, _, _ = W.routing(w)
+    c, _ = O.count(idx, w.E)
+    free = _plan_of(c, w.E, w.R, w.S, w.D)
+    pl = O.plan(c, w.E, w.R, w.S, w.D, min_tokens=mt)
+    check_plan_invariants(pl, c, False, mt)
+    keep = free.slot_quota >= mt
+    assert np.array_equal(pl.slot_expert, np.where(keep, free.slot_expert, -1))
+    assert pl.Q_star == free.Q_star
+    dropped = np.bincount(free.slot_expert[~keep & (free.slot_expert >= 0)],
+                          weights=free.slot_quota[~keep & (free.slot_expert >= 0)], minlength=w.E)
+    assert np.array_equal(pl.master_quota, free.master_quota + dropped.astype(np.int64))
+    top = O.plan(c, w.E, w.R, w.S, w.D, min_tokens=int(free.slot_quota.max()) + 1)
+    assert top.n_replicas == 0
