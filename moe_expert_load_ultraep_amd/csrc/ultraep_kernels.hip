@@ -818,12 +818,32 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       inst_phys[i] = p;
       inst_end[i] = end;
       inst_base[i] = L.pload[p] - (end - q);
-      // local take: min(quota, pairs of e from rank r's tiles)
-      int32_t own = 0;
-      for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * E + e];
-      inst_local[i] = min(q, own);
       ++i;
     }
+  }
+  // local take of each instance, min(quota, pairs of e from its rank's
+  // tiles), one thread per master or slot: the instance's index is e's
+  // first index + the ranks of e's instances below its own
+  for (int x = tid; x < E + R * S; x += kPlanThreads) {
+    int e, r;
+    int32_t q;
+    if (x < E) {
+      e = x;
+      r = e / M;
+      q = L.mq[e];
+    } else {
+      e = L.slotE[x - E];
+      if (e < 0) continue;
+      r = (x - E) / S;
+      q = L.slotQ[x - E];
+    }
+    const int home = e / M;
+    const uint64_t in_domain = D == 64 ? ~0ull : ((1ull << D) - 1);
+    const uint64_t m = (L.rmask[e] | (1ull << (home % D))) & in_domain;
+    const int i = L.iptr[e] + __builtin_popcountll(m & ((1ull << (r % D)) - 1));
+    int32_t own = 0;
+    for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * E + e];
+    inst_local[i] = min(q, own);
   }
   // unused instance entries and the padding between fields get fixed values,
   // so a record is a pure function of its inputs
@@ -1097,71 +1117,128 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
 // ranks).  Pass 1 is the same grouping as reroute_kernel and gives every
 // pair its ordinal o among its expert's pairs; t = o - (pairs of e from ranks
 // before r) is its place in rank r's block of e.  If e has an instance on
-// rank r and t is below that instance's local take, the pair is local (row
-// t of the instance).  Otherwise it is pool pair u = (pool pairs of e from
-// ranks before r) + t - local take; the pool fills the instances' remaining
-// quotas contiguously, or (INTERLEAVE) round by round: in round tau every
-// instance with rho_i > tau takes one pool pair, in instance order.  With
-// the distinct positive rho sorted, 0 = lam_0 < lam_1 < ... < lam_m, phase j
-// holds rounds [lam_{j-1}, lam_j) with act_j = #{rho_i >= lam_j} instances
-// and starts at pool pair P_j = sum over earlier phases of their rounds x
-// act; pool pair u of phase j is round lam_{j-1} + (u - P_j) / act_j of the
-// ((u - P_j) mod act_j)-th instance with rho_i >= lam_j.
+// rank r and t is below that instance's local take a_L, the pair is local
+// (row t of that instance).  Otherwise it is pool pair u = (pool pairs of e
+// from ranks before r) + t - a_L.  The pool fills the remaining quotas
+// rho_i = quota_i - a_i either contiguously in instance order, or
+// (INTERLEAVE) round by round: in round tau every instance with rho_i > tau
+// takes the next pool pair, in instance order.  Before round tau there are
+// F(tau) = sum_i min(rho_i, tau) pool pairs, so pool pair u is in the round
+// tau with F(tau) <= u < F(tau + 1), at place s = u - F(tau) among the
+// instances with rho_i > tau.  F is linear between consecutive rho values:
+// e's instances sorted by rho, each with F at its rho and the number of
+// instances whose rho is at least as large, give tau and s with one search
+// and one division.
+//
+// From one tile an instance receives its pool pairs in consecutive rows.
+// With A_i(u) the pool pairs before u that instance i takes,
+// clamp(u - pool start of i, 0, rho_i) for the contiguous fill and
+// min(rho_i, tau(u)) + [rho_i > tau(u) and fewer than s(u) instances before
+// i have rho > tau(u)] for the interleave, the tile's pool pairs [u0, u1) of
+// e put A_i(u1) - A_i(u0) pairs on instance i from row A_i(u0) of its pool
+// part.  With LAYOUT those runs, and the local run, are staged in LDS as in
+// reroute_kernel and written out with consecutive lanes on consecutive rows.
 struct LocalLds {
-  unsigned long long* peers;  // [waves][E+1]
-  int32_t* cntw;   // [waves][E]
+  unsigned long long* peers;  // [waves][E+1] lane masks (pass 1)
+  uint32_t* sp;    // [kTile] LAYOUT: staged slot, run << 16 | pair index in the tile
+                   // (pass 2; shares its words with peers)
+  int32_t* cntw;   // [waves][E] per-wave counters, then per-wave ordinal bases
+  int32_t* tcnt;   // [E] the tile's ordinal base of e, then the tile's pairs of e
   int32_t* blk;    // [E] pairs of e from ranks before r (block base)
   int32_t* loc;    // [E] instance of e on rank r, or -1
   int32_t* pbase;  // [E] pool pairs of e from ranks before r
+  int32_t* kfirst; // [E] where the tile's first pool pair of e lies: its
+                   // instance, or (INTERLEAVE) its entry of the sorted tables
   int32_t* iptr;   // [E+1]
+  int32_t* ie;     // [n_inst] expert of the instance
   int32_t* iphys;  // [n_inst]
   int32_t* irow;   // [n_inst] first layout row of the instance
   int32_t* ia;     // [n_inst] local take
-  int32_t* ipool;  // [n_inst] pool pairs before the instance's (contiguous order)
+  int32_t* ipool;  // [n_inst] the plan's cumulative quota ends, then the
+                   // pool pairs before the instance's (contiguous fill)
   int32_t* irho;   // [n_inst] remaining quota after the local take
-  int32_t* lev;    // [n_inst] INTERLEAVE: phase levels lam_j of each expert (its instance slots)
-  int32_t* pst;    // [n_inst] INTERLEAVE: pool pair at which phase j starts
-  int32_t* nph;    // [E] INTERLEAVE: phases of each expert
+  int32_t* lev;    // [n_inst] INTERLEAVE: e's rho values ascending (in e's instance entries)
+  int32_t* fv;     // [n_inst] INTERLEAVE: F at that value
+  int32_t* act;    // [n_inst] INTERLEAVE: e's instances whose rho is at least that value
+  int32_t* roff;   // [n_inst+E+1] LAYOUT: run offsets in the staging area
+                   // (instance i's pool run at i, e's local run at n_inst + e)
+  int32_t* ro0;    // [n_inst+E] LAYOUT: first layout row of the run
+  int32_t* tmp;    // [waves+1]
+  float* wt;       // [kTile] LAYOUT: the tile's routing weights, in pair order
 };
 
-__host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, int waves) {
-  return 4 * (2ull * waves * (E + 1) + static_cast<size_t>(waves) * E + 4ull * E + (E + 1) +
-              7ull * n_inst);
+__host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout, int waves) {
+  size_t words = reroute_shared_words(E, layout, waves) + static_cast<size_t>(waves) * E +
+                 5ull * E + (E + 1) + 9ull * n_inst;
+  if (layout) words += 2ull * (n_inst + E) + 1 + (waves + 1) + kTile;
+  return 4 * words;
 }
 
-template <bool INTERLEAVE, int W>
+// Round and place of pool pair u of the expert whose sorted tables are the
+// entries [i0, i1), searching from entry j (whose F is at most u's).  A u at
+// or past the end of the pool gives the last round and place 0.
+__device__ inline void interleave_round(const LocalLds& S_, int i0, int i1, int j, int32_t u,
+                                        int32_t* tau, int32_t* s) {
+  while (j < i1 && S_.fv[j] <= u) ++j;
+  if (j == i1) {
+    *tau = S_.lev[i1 - 1];
+    *s = 0;
+    return;
+  }
+  const int32_t lam0 = j > i0 ? S_.lev[j - 1] : 0;
+  const int32_t f0 = j > i0 ? S_.fv[j - 1] : 0;
+  const int32_t a = max(S_.act[j], 1);
+  const int32_t off = u - f0;
+  *tau = lam0 + off / a;
+  *s = off % a;
+}
+
+template <bool INTERLEAVE, bool LAYOUT, int W>
 __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
-    const int32_t* __restrict__ idx, int32_t N, int32_t TK, int32_t tpr, int32_t E, int32_t M,
-    int32_t S, int32_t ntiles, const int32_t* __restrict__ tile_base,
-    const int32_t* __restrict__ plans, int32_t rec_words, int32_t off_iptr, int32_t off_iend,
-    int32_t off_iphys, int32_t off_ibase, int32_t off_ilocal, int32_t n_inst,
-    int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos) {
+    const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t TK,
+    int32_t tpr, int32_t E, int32_t M, int32_t S, int32_t ntiles,
+    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans, int32_t rec_words,
+    int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase, int32_t off_ilocal,
+    int32_t n_inst, int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos,
+    int32_t* __restrict__ inv, float* __restrict__ w_perm) {
   using T = TileShape<W>;
   constexpr int NT = T::kThreads;
   extern __shared__ __align__(16) int32_t lds[];
   LocalLds S_;
   {
     int32_t* q = lds;
-    S_.peers = reinterpret_cast<unsigned long long*>(q); q += 2 * W * (E + 1);
+    S_.peers = reinterpret_cast<unsigned long long*>(q);
+    S_.sp = reinterpret_cast<uint32_t*>(q);
+    q += reroute_shared_words(E, LAYOUT, W);
     S_.cntw = q; q += W * E;
+    S_.tcnt = q; q += E;
     S_.blk = q; q += E;
     S_.loc = q; q += E;
     S_.pbase = q; q += E;
+    S_.kfirst = q; q += E;
     S_.iptr = q; q += E + 1;
+    S_.ie = q; q += n_inst;
     S_.iphys = q; q += n_inst;
     S_.irow = q; q += n_inst;
     S_.ia = q; q += n_inst;
     S_.ipool = q; q += n_inst;
     S_.irho = q; q += n_inst;
     S_.lev = q; q += n_inst;
-    S_.pst = q; q += n_inst;
-    S_.nph = q;
+    S_.fv = q; q += n_inst;
+    S_.act = q; q += n_inst;
+    if (LAYOUT) {
+      S_.roff = q; q += n_inst + E + 1;
+      S_.ro0 = q; q += n_inst + E;
+      S_.tmp = q; q += W + 1;
+      S_.wt = reinterpret_cast<float*>(q);
+    }
   }
   const int64_t blkid = blockIdx.x;
   const int32_t layer = static_cast<int32_t>(blkid / ntiles);
   const int32_t tile = static_cast<int32_t>(blkid % ntiles);
   const int32_t src_rank = tile / tpr;
   const int32_t* plan = plans + static_cast<int64_t>(layer) * rec_words;
+  const int64_t lb = static_cast<int64_t>(layer) * N;
   const TileSpan span = tile_span(layer, tile, N, TK, tpr);
   const int64_t first = span.first;
   const int n_here = span.n;
@@ -1170,72 +1247,42 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
   const int base = wave * T::kWavePairs;
   const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
   const int32_t* rb = tile_base + (static_cast<int64_t>(layer) * ntiles + src_rank * tpr) * E;
+  const int PS = M + S;
 
+  // every global load of the kernel is issued before the first wait
   uint32_t v[T::kChunks];
   load_tile_ids(idx + first, base, n_here, lane, E, v);
+  if (LAYOUT) {
+    constexpr int kPer = kTile / NT;
+    float x[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      x[u] = __builtin_nontemporal_load(
+          w + first + min(u * NT + static_cast<int>(threadIdx.x), n_here - 1));
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) S_.wt[u * NT + threadIdx.x] = x[u];
+  }
   for (int i = threadIdx.x; i < W * (E + 1); i += NT) S_.peers[i] = 0;
   for (int i = threadIdx.x; i < W * E; i += NT) S_.cntw[i] = 0;
   for (int i = threadIdx.x; i <= E; i += NT) S_.iptr[i] = plan[off_iptr + i];
   for (int e = threadIdx.x; e < E; e += NT) {
-    S_.cntw[e] = 0;
+    S_.tcnt[e] = tb[e];
     S_.blk[e] = rb[e];
+    S_.pbase[e] = rb[e];
+    S_.loc[e] = -1;
+  }
+  for (int i = threadIdx.x; i < n_inst; i += NT) {
+    S_.iphys[i] = plan[off_iphys + i];
+    S_.irow[i] = plan[off_ibase + i];
+    S_.ia[i] = plan[off_ilocal + i];
+    S_.ipool[i] = plan[off_iend + i];
   }
   __syncthreads();
 
-  // per expert: its instances' rows, local takes and pool ranges, and the
-  // instance on this tile's rank
-  for (int e = threadIdx.x; e < E; e += NT) {
-    int32_t start = 0, pool = 0, before = 0, loc = -1;
-    for (int i = S_.iptr[e]; i < S_.iptr[e + 1]; ++i) {
-      const int32_t p = plan[off_iphys + i];
-      const int32_t end = plan[off_iend + i];
-      const int32_t a = plan[off_ilocal + i];
-      const int32_t h = p / (M + S);
-      S_.iphys[i] = p;
-      S_.irow[i] = plan[off_ibase + i] + start;  // phys_off of the instance
-      S_.ia[i] = a;
-      S_.ipool[i] = pool;
-      S_.irho[i] = end - start - a;
-      pool += end - start - a;
-      if (h < src_rank) before += a;
-      if (h == src_rank) loc = i;
-      start = end;
-    }
-    S_.loc[e] = loc;
-    S_.pbase[e] = S_.blk[e] - before;
-    if (INTERLEAVE) {
-      // distinct positive remaining quotas, ascending (insertion into the
-      // expert's own instance slots), then each phase's first pool pair
-      const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
-      int m = 0;
-      for (int i = i0; i < i1; ++i) {
-        const int32_t x = S_.irho[i];
-        if (x <= 0) continue;
-        int j = m;
-        bool dup = false;
-        for (int k = 0; k < m; ++k) dup |= S_.lev[i0 + k] == x;
-        if (dup) continue;
-        while (j > 0 && S_.lev[i0 + j - 1] > x) {
-          S_.lev[i0 + j] = S_.lev[i0 + j - 1];
-          --j;
-        }
-        S_.lev[i0 + j] = x;
-        ++m;
-      }
-      int32_t prev = 0, at = 0;
-      for (int j = 0; j < m; ++j) {
-        int act = 0;
-        for (int i = i0; i < i1; ++i) act += S_.irho[i] >= S_.lev[i0 + j] ? 1 : 0;
-        S_.pst[i0 + j] = at;
-        at += (S_.lev[i0 + j] - prev) * act;
-        prev = S_.lev[i0 + j];
-      }
-      S_.nph[e] = m;
-    }
-  }
-  __syncthreads();
-
-  // pass 1: rank of each pair among the wave's earlier pairs of its expert
+  // expert of each instance; pass 1: rank of each pair among the wave's
+  // earlier pairs of its expert
+  for (int e = threadIdx.x; e < E; e += NT)
+    for (int i = S_.iptr[e]; i < S_.iptr[e + 1]; ++i) S_.ie[i] = e;
   int32_t* my = S_.cntw + wave * E;
   unsigned long long* mw = S_.peers + wave * (E + 1);
   int32_t lr[T::kChunks];
@@ -1251,18 +1298,119 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
     lr[c] = old + count_below(peers);
   }
   __syncthreads();
+
+  // per instance: its first row and remaining quota; per expert: the waves'
+  // ordinal bases and the tile's pairs of e
+  const int n_used = S_.iptr[E];
+  for (int i = threadIdx.x; i < n_used; i += NT) {
+    const int e = S_.ie[i];
+    const int32_t start = i > S_.iptr[e] ? S_.ipool[i - 1] : 0;
+    S_.irow[i] += start;  // phys_off of the instance
+    S_.irho[i] = S_.ipool[i] - start - S_.ia[i];
+  }
   for (int e = threadIdx.x; e < E; e += NT) {
-    int32_t run = tb[e];
+    const int32_t b0 = S_.tcnt[e];
+    int32_t run = b0;
 #pragma unroll
     for (int q = 0; q < W; ++q) {
       const int32_t x = S_.cntw[q * E + e];
       S_.cntw[q * E + e] = run;
       run += x;
     }
+    S_.tcnt[e] = run - b0;
   }
   __syncthreads();
 
-  // pass 2
+  // per instance: pool pairs before it, the instance on rank r and the local
+  // pairs of ranks before r, and the sorted interleave tables
+  for (int i = threadIdx.x; i < n_used; i += NT) {
+    const int e = S_.ie[i];
+    const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
+    int32_t pool = 0;
+    for (int j = i0; j < i; ++j) pool += S_.irho[j];
+    S_.ipool[i] = pool;
+    const int h = S_.iphys[i] / PS;
+    if (h == src_rank) S_.loc[e] = i;
+    // the last instance below rank r holds the local takes of ranks before r
+    if (h < src_rank && (i + 1 == i1 || S_.iphys[i + 1] / PS >= src_rank)) {
+      int32_t before = 0;
+      for (int j = i0; j <= i; ++j) before += S_.ia[j];
+      S_.pbase[e] = S_.blk[e] - before;
+    }
+    if (INTERLEAVE) {
+      const int32_t rho = S_.irho[i];
+      int ord = 0, ge = 0;
+      int32_t f = 0;
+      for (int j = i0; j < i1; ++j) {
+        const int32_t x = S_.irho[j];
+        ord += (x < rho || (x == rho && j < i)) ? 1 : 0;
+        ge += x >= rho ? 1 : 0;
+        f += min(x, rho);
+      }
+      S_.lev[i0 + ord] = rho;
+      S_.fv[i0 + ord] = f;
+      S_.act[i0 + ord] = ge;
+    }
+  }
+  __syncthreads();
+
+  // per expert: where the tile's pool pairs start, and the tile's runs
+  for (int e = threadIdx.x; e < E; e += NT) {
+    const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
+    const int32_t t0 = S_.cntw[e] - S_.blk[e], t1 = t0 + S_.tcnt[e];
+    const int L = S_.loc[e];
+    const int32_t aL = L >= 0 ? S_.ia[L] : 0;
+    const int32_t u0 = S_.pbase[e] + max(t0, aL) - aL, u1 = S_.pbase[e] + max(t1, aL) - aL;
+    if (LAYOUT) {
+      S_.roff[n_inst + e] = L >= 0 ? max(0, min(t1, aL) - t0) : 0;
+      S_.ro0[n_inst + e] = L >= 0 ? S_.irow[L] + t0 : 0;
+    }
+    if (!INTERLEAVE) {
+      int k = i0;
+      while (k < i1 - 1 && u0 >= S_.ipool[k] + S_.irho[k]) ++k;
+      S_.kfirst[e] = k;
+      if (LAYOUT) {
+        for (int i = i0; i < i1; ++i) {
+          const int32_t a0 = min(max(u0 - S_.ipool[i], 0), S_.irho[i]);
+          const int32_t a1 = min(max(u1 - S_.ipool[i], 0), S_.irho[i]);
+          S_.roff[i] = a1 - a0;
+          S_.ro0[i] = S_.irow[i] + S_.ia[i] + a0;
+        }
+      }
+    } else {
+      int j = i0;
+      while (j < i1 && S_.fv[j] <= u0) ++j;
+      S_.kfirst[e] = j;
+      if (LAYOUT) {
+        int32_t tau0, s0, tau1, s1;
+        interleave_round(S_, i0, i1, j, u0, &tau0, &s0);
+        interleave_round(S_, i0, i1, j, u1, &tau1, &s1);
+        int32_t p0 = 0, p1 = 0;  // instances before i still taking in round tau0 / tau1
+        for (int i = i0; i < i1; ++i) {
+          const int32_t r = S_.irho[i];
+          const int32_t a0 = min(r, tau0) + (r > tau0 && p0 < s0 ? 1 : 0);
+          const int32_t a1 = min(r, tau1) + (r > tau1 && p1 < s1 ? 1 : 0);
+          p0 += r > tau0 ? 1 : 0;
+          p1 += r > tau1 ? 1 : 0;
+          S_.roff[i] = a1 - a0;
+          S_.ro0[i] = S_.irow[i] + S_.ia[i] + a0;
+        }
+      }
+    }
+  }
+  if (LAYOUT) {
+    // instance entries beyond the plan's used ones are empty runs
+    for (int i = n_used + threadIdx.x; i < n_inst; i += NT) {
+      S_.roff[i] = 0;
+      S_.ro0[i] = 0;
+    }
+    __syncthreads();
+    block_exclusive_scan<NT>(S_.roff, n_inst + E, S_.tmp);
+  } else {
+    __syncthreads();
+  }
+
+  // pass 2: instance, physical expert and layout row of each pair
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c) {
     const int i = base + c * 64 + lane;
@@ -1270,47 +1418,68 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
     if (v[c] < static_cast<uint32_t>(E)) {
       const int e = static_cast<int>(v[c]);
       const int32_t t = my[e] + lr[c] - S_.blk[e];
-      const int32_t L = S_.loc[e];
+      const int L = S_.loc[e];
       const int32_t aL = L >= 0 ? S_.ia[L] : 0;
+      int run;
       if (t < aL) {
         p = S_.iphys[L];
         row = S_.irow[L] + t;
+        run = n_inst + e;
       } else {
         const int32_t u = S_.pbase[e] + t - aL;
         const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
-        int k = i0;
-        int32_t rank_in = 0;
+        int k;
+        int32_t rank_in;
         if (!INTERLEAVE) {
+          k = S_.kfirst[e];
           while (k < i1 - 1 && u >= S_.ipool[k] + S_.irho[k]) ++k;
           rank_in = u - S_.ipool[k];
         } else {
-          // the phase holding pool pair u, then its round and instance
-          const int m = S_.nph[e];
-          int j = 0;
-          while (j < m - 1 && u >= S_.pst[i0 + j + 1]) ++j;
-          const int32_t lam = m > 0 ? S_.lev[i0 + j] : 0;
-          const int32_t lam0 = j > 0 ? S_.lev[i0 + j - 1] : 0;
-          int act = 0;
-          for (int x = i0; x < i1; ++x) act += S_.irho[x] >= lam ? 1 : 0;
-          const int32_t off = u - (m > 0 ? S_.pst[i0 + j] : 0);
-          const int32_t round = lam0 + off / max(act, 1);
-          int slot = off % max(act, 1);
+          int32_t tau, s;
+          interleave_round(S_, i0, i1, S_.kfirst[e], u, &tau, &s);
           k = i1 - 1;
           for (int x = i0; x < i1; ++x) {
-            if (S_.irho[x] >= lam) {
-              if (slot == 0) { k = x; break; }
-              --slot;
+            if (S_.irho[x] > tau) {
+              if (s == 0) {
+                k = x;
+                break;
+              }
+              --s;
             }
           }
-          rank_in = round;
+          rank_in = tau;
         }
         p = S_.iphys[k];
         row = S_.irow[k] + S_.ia[k] + rank_in;
+        run = k;
+      }
+      if (LAYOUT) {
+        const int32_t sl = S_.roff[run] + (row - S_.ro0[run]);
+        if (sl >= 0 && sl < kTile) S_.sp[sl] = (static_cast<uint32_t>(run) << 16) | static_cast<uint32_t>(i);
       }
     }
     if (i < n_here) {
       phys_idx[first + i] = p;
       pos[first + i] = row;
+    }
+  }
+  if (LAYOUT) {
+    __syncthreads();
+    // the staged slots in order: consecutive threads take consecutive slots,
+    // which are consecutive layout rows inside each run.  The clamp and the
+    // checks only matter for a corrupted plan record.
+    const int nruns = n_inst + E;
+    const int nt = min(S_.roff[nruns], n_here);
+    const int32_t tile0 = span.tile0;
+    for (int j = threadIdx.x; j < nt; j += NT) {
+      const uint32_t sp = S_.sp[j];
+      const int r = static_cast<int>(sp >> 16), n = static_cast<int>(sp & 0xFFFFu);
+      if (r >= nruns || n >= n_here) continue;
+      const int32_t row = S_.ro0[r] + (j - S_.roff[r]);
+      if (row >= 0 && row < N) {
+        inv[lb + row] = tile0 + n;
+        w_perm[lb + row] = S_.wt[n];
+      }
     }
   }
 }
@@ -1539,40 +1708,53 @@ hipError_t launch_reroute_w(const Shape& sh, int64_t blocks, const int32_t* idx,
   }
 }
 
-int local_waves(const Shape& sh) {
-  for (int waves : {16, 8})
-    if (local_lds_bytes(sh.E, sh.n_inst, waves) <= kLdsBytes) return waves;
-  return 4;
+// Waves per locality workgroup, as for reroute_kernel; 0 when even four
+// waves' tables do not fit (then the layout is left to layout_kernel).
+int local_waves(const Shape& sh, bool layout) {
+  for (int waves : {16, 8, 4})
+    if (local_lds_bytes(sh.E, sh.n_inst, layout, waves) <= kLdsBytes) return waves;
+  return 0;
 }
 
-template <bool INTERLEAVE, int W>
-hipError_t launch_reroute_local_w(const Shape& sh, int64_t blocks, const int32_t* idx, const Tiling& tl,
-                                  const int32_t* tbase, const int32_t* plans, int32_t* phys_idx,
-                                  int32_t* pos, hipStream_t st) {
-  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, W);
-  const void* fn = reinterpret_cast<const void*>(&reroute_local_kernel<INTERLEAVE, W>);
+template <bool INTERLEAVE, bool LAYOUT, int W>
+hipError_t launch_reroute_local_w(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
+                                  const Tiling& tl, const int32_t* tbase, const int32_t* plans,
+                                  int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                                  hipStream_t st) {
+  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, LAYOUT, W);
+  const void* fn = reinterpret_cast<const void*>(&reroute_local_kernel<INTERLEAVE, LAYOUT, W>);
   if (rl > 65536) {
     const hipError_t e =
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
     if (e != hipSuccess) return e;
   }
-  reroute_local_kernel<INTERLEAVE, W><<<dim3(static_cast<uint32_t>(blocks)), dim3(TileShape<W>::kThreads),
-                                        rl, st>>>(
-      idx, tl.N, tl.TK, tl.tpr, sh.E, sh.M, sh.S, tl.ntiles, tbase, plans, sh.lay.words,
-      sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
-      sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE],
-      sh.lay.off[ULTRAEP_PLAN_INST_LOCAL], sh.n_inst, phys_idx, pos);
+  reroute_local_kernel<INTERLEAVE, LAYOUT, W>
+      <<<dim3(static_cast<uint32_t>(blocks)), dim3(TileShape<W>::kThreads), rl, st>>>(
+          idx, w, tl.N, tl.TK, tl.tpr, sh.E, sh.M, sh.S, tl.ntiles, tbase, plans, sh.lay.words,
+          sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
+          sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.lay.off[ULTRAEP_PLAN_INST_BASE],
+          sh.lay.off[ULTRAEP_PLAN_INST_LOCAL], sh.n_inst, phys_idx, pos, inv, w_perm);
   return hipGetLastError();
 }
 
-template <bool INTERLEAVE>
-hipError_t launch_reroute_local(const Shape& sh, int64_t blocks, const int32_t* idx, const Tiling& tl,
-                                const int32_t* tbase, const int32_t* plans, int32_t* phys_idx,
-                                int32_t* pos, hipStream_t st) {
-  switch (local_waves(sh)) {
-    case 16: return launch_reroute_local_w<INTERLEAVE, 16>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
-    case 8: return launch_reroute_local_w<INTERLEAVE, 8>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
-    default: return launch_reroute_local_w<INTERLEAVE, 4>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
+// With inv non-null the layout is fused; the caller checks that it fits.
+template <bool INTERLEAVE, bool LAYOUT>
+hipError_t launch_reroute_local(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
+                                const Tiling& tl, const int32_t* tbase, const int32_t* plans,
+                                int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                                hipStream_t st) {
+  switch (local_waves(sh, LAYOUT)) {
+    case 16:
+      return launch_reroute_local_w<INTERLEAVE, LAYOUT, 16>(sh, blocks, idx, w, tl, tbase, plans,
+                                                            phys_idx, pos, inv, w_perm, st);
+    case 8:
+      return launch_reroute_local_w<INTERLEAVE, LAYOUT, 8>(sh, blocks, idx, w, tl, tbase, plans,
+                                                           phys_idx, pos, inv, w_perm, st);
+    case 4:
+      return launch_reroute_local_w<INTERLEAVE, LAYOUT, 4>(sh, blocks, idx, w, tl, tbase, plans,
+                                                           phys_idx, pos, inv, w_perm, st);
+    default:
+      return hipErrorInvalidConfiguration;
   }
 }
 
@@ -1580,7 +1762,10 @@ hipError_t launch_reroute_local(const Shape& sh, int64_t blocks, const int32_t* 
 
 size_t rerouting_lds_bytes(const Shape& sh, bool layout) {
   const size_t a = reroute_lds_bytes(sh.E, sh.n_inst, layout, reroute_waves(sh, layout));
-  const size_t b = local_lds_bytes(sh.E, sh.n_inst, local_waves(sh));
+  // the locality kernel without the layout always has a fitting shape when
+  // this is within bounds; with it, it is used only where it fits
+  const int lw = local_waves(sh, false);
+  const size_t b = local_lds_bytes(sh.E, sh.n_inst, false, lw > 0 ? lw : 4);
   return a > b ? a : b;
 }
 
@@ -1635,10 +1820,19 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   if (e != hipSuccess) return e;
   if (blocks > 0) {
     if (sh.reroute_mode != ULTRAEP_REROUTE_RANGES) {
-      e = sh.reroute_mode == ULTRAEP_REROUTE_INTERLEAVE
-              ? launch_reroute_local<true>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st)
-              : launch_reroute_local<false>(sh, blocks, idx, tl, tbase, plans, phys_idx, pos, st);
-      if (e == hipSuccess && inv != nullptr) e = launch_layout(L, N, pos, w, inv, w_perm, st);
+      const bool il = sh.reroute_mode == ULTRAEP_REROUTE_INTERLEAVE;
+      if (inv != nullptr && local_waves(sh, true) > 0) {
+        e = il ? launch_reroute_local<true, true>(sh, blocks, idx, w, tl, tbase, plans, phys_idx,
+                                                  pos, inv, w_perm, st)
+               : launch_reroute_local<false, true>(sh, blocks, idx, w, tl, tbase, plans, phys_idx,
+                                                   pos, inv, w_perm, st);
+      } else {
+        e = il ? launch_reroute_local<true, false>(sh, blocks, idx, w, tl, tbase, plans, phys_idx,
+                                                   pos, nullptr, nullptr, st)
+               : launch_reroute_local<false, false>(sh, blocks, idx, w, tl, tbase, plans, phys_idx,
+                                                    pos, nullptr, nullptr, st);
+        if (e == hipSuccess && inv != nullptr) e = launch_layout(L, N, pos, w, inv, w_perm, st);
+      }
     } else if (inv != nullptr) {
       e = launch_reroute_w<true>(sh, blocks, idx, w, tl, tbase, plans, phys_idx, pos, inv,
                                  w_perm, st);

@@ -151,6 +151,15 @@ def test_minimum_tokens_per_replica(cfg, T, mt):
     check_plan_invariants(pl, pl.c, False, mt)
 
 
+@pytest.mark.parametrize("mode", [1, 2])
+def test_minimum_tokens_with_locality(mode):
+    w = W.CONFIGS[2].with_(T=1024)
+    idx, wt = routing_cached(2, 0, 0, 1024)
+    ctx = _ctx(w, min_tokens=1024, reroute_mode=mode)
+    got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
+    assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D, min_tokens=1024)
+
+
 def test_large_counts_take_the_unpacked_probe():
     """One expert with more than 2^22 pairs at 16 masters per rank: the
     planner's packed selection keys cannot hold such pieces, so it takes its
@@ -358,10 +367,28 @@ def test_locality_reroute_edge_shapes(mode, E, R, S, D, T, k, invalid, allow_zer
     assert_layer_equal(ctx, got, 0, idx, wt, E, R, S, D, allow_zero_master=allow_zero)
 
 
-def test_locality_interleave_single_layer_full_size():
-    """Mode 2 on the full single-layer workload (4,194,304 pairs)."""
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("fused", [True, False])
+def test_locality_several_layers_one_call(mode, fused):
+    """Eight layers of the tiny workload and three of the topology workload
+    (several tiles per rank) in one batched call each."""
+    for cfg, n, T in ((1, 8, None), (5, 3, 2048)):
+        w = W.CONFIGS[cfg] if T is None else W.CONFIGS[cfg].with_(T=T)
+        say(f"locality layers mode={mode} fused={fused} cfg={cfg} L={n}")
+        layers = [routing_cached(cfg, l, 0, T) for l in range(n)]
+        idx = np.stack([x for x, _ in layers])
+        wt = np.stack([y for _, y in layers])
+        ctx = _ctx(w, reroute_mode=mode)
+        got = run_balance(ctx, idx, wt, w.T, w.k, fused=fused)
+        for l in range(n):
+            assert_layer_equal(ctx, got, l, idx[l], wt[l], w.E, w.R, w.S, w.D)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_locality_single_layer_full_size(mode):
+    """Modes 1 and 2 on the full single-layer workload (4,194,304 pairs)."""
     w = W.SINGLE
     idx, wt = routing_cached(2, 0, 0)
-    ctx = _ctx(w, reroute_mode=2)
+    ctx = _ctx(w, reroute_mode=mode)
     got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
     assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D)
