@@ -87,6 +87,8 @@ __device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(
 // these, not HIP's struct vector types).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
 
 // Wave-wide fp32 sum in one fixed order (the same butterfly inside each row,
 // then rows 0 + 1 + 2 + 3), so repeated runs give identical bits.

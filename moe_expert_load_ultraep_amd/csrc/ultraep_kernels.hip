@@ -1138,39 +1138,70 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
 // e put A_i(u1) - A_i(u0) pairs on instance i from row A_i(u0) of its pool
 // part.  With LAYOUT those runs, and the local run, are staged in LDS as in
 // reroute_kernel and written out with consecutive lanes on consecutive rows.
+//
+// Pass 2 is bound by LDS traffic, so the set-up steps pack what it reads:
+// per expert one 8-word record, per instance one packed entry (for the
+// interleave, the instances of the phase where the tile's pool pairs of e
+// start, in round-robin order, so a pair needs one division and one entry),
+// and per run the offset from layout row to staging slot.  A pair whose pool
+// index lies past that phase (the tile straddles a change in the number of
+// instances still taking pairs) takes the general search.  The tables stay
+// small enough (about 59 KiB at E = 128) for two 16-wave workgroups per CU.
 struct LocalLds {
   unsigned long long* peers;  // [waves][E+1] lane masks (pass 1)
-  uint32_t* sp;    // [kTile] LAYOUT: staged slot, run << 16 | pair index in the tile
-                   // (pass 2; shares its words with peers)
-  int32_t* cntw;   // [waves][E] per-wave counters, then per-wave ordinal bases
-  int32_t* tcnt;   // [E] the tile's ordinal base of e, then the tile's pairs of e
-  int32_t* blk;    // [E] pairs of e from ranks before r (block base)
-  int32_t* loc;    // [E] instance of e on rank r, or -1
-  int32_t* pbase;  // [E] pool pairs of e from ranks before r
-  int32_t* kfirst; // [E] where the tile's first pool pair of e lies: its
-                   // instance, or (INTERLEAVE) its entry of the sorted tables
+  uint32_t* park;  // [kTile] the packed pair values between the passes
+                   // (shares its words with peers)
+  float* wst;      // [kTile] LAYOUT: the staged slots' routing weights (pass 2;
+                   // shares its words with peers and park)
+  uint16_t* sn;    // [kTile] LAYOUT: the staged slots' pair indices in the tile
+  int32_t* cntw;   // [waves][E] per-wave counters, then per-wave bases of t
+  int32_t* er;     // [E][8] per expert: set-up words (kEr*), then the record of pass 2
+  int32_t* al;     // INTERLEAVE: [n_inst][2] the phase's instances (its words are ipool and ie)
+  int32_t* ipool;  // [n4] the plan's cumulative quota ends, then (contiguous
+                   // fill) the pool pairs before the instance
+  int32_t* ie;     // [n4] expert of the instance
+  int32_t* pi;     // !INTERLEAVE: [n_inst][4] packed instances (its words are ie, lev, fv, act)
+  int32_t* lev;    // [n4] INTERLEAVE: e's rho values ascending (in e's instance entries)
+  int32_t* fv;     // [n4] INTERLEAVE: F at that value
+  int32_t* act;    // [n4] INTERLEAVE: e's instances whose rho is at least that value
+  int32_t* iphys;  // [n4]
+  int32_t* irow;   // [n4] first layout row of the instance
+  int32_t* ia;     // [n4] local take
+  int32_t* irho;   // [n4] remaining quota after the local take
   int32_t* iptr;   // [E+1]
-  int32_t* ie;     // [n_inst] expert of the instance
-  int32_t* iphys;  // [n_inst]
-  int32_t* irow;   // [n_inst] first layout row of the instance
-  int32_t* ia;     // [n_inst] local take
-  int32_t* ipool;  // [n_inst] the plan's cumulative quota ends, then the
-                   // pool pairs before the instance's (contiguous fill)
-  int32_t* irho;   // [n_inst] remaining quota after the local take
-  int32_t* lev;    // [n_inst] INTERLEAVE: e's rho values ascending (in e's instance entries)
-  int32_t* fv;     // [n_inst] INTERLEAVE: F at that value
-  int32_t* act;    // [n_inst] INTERLEAVE: e's instances whose rho is at least that value
   int32_t* roff;   // [n_inst+E+1] LAYOUT: run offsets in the staging area
                    // (instance i's pool run at i, e's local run at n_inst + e)
-  int32_t* ro0;    // [n_inst+E] LAYOUT: first layout row of the run
+  int32_t* ro0;    // [n_inst+E] LAYOUT: first layout row of the run, then
+                   // staging slot minus layout row
   int32_t* tmp;    // [waves+1]
-  float* wt;       // [kTile] LAYOUT: the tile's routing weights, in pair order
+  int32_t* phdr;   // INTERLEAVE: [kPhaseHeaders][4] later phases the tile reaches
+  int32_t* pent;   // INTERLEAVE: [kPhaseEntries][2] their instances, in order
+  int32_t* pcnt;   // INTERLEAVE: [4] headers and entries handed out
 };
 
-__host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout, int waves) {
-  size_t words = reroute_shared_words(E, layout, waves) + static_cast<size_t>(waves) * E +
-                 5ull * E + (E + 1) + 9ull * n_inst;
-  if (layout) words += 2ull * (n_inst + E) + 1 + (waves + 1) + kTile;
+// The tile's pool for the interleave's later phases: a tile's pool pairs of
+// an expert reach past the first phase only where the number of instances
+// still taking pairs changes inside the tile, which few (tile, expert) pairs
+// do.  Without room a pair takes the general search.
+constexpr int kPhaseHeaders = 64;
+constexpr int kPhaseEntries = 256;
+
+// Set-up words of an expert's record: the tile's ordinal base of e, then
+// its pairs in the tile; pairs of e from ranks before r; pool pairs of e
+// from ranks before r; e's instance on rank r (or -1).
+constexpr int kErWords = 8;
+constexpr int kErCount = 0, kErBlk = 1, kErPool = 2, kErLoc = 3;
+
+__host__ __device__ inline int local_n4(int n_inst) { return (n_inst + 3) & ~3; }
+
+__host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout, bool interleave,
+                                                  int waves) {
+  const size_t n4 = static_cast<size_t>(local_n4(n_inst));
+  // the shared region also parks the packed pair values between the passes
+  size_t words = reroute_shared_words(E, true, waves) + static_cast<size_t>(waves) * E +
+                 static_cast<size_t>(kErWords) * E + 9 * n4 + (E + 1);
+  if (interleave) words += 4 * kPhaseHeaders + 2 * kPhaseEntries + 4;
+  if (layout) words += kTile / 2 + 2ull * (n_inst + E) + 1 + (waves + 1);
   return 4 * words;
 }
 
@@ -1193,8 +1224,11 @@ __device__ inline void interleave_round(const LocalLds& S_, int i0, int i1, int 
   *s = off % a;
 }
 
+// Two 16-wave workgroups per CU need at most 64 VGPRs per lane (8 waves per
+// SIMD).
 template <bool INTERLEAVE, bool LAYOUT, int W>
-__global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
+__global__ __launch_bounds__(TileShape<W>::kThreads)
+__attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t TK,
     int32_t tpr, int32_t E, int32_t M, int32_t S, int32_t ntiles,
     const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans, int32_t rec_words,
@@ -1205,32 +1239,42 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
   constexpr int NT = T::kThreads;
   extern __shared__ __align__(16) int32_t lds[];
   LocalLds S_;
+  const int n4 = local_n4(n_inst);
   {
+    // the record arrays first: every offset up to the per-instance arrays is
+    // a multiple of four words, so the packed entries are 16-byte aligned
     int32_t* q = lds;
     S_.peers = reinterpret_cast<unsigned long long*>(q);
-    S_.sp = reinterpret_cast<uint32_t*>(q);
-    q += reroute_shared_words(E, LAYOUT, W);
+    S_.park = reinterpret_cast<uint32_t*>(q);
+    S_.wst = reinterpret_cast<float*>(q);
+    q += reroute_shared_words(E, true, W);
+    if (LAYOUT) {
+      S_.sn = reinterpret_cast<uint16_t*>(q);
+      q += kTile / 2;
+    }
     S_.cntw = q; q += W * E;
-    S_.tcnt = q; q += E;
-    S_.blk = q; q += E;
-    S_.loc = q; q += E;
-    S_.pbase = q; q += E;
-    S_.kfirst = q; q += E;
+    S_.er = q; q += kErWords * E;
+    if (INTERLEAVE) {
+      S_.phdr = q; q += 4 * kPhaseHeaders;
+      S_.pent = q; q += 2 * kPhaseEntries;
+      S_.pcnt = q; q += 4;
+    }
+    S_.al = q;
+    S_.ipool = q; q += n4;
+    S_.ie = q; q += n4;
+    S_.pi = S_.ie;
+    S_.lev = q; q += n4;
+    S_.fv = q; q += n4;
+    S_.act = q; q += n4;
+    S_.iphys = q; q += n4;
+    S_.irow = q; q += n4;
+    S_.ia = q; q += n4;
+    S_.irho = q; q += n4;
     S_.iptr = q; q += E + 1;
-    S_.ie = q; q += n_inst;
-    S_.iphys = q; q += n_inst;
-    S_.irow = q; q += n_inst;
-    S_.ia = q; q += n_inst;
-    S_.ipool = q; q += n_inst;
-    S_.irho = q; q += n_inst;
-    S_.lev = q; q += n_inst;
-    S_.fv = q; q += n_inst;
-    S_.act = q; q += n_inst;
     if (LAYOUT) {
       S_.roff = q; q += n_inst + E + 1;
       S_.ro0 = q; q += n_inst + E;
-      S_.tmp = q; q += W + 1;
-      S_.wt = reinterpret_cast<float*>(q);
+      S_.tmp = q;
     }
   }
   const int64_t blkid = blockIdx.x;
@@ -1248,28 +1292,19 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
   const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
   const int32_t* rb = tile_base + (static_cast<int64_t>(layer) * ntiles + src_rank * tpr) * E;
   const int PS = M + S;
+  int32_t* er = S_.er;
 
-  // every global load of the kernel is issued before the first wait
   uint32_t v[T::kChunks];
   load_tile_ids(idx + first, base, n_here, lane, E, v);
-  if (LAYOUT) {
-    constexpr int kPer = kTile / NT;
-    float x[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      x[u] = __builtin_nontemporal_load(
-          w + first + min(u * NT + static_cast<int>(threadIdx.x), n_here - 1));
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) S_.wt[u * NT + threadIdx.x] = x[u];
-  }
   for (int i = threadIdx.x; i < W * (E + 1); i += NT) S_.peers[i] = 0;
   for (int i = threadIdx.x; i < W * E; i += NT) S_.cntw[i] = 0;
   for (int i = threadIdx.x; i <= E; i += NT) S_.iptr[i] = plan[off_iptr + i];
+  if (INTERLEAVE && threadIdx.x < 4) S_.pcnt[threadIdx.x] = 0;
   for (int e = threadIdx.x; e < E; e += NT) {
-    S_.tcnt[e] = tb[e];
-    S_.blk[e] = rb[e];
-    S_.pbase[e] = rb[e];
-    S_.loc[e] = -1;
+    er[e * kErWords + kErCount] = tb[e];
+    er[e * kErWords + kErBlk] = rb[e];
+    er[e * kErWords + kErPool] = rb[e];
+    er[e * kErWords + kErLoc] = -1;
   }
   for (int i = threadIdx.x; i < n_inst; i += NT) {
     S_.iphys[i] = plan[off_iphys + i];
@@ -1280,12 +1315,13 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
   __syncthreads();
 
   // expert of each instance; pass 1: rank of each pair among the wave's
-  // earlier pairs of its expert
+  // earlier pairs of its expert.  Afterwards v[c] holds the pair's expert id
+  // (E for an invalid one) in its low 11 bits and its rank in the wave above
+  // them (E <= 1024 and a wave's pairs number at most kTile).
   for (int e = threadIdx.x; e < E; e += NT)
     for (int i = S_.iptr[e]; i < S_.iptr[e + 1]; ++i) S_.ie[i] = e;
   int32_t* my = S_.cntw + wave * E;
   unsigned long long* mw = S_.peers + wave * (E + 1);
-  int32_t lr[T::kChunks];
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c) {
     const uint64_t peers = match_peers_lds(mw, v[c], lane);
@@ -1295,12 +1331,18 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
       if (valid) my[v[c]] = old + __builtin_popcountll(peers);
       mw[v[c]] = 0;
     }
-    lr[c] = old + count_below(peers);
+    const uint32_t lr = static_cast<uint32_t>(old + count_below(peers));
+    v[c] = (lr << 11) | (valid ? v[c] : static_cast<uint32_t>(E));
   }
   __syncthreads();
+  // the packed values wait out the set-up steps in the staging area (pass 1
+  // is done with its lane masks; pass 2 reloads them before any staging),
+  // so they hold no registers meanwhile
+#pragma unroll
+  for (int c = 0; c < T::kChunks; ++c) S_.park[c * NT + threadIdx.x] = v[c];
 
-  // per instance: its first row and remaining quota; per expert: the waves'
-  // ordinal bases and the tile's pairs of e
+  // per instance: its first row and remaining quota; per expert: each
+  // wave's first t and the tile's pairs of e
   const int n_used = S_.iptr[E];
   for (int i = threadIdx.x; i < n_used; i += NT) {
     const int e = S_.ie[i];
@@ -1309,7 +1351,7 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
     S_.irho[i] = S_.ipool[i] - start - S_.ia[i];
   }
   for (int e = threadIdx.x; e < E; e += NT) {
-    const int32_t b0 = S_.tcnt[e];
+    const int32_t b0 = er[e * kErWords + kErCount] - er[e * kErWords + kErBlk];
     int32_t run = b0;
 #pragma unroll
     for (int q = 0; q < W; ++q) {
@@ -1317,25 +1359,28 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
       S_.cntw[q * E + e] = run;
       run += x;
     }
-    S_.tcnt[e] = run - b0;
+    er[e * kErWords + kErCount] = run - b0;
   }
   __syncthreads();
 
-  // per instance: pool pairs before it, the instance on rank r and the local
-  // pairs of ranks before r, and the sorted interleave tables
+  // per instance: pool pairs before it (contiguous fill), the instance on
+  // rank r and the local pairs of ranks before r, and the sorted interleave
+  // tables
   for (int i = threadIdx.x; i < n_used; i += NT) {
     const int e = S_.ie[i];
     const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
-    int32_t pool = 0;
-    for (int j = i0; j < i; ++j) pool += S_.irho[j];
-    S_.ipool[i] = pool;
+    if (!INTERLEAVE) {
+      int32_t pool = 0;
+      for (int j = i0; j < i; ++j) pool += S_.irho[j];
+      S_.ipool[i] = pool;
+    }
     const int h = S_.iphys[i] / PS;
-    if (h == src_rank) S_.loc[e] = i;
+    if (h == src_rank) er[e * kErWords + kErLoc] = i;
     // the last instance below rank r holds the local takes of ranks before r
     if (h < src_rank && (i + 1 == i1 || S_.iphys[i + 1] / PS >= src_rank)) {
       int32_t before = 0;
       for (int j = i0; j <= i; ++j) before += S_.ia[j];
-      S_.pbase[e] = S_.blk[e] - before;
+      er[e * kErWords + kErPool] = er[e * kErWords + kErBlk] - before;
     }
     if (INTERLEAVE) {
       const int32_t rho = S_.irho[i];
@@ -1354,33 +1399,107 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
   }
   __syncthreads();
 
-  // per expert: where the tile's pool pairs start, and the tile's runs
+  // per expert (one thread owns e, its record and its instances' entries):
+  // the tile's runs and the packed record of pass 2.  Record words 0-3:
+  // local take, pool offset (contiguous: u = t + it; interleave: the place x
+  // counted from the tile's first pool pair = t + it), then contiguous: first
+  // instance and end of e's instances; interleave: the bound on x inside the
+  // phase, and phase entry base | phase instances << 16.  Words 4-6: local
+  // instance's physical expert and first row, and (interleave) u - x.
   for (int e = threadIdx.x; e < E; e += NT) {
     const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
-    const int32_t t0 = S_.cntw[e] - S_.blk[e], t1 = t0 + S_.tcnt[e];
-    const int L = S_.loc[e];
+    int32_t* rec = er + e * kErWords;
+    const int32_t t0 = S_.cntw[e], t1 = t0 + rec[kErCount];
+    const int32_t pbase = rec[kErPool];
+    const int L = rec[kErLoc];
     const int32_t aL = L >= 0 ? S_.ia[L] : 0;
-    const int32_t u0 = S_.pbase[e] + max(t0, aL) - aL, u1 = S_.pbase[e] + max(t1, aL) - aL;
+    const int32_t u0 = pbase + max(t0, aL) - aL, u1 = pbase + max(t1, aL) - aL;
     if (LAYOUT) {
       S_.roff[n_inst + e] = L >= 0 ? max(0, min(t1, aL) - t0) : 0;
       S_.ro0[n_inst + e] = L >= 0 ? S_.irow[L] + t0 : 0;
     }
+    int32_t w2, w3, w6 = 0, w7 = -1;
     if (!INTERLEAVE) {
       int k = i0;
       while (k < i1 - 1 && u0 >= S_.ipool[k] + S_.irho[k]) ++k;
-      S_.kfirst[e] = k;
-      if (LAYOUT) {
-        for (int i = i0; i < i1; ++i) {
-          const int32_t a0 = min(max(u0 - S_.ipool[i], 0), S_.irho[i]);
-          const int32_t a1 = min(max(u1 - S_.ipool[i], 0), S_.irho[i]);
+      w2 = k;
+      w3 = i1;
+      for (int i = i0; i < i1; ++i) {
+        const int32_t a = S_.ia[i], r = S_.irho[i], pl0 = S_.ipool[i];
+        if (LAYOUT) {
+          const int32_t a0 = min(max(u0 - pl0, 0), r);
+          const int32_t a1 = min(max(u1 - pl0, 0), r);
           S_.roff[i] = a1 - a0;
-          S_.ro0[i] = S_.irow[i] + S_.ia[i] + a0;
+          S_.ro0[i] = S_.irow[i] + a + a0;
         }
+        i32x4 ent;
+        ent.x = S_.iphys[i];
+        ent.y = S_.irow[i] + a - pl0;  // row = this + u
+        ent.z = pl0 + r;                // end of the instance's pool range
+        ent.w = 0;
+        *reinterpret_cast<i32x4*>(S_.pi + 4 * i) = ent;
       }
     } else {
       int j = i0;
       while (j < i1 && S_.fv[j] <= u0) ++j;
-      S_.kfirst[e] = j;
+      const int32_t lam0 = j > i0 ? S_.lev[j - 1] : 0;
+      const int32_t f0 = j > i0 ? S_.fv[j - 1] : 0;
+      // the tile's first pool pair of e is round lam0 + q0, place r0 of the
+      // phase; a later pool pair u of the tile is x = u - u0 + r0 places
+      // further (x < kTile + 64, small enough for a float quotient)
+      int n = 0, q0 = 0, r0 = 0;
+      if (j < i1) {
+        const int32_t a = max(S_.act[j], 1);
+        q0 = (u0 - f0) / a;
+        r0 = (u0 - f0) - q0 * a;
+        for (int i = i0; i < i1; ++i) {
+          if (S_.irho[i] > lam0) {
+            i32x2 ent;
+            ent.x = S_.iphys[i] | (i << 16);
+            ent.y = S_.irow[i] + S_.ia[i] + lam0 + q0;  // row = this + x / a
+            *reinterpret_cast<i32x2*>(S_.al + 2 * (i0 + n)) = ent;
+            ++n;
+          }
+        }
+      }
+      w2 = j < i1 ? S_.fv[j] - u0 + r0 : 0;  // x below this: in the phase
+      w3 = i0 | (n << 16);
+      w6 = u0 - r0;                           // u = x + this
+      // the later phases the tile's pool pairs of e reach (up to the first
+      // whose end is at or past u1): a header {x bound, x at the phase
+      // start, instances | first entry << 8, rounds before the phase} and
+      // the phase's instances in order, from the tile's pool
+      if (j < i1 && S_.fv[j] < u1) {
+        int jl = j + 1;
+        while (jl < i1 - 1 && S_.fv[jl] < u1) ++jl;
+        const int nh = jl - j;
+        int ne = 0;
+        for (int jj = j + 1; jj <= jl; ++jj) ne += S_.act[jj];
+        const int hb = atomicAdd(&S_.pcnt[0], nh);
+        const int eb = atomicAdd(&S_.pcnt[1], ne);
+        if (hb + nh <= kPhaseHeaders && eb + ne <= kPhaseEntries) {
+          int ep = eb;
+          for (int jj = j + 1; jj <= jl; ++jj) {
+            const int32_t lamp = S_.lev[jj - 1];
+            i32x4 h;
+            h.x = S_.fv[jj] - w6;
+            h.y = S_.fv[jj - 1] - w6;
+            h.z = S_.act[jj] | (ep << 8);
+            h.w = lamp;
+            *reinterpret_cast<i32x4*>(S_.phdr + 4 * (hb + jj - j - 1)) = h;
+            for (int i = i0; i < i1; ++i) {
+              if (S_.irho[i] > lamp) {
+                i32x2 ent;
+                ent.x = S_.iphys[i] | (i << 16);
+                ent.y = S_.irow[i] + S_.ia[i];
+                *reinterpret_cast<i32x2*>(S_.pent + 2 * ep) = ent;
+                ++ep;
+              }
+            }
+          }
+          w7 = hb | (nh << 16);
+        }
+      }
       if (LAYOUT) {
         int32_t tau0, s0, tau1, s1;
         interleave_round(S_, i0, i1, j, u0, &tau0, &s0);
@@ -1397,6 +1516,17 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
         }
       }
     }
+    i32x4 lo, hi;
+    lo.x = aL;
+    lo.y = pbase - aL - w6;  // u (contiguous) or x (interleave) = t + this
+    lo.z = w2;
+    lo.w = w3;
+    hi.x = L >= 0 ? S_.iphys[L] : -1;
+    hi.y = L >= 0 ? S_.irow[L] : 0;
+    hi.z = w6;
+    hi.w = w7;
+    *reinterpret_cast<i32x4*>(rec) = lo;
+    *reinterpret_cast<i32x4*>(rec + 4) = hi;
   }
   if (LAYOUT) {
     // instance entries beyond the plan's used ones are empty runs
@@ -1406,79 +1536,197 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_local_kernel(
     }
     __syncthreads();
     block_exclusive_scan<NT>(S_.roff, n_inst + E, S_.tmp);
-  } else {
-    __syncthreads();
+    for (int r = threadIdx.x; r < n_inst + E; r += NT) S_.ro0[r] = S_.roff[r] - S_.ro0[r];
   }
+  __syncthreads();
 
-  // pass 2: instance, physical expert and layout row of each pair
+#pragma unroll
+  for (int c = 0; c < T::kChunks; ++c) v[c] = S_.park[c * NT + threadIdx.x];
+  // each pair's routing weight, one coalesced load per chunk, issued here
+  // so that they are in flight behind the LDS work of pass 2
+  float wl[LAYOUT ? T::kChunks : 1];
+  if (LAYOUT) {
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c)
+      wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
+  }
+  __syncthreads();
+
+  // pass 2: instance, physical expert and layout row of each pair.  The
+  // tile's stretches of phys_idx and pos are written through buffer
+  // resources sized to the tile (stores past it are dropped), which keeps
+  // the eight chunks' addresses out of vector registers.  Interleaved pool
+  // pairs past the tile's first phase of their expert are left to a second
+  // loop, which keeps the rare paths out of the unrolled one.
+  const __amdgpu_buffer_rsrc_t r_phys = row_rsrc(phys_idx + first, static_cast<uint32_t>(n_here) * 4u);
+  const __amdgpu_buffer_rsrc_t r_pos = row_rsrc(pos + first, static_cast<uint32_t>(n_here) * 4u);
+  uint32_t later = 0;
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c) {
     const int i = base + c * 64 + lane;
     int32_t p = -1, row = -1;
-    if (v[c] < static_cast<uint32_t>(E)) {
-      const int e = static_cast<int>(v[c]);
-      const int32_t t = my[e] + lr[c] - S_.blk[e];
-      const int L = S_.loc[e];
-      const int32_t aL = L >= 0 ? S_.ia[L] : 0;
-      int run;
-      if (t < aL) {
-        p = S_.iphys[L];
-        row = S_.irow[L] + t;
+    int run = -1;
+    const int e = static_cast<int>(v[c] & 0x7FFu);
+    if (e < E) {
+      const int32_t t = my[e] + static_cast<int32_t>(v[c] >> 11);
+      const i32x4 lo = *reinterpret_cast<const i32x4*>(er + e * kErWords);
+      if (t < lo.x) {
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(er + e * kErWords + 4);
+        p = hi.x;
+        row = hi.y + t;
         run = n_inst + e;
+      } else if (!INTERLEAVE) {
+        const int32_t u = t + lo.y;
+        int k = lo.z;
+        while (k < lo.w - 1 && u >= S_.pi[4 * k + 2]) ++k;
+        const i32x4 ent = *reinterpret_cast<const i32x4*>(S_.pi + 4 * k);
+        p = ent.x;
+        row = ent.y + u;
+        run = k;
       } else {
-        const int32_t u = S_.pbase[e] + t - aL;
-        const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
-        int k;
-        int32_t rank_in;
-        if (!INTERLEAVE) {
-          k = S_.kfirst[e];
-          while (k < i1 - 1 && u >= S_.ipool[k] + S_.irho[k]) ++k;
-          rank_in = u - S_.ipool[k];
+        const int32_t x = t + lo.y;
+        if (x < lo.z) {
+          // the phase of the tile's first pool pair of e, as nearly always:
+          // x / a from a float reciprocal (x < 2^14, a <= 64: the estimate
+          // is within one of the quotient, and the remainder fixes it)
+          const int32_t a = max(lo.w >> 16, 1);
+          int32_t q = static_cast<int32_t>(static_cast<float>(x) *
+                                           __builtin_amdgcn_rcpf(static_cast<float>(a)));
+          int32_t r = x - q * a;
+          if (r < 0) {
+            --q;
+            r += a;
+          } else if (r >= a) {
+            ++q;
+            r -= a;
+          }
+          const i32x2 ent = *reinterpret_cast<const i32x2*>(S_.al + 2 * ((lo.w & 0xFFFF) + r));
+          p = ent.x & 0xFFFF;
+          row = ent.y + q;
+          run = ent.x >> 16;
         } else {
+          later |= 1u << c;
+        }
+      }
+    }
+    if (!(later >> c & 1u)) {
+      if (LAYOUT && run >= 0) {
+        const int32_t sl = row + S_.ro0[run];
+        if (sl >= 0 && sl < kTile) {
+          S_.sn[sl] = static_cast<uint16_t>(i);
+          S_.wst[sl] = wl[c];
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, 0);
+    }
+  }
+  if (INTERLEAVE && later != 0u) {
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c) {
+      if (later >> c & 1u) {
+        const int i = base + c * 64 + lane;
+        const int e = static_cast<int>(v[c] & 0x7FFu);
+        const int32_t t = my[e] + static_cast<int32_t>(v[c] >> 11);
+        const i32x4 lo = *reinterpret_cast<const i32x4*>(er + e * kErWords);
+        const i32x4 hi = *reinterpret_cast<const i32x4*>(er + e * kErWords + 4);
+        const int32_t x = t + lo.y;
+        int32_t p = -1, row = -1;
+        int run = -1;
+        if (hi.w >= 0) {
+          // a later phase from the tile's pool: d = x - (x at its start) is
+          // below kTile + 64 as well
+          const int hb = hi.w & 0xFFFF, he = hb + (hi.w >> 16);
+          for (int h = hb; h < he; ++h) {
+            const i32x4 hd = *reinterpret_cast<const i32x4*>(S_.phdr + 4 * h);
+            if (x < hd.x) {
+              const int32_t a = max(hd.z & 0xFF, 1);
+              const int32_t d = x - hd.y;
+              int32_t q = static_cast<int32_t>(static_cast<float>(d) *
+                                               __builtin_amdgcn_rcpf(static_cast<float>(a)));
+              int32_t r = d - q * a;
+              if (r < 0) {
+                --q;
+                r += a;
+              } else if (r >= a) {
+                ++q;
+                r -= a;
+              }
+              const i32x2 ent = *reinterpret_cast<const i32x2*>(S_.pent + 2 * ((hd.z >> 8) + r));
+              p = ent.x & 0xFFFF;
+              row = ent.y + hd.w + q;
+              run = ent.x >> 16;
+              break;
+            }
+          }
+        }
+        if (run < 0) {
+          // the general search (the tile's pool was full)
+          const int i0 = lo.w & 0xFFFF, i1 = S_.iptr[e + 1];
           int32_t tau, s;
-          interleave_round(S_, i0, i1, S_.kfirst[e], u, &tau, &s);
-          k = i1 - 1;
-          for (int x = i0; x < i1; ++x) {
-            if (S_.irho[x] > tau) {
+          interleave_round(S_, i0, i1, i0, x + hi.z, &tau, &s);
+          int k = i1 - 1;
+          for (int y = i0; y < i1; ++y) {
+            if (S_.irho[y] > tau) {
               if (s == 0) {
-                k = x;
+                k = y;
                 break;
               }
               --s;
             }
           }
-          rank_in = tau;
+          p = S_.iphys[k];
+          row = S_.irow[k] + S_.ia[k] + tau;
+          run = k;
         }
-        p = S_.iphys[k];
-        row = S_.irow[k] + S_.ia[k] + rank_in;
-        run = k;
+        if (LAYOUT) {
+          const int32_t sl = row + S_.ro0[run];
+          if (sl >= 0 && sl < kTile) {
+            S_.sn[sl] = static_cast<uint16_t>(i);
+            S_.wst[sl] = wl[c];
+          }
+        }
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, 0);
       }
-      if (LAYOUT) {
-        const int32_t sl = S_.roff[run] + (row - S_.ro0[run]);
-        if (sl >= 0 && sl < kTile) S_.sp[sl] = (static_cast<uint32_t>(run) << 16) | static_cast<uint32_t>(i);
-      }
-    }
-    if (i < n_here) {
-      phys_idx[first + i] = p;
-      pos[first + i] = row;
     }
   }
   if (LAYOUT) {
     __syncthreads();
     // the staged slots in order: consecutive threads take consecutive slots,
-    // which are consecutive layout rows inside each run.  The clamp and the
-    // checks only matter for a corrupted plan record.
+    // which are consecutive layout rows inside each run.  A slot's run is
+    // the last one starting at or before it: a binary search over the run
+    // offsets in a fixed number of steps (runs number fewer than 4096), so
+    // the searches of a thread's slots interleave.  The checks only matter
+    // for a corrupted plan record.
+    constexpr int kPer = kTile / NT;
+    constexpr int kSearchSteps = 12;
     const int nruns = n_inst + E;
     const int nt = min(S_.roff[nruns], n_here);
     const int32_t tile0 = span.tile0;
-    for (int j = threadIdx.x; j < nt; j += NT) {
-      const uint32_t sp = S_.sp[j];
-      const int r = static_cast<int>(sp >> 16), n = static_cast<int>(sp & 0xFFFFu);
-      if (r >= nruns || n >= n_here) continue;
-      const int32_t row = S_.ro0[r] + (j - S_.roff[r]);
-      if (row >= 0 && row < N) {
-        inv[lb + row] = tile0 + n;
-        w_perm[lb + row] = S_.wt[n];
+    int lo[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) lo[u] = 0;
+    // invariant: roff[lo] <= j; the step sizes halve from 2^11
+#pragma unroll
+    for (int st = kSearchSteps - 1; st >= 0; --st) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int j = u * NT + static_cast<int>(threadIdx.x);
+        const int mid = lo[u] + (1 << st);
+        if (mid < nruns && S_.roff[mid] <= j) lo[u] = mid;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = u * NT + static_cast<int>(threadIdx.x);
+      if (j < nt) {
+        const int n = S_.sn[j];
+        const int32_t row = j - S_.ro0[lo[u]];
+        if (n < n_here && row >= 0 && row < N) {
+          inv[lb + row] = tile0 + n;
+          w_perm[lb + row] = S_.wst[j];
+        }
       }
     }
   }
@@ -1712,7 +1960,7 @@ hipError_t launch_reroute_w(const Shape& sh, int64_t blocks, const int32_t* idx,
 // waves' tables do not fit (then the layout is left to layout_kernel).
 int local_waves(const Shape& sh, bool layout) {
   for (int waves : {16, 8, 4})
-    if (local_lds_bytes(sh.E, sh.n_inst, layout, waves) <= kLdsBytes) return waves;
+    if (local_lds_bytes(sh.E, sh.n_inst, layout, true, waves) <= kLdsBytes) return waves;
   return 0;
 }
 
@@ -1721,7 +1969,7 @@ hipError_t launch_reroute_local_w(const Shape& sh, int64_t blocks, const int32_t
                                   const Tiling& tl, const int32_t* tbase, const int32_t* plans,
                                   int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
                                   hipStream_t st) {
-  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, LAYOUT, W);
+  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, LAYOUT, INTERLEAVE, W);
   const void* fn = reinterpret_cast<const void*>(&reroute_local_kernel<INTERLEAVE, LAYOUT, W>);
   if (rl > 65536) {
     const hipError_t e =
@@ -1765,7 +2013,7 @@ size_t rerouting_lds_bytes(const Shape& sh, bool layout) {
   // the locality kernel without the layout always has a fitting shape when
   // this is within bounds; with it, it is used only where it fits
   const int lw = local_waves(sh, false);
-  const size_t b = local_lds_bytes(sh.E, sh.n_inst, false, lw > 0 ? lw : 4);
+  const size_t b = local_lds_bytes(sh.E, sh.n_inst, false, true, lw > 0 ? lw : 4);
   return a > b ? a : b;
 }
 
