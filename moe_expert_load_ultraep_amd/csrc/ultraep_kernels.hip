@@ -469,13 +469,24 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     nh += me ? 1 : 0;
   };
 
-  const int max_steps = D * S + 1;
-  for (int step = 0; step <= max_steps; ++step) {
+  // the queue's pop key: the largest piece, ties to the lowest expert id
+  auto queue_key = [&]() {
     uint32_t mk = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j)
       mk = max(mk, pa[j] > 0 ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u);
-    const uint32_t km = wave_max_bcast(mk);
+    return mk;
+  };
+
+  // One reduction stage per step: the receiver key, the donor key and the
+  // queue's key after the pop are reduced together.  The next pop key is
+  // then known without another reduction: a fit leaves the queue as the pop
+  // left it; a chain grows the donor's piece (its key grows by the pairs
+  // added, the tie bits stay) and may re-queue the rest of the popped piece
+  // under its own tie bits; a fill re-queues the rest.
+  uint32_t km = wave_max_bcast(queue_key());
+  const int max_steps = D * S + 1;
+  for (int step = 0; step <= max_steps; ++step) {
     if (km == 0) {
       if (act) {
 #pragma unroll
@@ -507,12 +518,16 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
                        ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u);
     const uint32_t kmax = wave_max_bcast(key);
     const uint32_t dmax = wave_max_bcast(dk);
+    const uint32_t knext = wave_max_bcast(queue_key());
     const int kl = 63 - static_cast<int>(kmax & 63);
     if (kmax & (kFitBit << 6)) {  // fit
       spare -= lane == kl ? amt : 0;
       place(kl, e, amt);
+      km = knext;
       continue;
     }
+    const uint32_t own_tie = km & TMASK;
+    km = knext;
     const int32_t rmax = static_cast<int32_t>(kmax >> 6);  // roomiest spare (0: none)
     if (dmax > 0) {  // chain through the donor's rank
       const uint32_t dt = TMASK - (dmax & TMASK);
@@ -534,6 +549,7 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
         pa[j] += here ? x : 0;
         room[j] -= here ? x : 0;
       }
+      km = max(km, dmax + (static_cast<uint32_t>(x) << TB));
       amt -= x;
     } else if (rmax > 0) {  // fill the roomiest receiver
       place(kl, e, rmax);
@@ -545,6 +561,7 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     if (amt > 0) {
 #pragma unroll
       for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? amt : pa[j];
+      km = max(km, (static_cast<uint32_t>(amt) << TB) | own_tie);
     }
   }
   return false;
@@ -617,7 +634,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
   const PlanLds L = carve(lds, a);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = lane_id();
+  // the wave index is uniform: kept in a scalar register, so the probe's
+  // per-item values (quota, domain, popped expert) stay scalar too
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = lane_id();
   int32_t* rec = plans + static_cast<int64_t>(layer) * a.rec_words;
 
   if (tid < kScalars) L.scal[tid] = 0;
