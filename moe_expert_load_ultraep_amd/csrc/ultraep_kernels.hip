@@ -926,10 +926,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 //
 // With LAYOUT the kernel also writes the inverse index and permuted weights.
 // Inside one tile, the pairs that land on one instance have consecutive
-// ordinals, so they fill one contiguous run of layout rows.  Each pair is
-// first placed at its run's slot in LDS; the runs are then written out with
-// consecutive lanes on consecutive rows, instead of one 4-byte scatter per
-// pair.
+// ordinals, so they fill one contiguous run of layout rows.  Each pair's
+// weight and index are first placed at its run's slot in LDS; the runs are
+// then written out with consecutive lanes on consecutive rows, instead of
+// one 4-byte scatter per pair.  The staged weights reuse the words of the
+// grouping masks and the indices are 16-bit, which keeps the tables (about
+// 64 KiB at E = 128) small enough for two 16-wave workgroups per CU.
 struct RerouteLds {
   unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids (pass 1)
   int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
@@ -942,9 +944,9 @@ struct RerouteLds {
   int32_t* roff;   // [n_inst+1] run offsets inside the tile's staging area
   int32_t* ro0;    // [n_inst] first ordinal of the run
   int32_t* tmp;    // [waves + 1]
-  float* wt;       // [kTile] the tile's routing weights, in pair order
-  uint32_t* sp;    // [kTile] staged slot: run index << 16 | pair index inside the tile
-                   // (pass 2; shares its words with peers, which pass 1 is done with)
+  float* wst;      // [kTile] staged slot's routing weight (pass 2; shares its
+                   // words with peers, which pass 1 is done with)
+  uint16_t* sn;    // [kTile] staged slot's pair index inside the tile
 };
 
 // Words of the region that holds peers, and with the layout also sp.
@@ -956,12 +958,14 @@ __host__ __device__ inline size_t reroute_shared_words(int E, bool layout, int w
 __host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layout, int waves) {
   size_t words = reroute_shared_words(E, layout, waves) + static_cast<size_t>(waves) * E + 2ull * E +
                  (E + 1) + 3ull * n_inst;
-  if (layout) words += (n_inst + 1) + n_inst + (waves + 1) + kTile;
+  if (layout) words += (n_inst + 1) + n_inst + (waves + 1) + kTile / 2;
   return 4 * words;
 }
 
+// Two 16-wave workgroups per CU need at most 64 VGPRs per lane.
 template <bool LAYOUT, int W>
-__global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
+__global__ __launch_bounds__(TileShape<W>::kThreads)
+__attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t TK, int32_t tpr,
     int32_t E, int32_t ntiles, const int32_t* __restrict__ tile_base, const int32_t* __restrict__ plans,
     int32_t rec_words, int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase,
@@ -974,7 +978,7 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
   {
     int32_t* q = lds;
     S.peers = reinterpret_cast<unsigned long long*>(q);
-    S.sp = reinterpret_cast<uint32_t*>(q);
+    S.wst = reinterpret_cast<float*>(q);
     q += reroute_shared_words(E, LAYOUT, W);
     S.cntw = q; q += W * E;
     S.tcnt = q; q += E;
@@ -987,7 +991,7 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
       S.roff = q; q += n_inst + 1;
       S.ro0 = q; q += n_inst;
       S.tmp = q; q += W + 1;
-      S.wt = reinterpret_cast<float*>(q);
+      S.sn = reinterpret_cast<uint16_t*>(q);
     }
   }
   const int64_t blk = blockIdx.x;
@@ -1003,19 +1007,8 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
   const int base = wave * T::kWavePairs;
   const int32_t* tb = tile_base + (static_cast<int64_t>(layer) * ntiles + tile) * E;
 
-  // every global load of the kernel is issued before the first wait
   uint32_t v[T::kChunks];
   load_tile_ids(idx + first, base, n_here, lane, E, v);
-  if (LAYOUT) {
-    constexpr int kPer = kTile / NT;
-    float x[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      x[u] = __builtin_nontemporal_load(
-          w + first + min(u * NT + static_cast<int>(threadIdx.x), n_here - 1));
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) S.wt[u * NT + threadIdx.x] = x[u];
-  }
   for (int i = threadIdx.x; i < W * (E + 1); i += NT) S.peers[i] = 0;
   for (int i = threadIdx.x; i < W * E; i += NT) S.cntw[i] = 0;
   for (int i = threadIdx.x; i <= E; i += NT) S.iptr[i] = plan[off_iptr + i];
@@ -1027,10 +1020,11 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
   for (int e = threadIdx.x; e < E; e += NT) S.tcnt[e] = tb[e];
   __syncthreads();
 
-  // pass 1: rank of each pair among the wave's earlier pairs of its expert
+  // pass 1: rank of each pair among the wave's earlier pairs of its expert.
+  // Afterwards v[c] holds the pair's expert id (E for an invalid one) in its
+  // low 11 bits and its rank in the wave above them.
   int32_t* my = S.cntw + wave * E;
   unsigned long long* mw = S.peers + wave * (E + 1);
-  int32_t lr[T::kChunks];
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c) {
     const uint64_t peers = match_peers_lds(mw, v[c], lane);
@@ -1040,9 +1034,17 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
       if (valid) my[v[c]] = old + __builtin_popcountll(peers);
       mw[v[c]] = 0;
     }
-    lr[c] = old + count_below(peers);
+    const uint32_t lr = static_cast<uint32_t>(old + count_below(peers));
+    v[c] = (lr << 11) | (valid ? v[c] : static_cast<uint32_t>(E));
   }
   __syncthreads();
+  // with the layout, the packed values wait out the steps up to pass 2 in
+  // the staging words (pass 1 is done with its lane masks), so they hold no
+  // registers meanwhile
+  if (LAYOUT) {
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c) reinterpret_cast<uint32_t*>(S.wst)[c * NT + threadIdx.x] = v[c];
+  }
   for (int e = threadIdx.x; e < E; e += NT) {
     const int32_t b0 = S.tcnt[e];
     int32_t run = b0;
@@ -1083,46 +1085,83 @@ __global__ __launch_bounds__(TileShape<W>::kThreads) void reroute_kernel(
     }
     __syncthreads();
     block_exclusive_scan<NT>(S.roff, n_inst, S.tmp);
+    // ro0 becomes staging slot minus layout row of each run
+    for (int i = threadIdx.x; i < n_inst; i += NT) S.ro0[i] = S.roff[i] - S.ibase[i] - S.ro0[i];
+    __syncthreads();
   }
 
-  // pass 2: instance, physical expert and layout row of each pair
+  // pass 2: instance, physical expert and layout row of each pair; with the
+  // layout, each pair's weight (one coalesced load per chunk, issued first)
+  // and index go to its run's slot
+  float wl[LAYOUT ? T::kChunks : 1];
+  if (LAYOUT) {
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c)
+      wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c) v[c] = reinterpret_cast<const uint32_t*>(S.wst)[c * NT + threadIdx.x];
+    __syncthreads();
+  }
+  const __amdgpu_buffer_rsrc_t r_phys = row_rsrc(phys_idx + first, static_cast<uint32_t>(n_here) * 4u);
+  const __amdgpu_buffer_rsrc_t r_pos = row_rsrc(pos + first, static_cast<uint32_t>(n_here) * 4u);
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c) {
     const int i = base + c * 64 + lane;
     int32_t p = -1, row = -1;
-    if (v[c] < static_cast<uint32_t>(E)) {
-      const int e = static_cast<int>(v[c]);
-      const int32_t o = my[e] + lr[c];
+    const int e = static_cast<int>(v[c] & 0x7FFu);
+    if (e < E) {
+      const int32_t o = my[e] + static_cast<int32_t>(v[c] >> 11);
       int k = S.kfirst[e];
       const int last = S.iptr[e + 1] - 1;
       while (k < last && o >= S.iend[k]) ++k;
       p = S.iphys[k];
       row = S.ibase[k] + o;
       if (LAYOUT) {
-        const int32_t sl = S.roff[k] + (o - S.ro0[k]);
-        if (sl >= 0 && sl < kTile) S.sp[sl] = (static_cast<uint32_t>(k) << 16) | static_cast<uint32_t>(i);
+        const int32_t sl = row + S.ro0[k];
+        if (sl >= 0 && sl < kTile) {
+          S.sn[sl] = static_cast<uint16_t>(i);
+          S.wst[sl] = wl[c];
+        }
       }
     }
-    if (i < n_here) {
-      phys_idx[first + i] = p;
-      pos[first + i] = row;
-    }
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, 0);
   }
   if (LAYOUT) {
     __syncthreads();
     // write the staged slots in order: consecutive threads take consecutive
-    // slots, which are consecutive layout rows inside each run.  A tile holds
-    // at most n_here valid pairs; the clamp and the row check only matter for
-    // a corrupted plan record.
+    // slots, which are consecutive layout rows inside each run.  A slot's
+    // run is the last one starting at or before it: a binary search over
+    // the run offsets in a fixed number of steps (instances number fewer
+    // than 4096), so the searches of a thread's slots interleave.  A tile
+    // holds at most n_here valid pairs; the checks only matter for a
+    // corrupted plan record.
+    constexpr int kPer = kTile / NT;
+    constexpr int kSearchSteps = 12;
     const int nt = min(S.roff[n_inst], n_here);
     const int32_t tile0 = span.tile0;
-    for (int j = threadIdx.x; j < nt; j += NT) {
-      const uint32_t sp = S.sp[j];
-      const int r = static_cast<int>(sp >> 16), n = static_cast<int>(sp & 0xFFFFu);
-      const int32_t row = S.ibase[r] + S.ro0[r] + (j - S.roff[r]);
-      if (r < n_inst && row >= 0 && row < N && n < n_here) {
-        inv[lb + row] = tile0 + n;
-        w_perm[lb + row] = S.wt[n];
+    int lo[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) lo[u] = 0;
+#pragma unroll
+    for (int st = kSearchSteps - 1; st >= 0; --st) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int j = u * NT + static_cast<int>(threadIdx.x);
+        const int mid = lo[u] + (1 << st);
+        if (mid < n_inst && S.roff[mid] <= j) lo[u] = mid;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = u * NT + static_cast<int>(threadIdx.x);
+      if (j < nt) {
+        const int n = S.sn[j];
+        const int32_t row = j - S.ro0[lo[u]];
+        if (n < n_here && row >= 0 && row < N) {
+          inv[lb + row] = tile0 + n;
+          w_perm[lb + row] = S.wst[j];
+        }
       }
     }
   }
