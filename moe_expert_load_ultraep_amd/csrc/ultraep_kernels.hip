@@ -1872,6 +1872,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 // fixed.  blockIdx.x strides over the elements.
 constexpr int kFoldThreads = 256;
 constexpr int kFoldMaxReps = 64;
+constexpr int kFoldVecs = 4;  // 16-byte vectors in flight per lane and stream
 
 __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
     const int32_t* __restrict__ slot_expert, const int32_t* __restrict__ inst_ptr,
@@ -1908,20 +1909,42 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
   const bool vec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(m) & 15) == 0) &&
                    ((reinterpret_cast<uintptr_t>(reps) & 15) == 0);
   if (vec) {
+    // each thread takes kFoldVecs 16-byte vectors a block-width apart, and
+    // every load of a replica round is issued before any add or store (the
+    // masters and the replica gradients are distinct buffers)
     const int64_t n4 = numel / 4;
     f32x4* m4 = reinterpret_cast<f32x4*>(m);
     const f32x4* r4 = reinterpret_cast<const f32x4*>(reps);
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x; i < n4;
-         i += tstride) {
-      f32x4 acc = m4[i];
-      for (int q = 0; q < n; ++q) {
-        const f32x4 g = __builtin_nontemporal_load(r4 + static_cast<int64_t>(s_list[q]) * n4 + i);
-        acc.x += g.x;
-        acc.y += g.y;
-        acc.z += g.z;
-        acc.w += g.w;
+    const int64_t span = static_cast<int64_t>(kFoldVecs) * kFoldThreads;
+    for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x; i0 < n4;
+         i0 += static_cast<int64_t>(gridDim.x) * span) {
+      f32x4 acc[kFoldVecs];
+#pragma unroll
+      for (int u = 0; u < kFoldVecs; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
+        acc[u] = i < n4 ? __builtin_nontemporal_load(m4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      m4[i] = acc;
+      for (int q = 0; q < n; ++q) {
+        const f32x4* rq = r4 + static_cast<int64_t>(s_list[q]) * n4;
+        f32x4 g[kFoldVecs];
+#pragma unroll
+        for (int u = 0; u < kFoldVecs; ++u) {
+          const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
+          g[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kFoldVecs; ++u) {
+          acc[u].x += g[u].x;
+          acc[u].y += g[u].y;
+          acc[u].z += g[u].z;
+          acc[u].w += g[u].w;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kFoldVecs; ++u) {
+        const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
+        if (i < n4) __builtin_nontemporal_store(acc[u], m4 + i);
+      }
     }
   } else {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kFoldThreads + threadIdx.x; i < numel;
@@ -2178,7 +2201,7 @@ hipError_t launch_fold(const Shape& sh, const int32_t* plan, float* const* maste
                        hipStream_t st) {
   const int32_t nslots = slot_end - slot_begin;
   if (nslots <= 0 || numel <= 0) return hipSuccess;
-  const int64_t per_block = static_cast<int64_t>(kFoldThreads) * 4 * 4;
+  const int64_t per_block = static_cast<int64_t>(kFoldThreads) * 4 * kFoldVecs;
   const int64_t want = (numel + per_block - 1) / per_block;
   const uint32_t bx = static_cast<uint32_t>(want < 2048 ? want : 2048);
   hipLaunchKernelGGL(fold_kernel, dim3(bx, static_cast<uint32_t>(nslots)), dim3(kFoldThreads), 0, st,
