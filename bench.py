@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = single layer, the headline)")
-    ap.add_argument("--cold-reps", type=int, default=20, help="repetitions of each cold / warm timing")
+    ap.add_argument("--cold-reps", type=int, default=100, help="repetitions of each cold / warm timing")
     ap.add_argument("--instances", type=int, default=0,
                     help="workload 4: instances used (0 = all 32 x 16)")
     ap.add_argument("--workers", type=int, default=16, help="host processes generating inputs")

@@ -127,6 +127,57 @@ __device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
   __syncthreads();
 }
 
+// Exclusive scans of two independent arrays with the barriers shared
+// (a[na] and b[nb] receive the totals); tmp holds 2 * (NT / 64 + 1) words.
+template <int NT>
+__device__ void block_exclusive_scan2(int32_t* a, int na, int32_t* b, int nb, int32_t* tmp) {
+  constexpr int W = NT / 64;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int pa = (na + NT - 1) / NT, pb = (nb + NT - 1) / NT;
+  const int ba = min(tid * pa, na), ea = min(ba + pa, na);
+  const int bb = min(tid * pb, nb), eb = min(bb + pb, nb);
+  int32_t sa = 0, sb = 0;
+  for (int i = ba; i < ea; ++i) sa += a[i];
+  for (int i = bb; i < eb; ++i) sb += b[i];
+  const int32_t ia = wave_inclusive_scan(sa), ib = wave_inclusive_scan(sb);
+  if (lane == 63) {
+    tmp[wave] = ia;
+    tmp[W + 1 + wave] = ib;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const int32_t t = lane < W ? tmp[lane] : 0;
+    const int32_t u = lane < W ? tmp[W + 1 + lane] : 0;
+    const int32_t ti = wave_inclusive_scan(t), ui = wave_inclusive_scan(u);
+    if (lane < W) {
+      tmp[lane] = ti - t;
+      tmp[W + 1 + lane] = ui - u;
+    }
+    if (lane == W - 1) {
+      tmp[W] = ti;
+      tmp[2 * W + 1] = ui;
+    }
+  }
+  __syncthreads();
+  int32_t ra = tmp[wave] + ia - sa;
+  for (int i = ba; i < ea; ++i) {
+    const int32_t v = a[i];
+    a[i] = ra;
+    ra += v;
+  }
+  int32_t rb = tmp[W + 1 + wave] + ib - sb;
+  for (int i = bb; i < eb; ++i) {
+    const int32_t v = b[i];
+    b[i] = rb;
+    rb += v;
+  }
+  if (tid == 0) {
+    a[na] = tmp[W];
+    b[nb] = tmp[2 * W + 1];
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------------
 // count: per-tile expert histogram ([README] intro: exact post-gating load)
 // ------------------------------------------------------------------------
@@ -195,6 +246,7 @@ struct PlanLds {
   int32_t* pload;  // [P+1]
   int32_t* slotE;  // [R*S]
   int32_t* slotQ;  // [R*S]
+  int32_t* instp;  // [E+R*S] physical expert of each instance entry
 };
 
 // The scan workgroups use only the first kPlanThreads words of the same
@@ -202,7 +254,8 @@ struct PlanLds {
 __host__ __device__ inline size_t plan_lds_words(int E, int R, int S, int D, int P, int ndom,
                                                  int items) {
   return static_cast<size_t>(E) + R + kPlanThreads + ndom + kScalars + items +
-         2ull * items * D * S + E + 2ull * E + (E + 1) + (P + 1) + 2ull * R * S;
+         2ull * items * D * S + E + 2ull * E + (E + 1) + (P + 1) + 2ull * R * S +
+         (static_cast<size_t>(E) + static_cast<size_t>(R) * S);
 }
 
 __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
@@ -222,7 +275,8 @@ __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
   L.iptr = p; p += a.E + 1;
   L.pload = p; p += a.P + 1;
   L.slotE = p; p += a.R * a.S;
-  L.slotQ = p;
+  L.slotQ = p; p += a.R * a.S;
+  L.instp = p;
   return L;
 }
 
@@ -806,63 +860,55 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     rec[a.off[ULTRAEP_PLAN_RANK_BEFORE] + r] = L.H[r];
   }
   __syncthreads();
-  block_exclusive_scan<kPlanThreads>(L.pload, P, L.part);  // pload -> phys_off
-  block_exclusive_scan<kPlanThreads>(L.iptr, E, L.part);   // instance counts -> inst_ptr
+  // pload -> phys_off, instance counts -> inst_ptr
+  block_exclusive_scan2<kPlanThreads>(L.pload, P, L.iptr, E, L.part);
 
   // instances of e in ascending physical id = ascending rank inside e's
-  // domain: walk the set bits of e's rank mask (its replicas and its home)
+  // domain.  One thread per master or filled slot places its instance: the
+  // index is e's first index + e's instances on lower ranks (the set bits of
+  // e's rank mask below its own); its local take is min(quota, pairs of e
+  // from its rank's tiles).  Then one thread per expert accumulates the
+  // quota ends and first rows over e's instances.
   int32_t* inst_phys = rec + a.off[ULTRAEP_PLAN_INST_PHYS];
   int32_t* inst_end = rec + a.off[ULTRAEP_PLAN_INST_END];
   int32_t* inst_base = rec + a.off[ULTRAEP_PLAN_INST_BASE];
   int32_t* inst_local = rec + a.off[ULTRAEP_PLAN_INST_LOCAL];
-  for (int e = tid; e < E; e += kPlanThreads) {
-    const int home = e / M, d = home / D;
-    const uint64_t in_domain = D == 64 ? ~0ull : ((1ull << D) - 1);
-    uint64_t m = (L.rmask[e] | (1ull << (home % D))) & in_domain;
-    int i = L.iptr[e];
-    int32_t end = 0;
-    while (m) {
-      const int r = d * D + __builtin_ctzll(m);
-      m &= m - 1;
-      int p = home * (M + S) + e % M;
-      int32_t q = L.mq[e];
-      if (r != home) {
-        for (int j = 0; j < S; ++j)
-          if (L.slotE[r * S + j] == e) {
-            p = r * (M + S) + M + j;
-            q = L.slotQ[r * S + j];
-          }
-      }
-      end += q;
-      inst_phys[i] = p;
-      inst_end[i] = end;
-      inst_base[i] = L.pload[p] - (end - q);
-      ++i;
-    }
-  }
-  // local take of each instance, min(quota, pairs of e from its rank's
-  // tiles), one thread per master or slot: the instance's index is e's
-  // first index + the ranks of e's instances below its own
   for (int x = tid; x < E + R * S; x += kPlanThreads) {
-    int e, r;
+    int e, r, p;
     int32_t q;
     if (x < E) {
       e = x;
       r = e / M;
+      p = r * (M + S) + e % M;
       q = L.mq[e];
     } else {
       e = L.slotE[x - E];
       if (e < 0) continue;
       r = (x - E) / S;
+      p = r * (M + S) + M + (x - E) % S;
       q = L.slotQ[x - E];
     }
     const int home = e / M;
     const uint64_t in_domain = D == 64 ? ~0ull : ((1ull << D) - 1);
     const uint64_t m = (L.rmask[e] | (1ull << (home % D))) & in_domain;
     const int i = L.iptr[e] + __builtin_popcountll(m & ((1ull << (r % D)) - 1));
+    L.instp[i] = p;
+    inst_phys[i] = p;
     int32_t own = 0;
     for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * E + e];
     inst_local[i] = min(q, own);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int32_t end = 0;
+    for (int i = L.iptr[e]; i < L.iptr[e + 1]; ++i) {
+      const int p = L.instp[i];
+      const int j = p % (M + S);
+      const int32_t q = j < M ? L.mq[e] : L.slotQ[(p / (M + S)) * S + (j - M)];
+      end += q;
+      inst_end[i] = end;
+      inst_base[i] = L.pload[p] - (end - q);
+    }
   }
   // unused instance entries and the padding between fields get fixed values,
   // so a record is a pure function of its inputs
