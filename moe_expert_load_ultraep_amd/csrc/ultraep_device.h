@@ -49,10 +49,11 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 // maxima are combined by DPP row broadcasts (lane 15 into rows 1 and 3, then
 // lane 31 into rows 2 and 3) instead of four read-lanes and scalar maxima,
 // which shortens the dependent chain.  Every lane must be active.
+// Rows outside ROWS read 0, the identity of an unsigned max, which lets the
+// compiler fold the move into the max as one DPP instruction.
 template <int CTRL, int ROWS>
 __device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v),
-                                                           CTRL, ROWS, 0xF, false));
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, ROWS, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t wave_max_bcast(uint32_t x) {
