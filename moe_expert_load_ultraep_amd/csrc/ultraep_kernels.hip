@@ -186,11 +186,16 @@ __device__ void block_exclusive_scan2(int32_t* a, int na, int32_t* b, int nb, in
 // valid id to an LDS counter.  The order of the additions does not matter
 // here, so a plain LDS atomic per pair is the cheapest form: equal ids in one
 // wave instruction only serialise inside the LDS, they cost no VALU work.
+// A tile holds at most kTile pairs, so its counts are stored as 16-bit
+// values, rows of hist_stride(E) entries: the planner reads every row, and
+// half the bytes is half its wait.
 using CountTile = TileShape<16>;
+
+__host__ __device__ inline int32_t hist_stride(int32_t E) { return (E + 1) & ~1; }
 
 __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
     const int32_t* __restrict__ idx, int32_t N, int32_t TK, int32_t tpr, int32_t E, int32_t ntiles,
-    int32_t* __restrict__ hist) {
+    uint16_t* __restrict__ hist) {
   using T = CountTile;
   extern __shared__ __align__(16) int32_t s_cnt[];
   const int64_t blk = blockIdx.x;
@@ -207,8 +212,9 @@ __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
   for (int c = 0; c < T::kChunks; ++c)
     if (v[c] < static_cast<uint32_t>(E)) atomicAdd(&s_cnt[v[c]], 1);
   __syncthreads();
-  int32_t* dst = hist + (static_cast<int64_t>(layer) * ntiles + tile) * E;
-  for (int i = threadIdx.x; i < E; i += T::kThreads) dst[i] = s_cnt[i];
+  uint16_t* dst = hist + (static_cast<int64_t>(layer) * ntiles + tile) * hist_stride(E);
+  for (int i = threadIdx.x; i < hist_stride(E); i += T::kThreads)
+    dst[i] = static_cast<uint16_t>(i < E ? s_cnt[i] : 0);
 }
 
 // ------------------------------------------------------------------------
@@ -626,8 +632,9 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
 // contiguous run of tiles of one expert, the runs are scanned in LDS, and the
 // run is re-read and written out as running prefixes.  Loads go in batches
 // of 16 with clamped indices so each batch is one round trip.
-__device__ void tile_base_scan(const int32_t* __restrict__ hist, int32_t* __restrict__ base,
+__device__ void tile_base_scan(const uint16_t* __restrict__ hist, int32_t* __restrict__ base,
                                int32_t ntiles, int32_t E, int32_t e0, int32_t ew, int32_t* part) {
+  const int32_t hs = hist_stride(E);
   constexpr int B = 16;
   const int tid = threadIdx.x;
   const int nch = kPlanThreads / ew;
@@ -641,7 +648,7 @@ __device__ void tile_base_scan(const int32_t* __restrict__ hist, int32_t* __rest
     for (int tb = t0; tb < t1; tb += B) {
       int32_t x[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * E + e];
+      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * hs + e];
 #pragma unroll
       for (int u = 0; u < B; ++u)
         if (tb + u < t1) sum += x[u];
@@ -655,7 +662,7 @@ __device__ void tile_base_scan(const int32_t* __restrict__ hist, int32_t* __rest
     for (int tb = t0; tb < t1; tb += B) {
       int32_t x[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * E + e];
+      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * hs + e];
 #pragma unroll
       for (int u = 0; u < B; ++u)
         if (tb + u < t1) {
@@ -670,7 +677,7 @@ __device__ void tile_base_scan(const int32_t* __restrict__ hist, int32_t* __rest
 // the plan; the other scan_wgs workgroups build the tile ordinal bases the
 // reroute kernel needs, on other CUs, while the plan is being solved.
 template <int MMAX, int SMAX>
-__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ hist,
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __restrict__ hist,
                                                             int32_t* __restrict__ tile_base,
                                                             int32_t* __restrict__ plans,
                                                             PlanParams a) {
@@ -679,7 +686,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   const int layer = blockIdx.x / group;
   const int role = blockIdx.x % group;
   const int E = a.E, R = a.R, S = a.S, D = a.D, M = a.M, P = a.P;
-  const int32_t* H = hist + static_cast<int64_t>(layer) * a.ntiles * E;
+  const int32_t hs = hist_stride(E);
+  const uint16_t* H = hist + static_cast<int64_t>(layer) * a.ntiles * hs;
   if (role > 0) {
     const int e0 = (role - 1) * a.scan_ew;
     tile_base_scan(H, tile_base + static_cast<int64_t>(layer) * a.ntiles * E, a.ntiles, E, e0,
@@ -697,30 +705,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   for (int d = tid; d < a.ndom; d += kPlanThreads) L.dom[d] = 0;
 
   // -- phase 0: pairs per expert = sum of the tile histograms.  Thread
-  // (e, ch) takes tiles ch, ch + nch, ... so each batch of loads reads whole
-  // histogram rows; batches of 32 loads are issued before any is used.
+  // (ep, ch) reads experts 2ep and 2ep + 1 of tiles ch, ch + nch, ... as one
+  // 32-bit word, so each batch of loads reads whole histogram rows; batches
+  // of 32 loads are issued before any is used.  The chunk sums meet in LDS.
   {
     constexpr int B = 32;
-    const int nch = kPlanThreads / E;
-    const int e = tid % E, ch = tid / E;
-    int32_t sum = 0;
+    const int npair = hs / 2;
+    const int nch = kPlanThreads / npair;
+    const int ep = tid % npair, ch = tid / npair;
+    const uint32_t* H2 = reinterpret_cast<const uint32_t*>(H);
+    for (int e = tid; e < E; e += kPlanThreads) L.c[e] = 0;
+    __syncthreads();
+    int32_t lo = 0, hi = 0;
     if (ch < nch && a.ntiles > 0) {
       for (int tb = ch; tb < a.ntiles; tb += B * nch) {
-        int32_t x[B];
+        uint32_t x[B];
 #pragma unroll
         for (int u = 0; u < B; ++u)
-          x[u] = H[static_cast<int64_t>(min(tb + u * nch, a.ntiles - 1)) * E + e];
+          x[u] = H2[static_cast<int64_t>(min(tb + u * nch, a.ntiles - 1)) * npair + ep];
 #pragma unroll
         for (int u = 0; u < B; ++u)
-          if (tb + u * nch < a.ntiles) sum += x[u];
+          if (tb + u * nch < a.ntiles) {
+            lo += static_cast<int32_t>(x[u] & 0xFFFFu);
+            hi += static_cast<int32_t>(x[u] >> 16);
+          }
       }
-    }
-    L.part[tid] = sum;
-    __syncthreads();
-    if (ch == 0) {
-      int32_t c = 0;
-      for (int q = 0; q < nch; ++q) c += L.part[q * E + e];
-      L.c[e] = c;
+      if (lo) atomicAdd(&L.c[2 * ep], lo);
+      if (hi && 2 * ep + 1 < E) atomicAdd(&L.c[2 * ep + 1], hi);
     }
     __syncthreads();
   }
@@ -895,7 +906,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     L.instp[i] = p;
     inst_phys[i] = p;
     int32_t own = 0;
-    for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * E + e];
+    for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * hs + e];
     inst_local[i] = min(q, own);
   }
   __syncthreads();
@@ -2003,7 +2014,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
 }
 
 template <int MMAX, int SMAX>
-hipError_t launch_plan_t(const PlanParams& pp, int32_t L, size_t lds, const int32_t* hist,
+hipError_t launch_plan_t(const PlanParams& pp, int32_t L, size_t lds, const uint16_t* hist,
                          int32_t* tbase, int32_t* plans, hipStream_t st) {
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&plan_kernel<MMAX, SMAX>),
@@ -2017,7 +2028,7 @@ hipError_t launch_plan_t(const PlanParams& pp, int32_t L, size_t lds, const int3
 }
 
 template <int SMAX>
-hipError_t launch_plan_m(int M, const PlanParams& pp, int32_t L, size_t lds, const int32_t* hist,
+hipError_t launch_plan_m(int M, const PlanParams& pp, int32_t L, size_t lds, const uint16_t* hist,
                          int32_t* tbase, int32_t* plans, hipStream_t st) {
   if (M <= 2) return launch_plan_t<2, SMAX>(pp, L, lds, hist, tbase, plans, st);
   if (M <= 4) return launch_plan_t<4, SMAX>(pp, L, lds, hist, tbase, plans, st);
@@ -2158,7 +2169,8 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   const int32_t ntiles = static_cast<int32_t>(ntiles_of(sh.R, TK));
   const Tiling tl{N, TK, static_cast<int32_t>(tiles_per_rank(TK)), ntiles};
   const int64_t blocks = static_cast<int64_t>(L) * ntiles;
-  int32_t* hist = ws;
+  // the 16-bit histograms take the first half of the histogram region
+  uint16_t* hist = reinterpret_cast<uint16_t*>(ws);
   int32_t* tbase = ws + static_cast<int64_t>(L) * ntiles * sh.E;
   if (blocks > 0) {
     hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(CountTile::kThreads),
