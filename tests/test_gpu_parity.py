@@ -349,8 +349,10 @@ def test_locality_reroute_workloads(mode, cfg, T, fused):
     (12, 4, 2, 2, 333, 3, 0.05, False),   # ragged tiles, dropped ids, two domains
     (16, 4, 0, 4, 500, 2, 0.0, False),    # no slots: every instance is a master
     (32, 8, 3, 4, 2049, 4, 0.01, True),   # zero-quota masters allowed
-    (1024, 64, 8, 64, 256, 16, 0.0, False),  # M = 16, S = 8
+    (1024, 64, 8, 64, 256, 16, 0.0, False),  # M = 16, S = 8 (layout by a separate scatter)
     (64, 64, 1, 64, 20000, 1, 0.0, False),   # several tiles per rank (T*k > 8192)
+    (512, 64, 4, 64, 512, 8, 0.0, False),    # fused layout in 8-wave workgroups
+    (1024, 64, 1, 64, 256, 8, 0.01, False),  # fused layout in 4-wave workgroups
 ])
 def test_locality_reroute_edge_shapes(mode, E, R, S, D, T, k, invalid, allow_zero):
     say(f"locality edge mode={mode} E={E} R={R} S={S} D={D} T={T} k={k}")
