@@ -988,7 +988,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
 // then written out with consecutive lanes on consecutive rows, instead of
 // one 4-byte scatter per pair.  The staged weights reuse the words of the
 // grouping masks and the indices are 16-bit, which keeps the tables (about
-// 64 KiB at E = 128) small enough for two 16-wave workgroups per CU.
+// 63 KiB at E = 128, 75 KiB at E = 256) small enough for two 16-wave
+// workgroups per CU.
 struct RerouteLds {
   unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids (pass 1)
   int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
@@ -1260,8 +1261,11 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
 // start, in round-robin order, so a pair needs one division and one entry),
 // and per run the offset from layout row to staging slot.  A pair whose pool
 // index lies past that phase (the tile straddles a change in the number of
-// instances still taking pairs) takes the general search.  The tables stay
-// small enough (about 59 KiB at E = 128) for two 16-wave workgroups per CU.
+// instances still taking pairs) finds its phase among the later ones the
+// tile reaches, whose headers and instance lists come from a small per-tile
+// pool; only if that pool is full does it take the general search.  The
+// tables stay small enough at E = 128 (about 73 KiB, 76 KiB with the
+// interleave's phase pool) for two 16-wave workgroups per CU.
 struct LocalLds {
   unsigned long long* peers;  // [waves][E+1] lane masks (pass 1)
   uint32_t* park;  // [kTile] the packed pair values between the passes
