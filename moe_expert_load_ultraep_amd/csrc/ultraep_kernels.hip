@@ -1273,6 +1273,8 @@ struct LocalLds {
   float* wst;      // [kTile] LAYOUT: the staged slots' routing weights (pass 2;
                    // shares its words with peers and park)
   uint16_t* sn;    // [kTile] LAYOUT: the staged slots' pair indices in the tile
+                   // (with the weights gathered instead of staged, sn takes
+                   // the words of wst)
   int32_t* cntw;   // [waves][E] per-wave counters, then per-wave bases of t
   int32_t* er;     // [E][8] per expert: set-up words (kEr*), then the record of pass 2
   int32_t* al;     // INTERLEAVE: [n_inst][2] the phase's instances (its words are ipool and ie)
@@ -1302,8 +1304,8 @@ struct LocalLds {
 // an expert reach past the first phase only where the number of instances
 // still taking pairs changes inside the tile, which few (tile, expert) pairs
 // do.  Without room a pair takes the general search.
-constexpr int kPhaseHeaders = 64;
-constexpr int kPhaseEntries = 256;
+constexpr int kPhaseHeaders = 32;
+constexpr int kPhaseEntries = 160;
 
 // Set-up words of an expert's record: the tile's ordinal base of e, then
 // its pairs in the tile; pairs of e from ranks before r; pool pairs of e
@@ -1313,14 +1315,16 @@ constexpr int kErCount = 0, kErBlk = 1, kErPool = 2, kErLoc = 3;
 
 __host__ __device__ inline int local_n4(int n_inst) { return (n_inst + 3) & ~3; }
 
+// gather: the write-out reads the weights from w instead of LDS, which
+// frees the words of the staged weights for the pair indices.
 __host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout, bool interleave,
-                                                  int waves) {
+                                                  int waves, bool gather = false) {
   const size_t n4 = static_cast<size_t>(local_n4(n_inst));
   // the shared region also parks the packed pair values between the passes
   size_t words = reroute_shared_words(E, true, waves) + static_cast<size_t>(waves) * E +
                  static_cast<size_t>(kErWords) * E + 9 * n4 + (E + 1);
   if (interleave) words += 4 * kPhaseHeaders + 2 * kPhaseEntries + 4;
-  if (layout) words += kTile / 2 + 2ull * (n_inst + E) + 1 + (waves + 1);
+  if (layout) words += (gather ? 0 : kTile / 2) + 2ull * (n_inst + E) + 1 + (waves + 1);
   return 4 * words;
 }
 
@@ -1345,7 +1349,7 @@ __device__ inline void interleave_round(const LocalLds& S_, int i0, int i1, int 
 
 // Two 16-wave workgroups per CU need at most 64 VGPRs per lane (8 waves per
 // SIMD).
-template <bool INTERLEAVE, bool LAYOUT, int W>
+template <bool INTERLEAVE, bool LAYOUT, int W, bool GATHER = false>
 __global__ __launch_bounds__(TileShape<W>::kThreads)
 __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ w, int32_t N, int32_t TK,
@@ -1354,6 +1358,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
     int32_t off_iptr, int32_t off_iend, int32_t off_iphys, int32_t off_ibase, int32_t off_ilocal,
     int32_t n_inst, int32_t* __restrict__ phys_idx, int32_t* __restrict__ pos,
     int32_t* __restrict__ inv, float* __restrict__ w_perm) {
+  constexpr bool gather_w = GATHER;
   using T = TileShape<W>;
   constexpr int NT = T::kThreads;
   extern __shared__ __align__(16) int32_t lds[];
@@ -1366,8 +1371,9 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
     S_.peers = reinterpret_cast<unsigned long long*>(q);
     S_.park = reinterpret_cast<uint32_t*>(q);
     S_.wst = reinterpret_cast<float*>(q);
+    S_.sn = reinterpret_cast<uint16_t*>(q);
     q += reroute_shared_words(E, true, W);
-    if (LAYOUT) {
+    if (LAYOUT && !gather_w) {
       S_.sn = reinterpret_cast<uint16_t*>(q);
       q += kTile / 2;
     }
@@ -1664,7 +1670,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
   // each pair's routing weight, one coalesced load per chunk, issued here
   // so that they are in flight behind the LDS work of pass 2
   float wl[LAYOUT ? T::kChunks : 1];
-  if (LAYOUT) {
+  if (LAYOUT && !gather_w) {
 #pragma unroll
     for (int c = 0; c < T::kChunks; ++c)
       wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
@@ -1733,7 +1739,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
         const int32_t sl = row + S_.ro0[run];
         if (sl >= 0 && sl < kTile) {
           S_.sn[sl] = static_cast<uint16_t>(i);
-          S_.wst[sl] = wl[c];
+          if (!gather_w) S_.wst[sl] = wl[c];
         }
       }
       __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
@@ -1802,7 +1808,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
           const int32_t sl = row + S_.ro0[run];
           if (sl >= 0 && sl < kTile) {
             S_.sn[sl] = static_cast<uint16_t>(i);
-            S_.wst[sl] = wl[c];
+            if (!gather_w) S_.wst[sl] = wl[c];
           }
         }
         __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
@@ -1844,7 +1850,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
         const int32_t row = j - S_.ro0[lo[u]];
         if (n < n_here && row >= 0 && row < N) {
           inv[lb + row] = tile0 + n;
-          w_perm[lb + row] = S_.wst[j];
+          w_perm[lb + row] = gather_w ? w[first + n] : S_.wst[j];
         }
       }
     }
@@ -2106,19 +2112,30 @@ int local_waves(const Shape& sh, bool layout) {
   return 0;
 }
 
-template <bool INTERLEAVE, bool LAYOUT, int W>
+// Two 16-wave workgroups share a CU when each needs at most this much LDS
+// (measured: 77.4 KiB does, 78.6 KiB does not).
+constexpr size_t kTwoPerCu = 78 * 1024;
+
+// Gather the weights in the write-out only where that is what lets two
+// workgroups share a CU; staged weights are cheaper otherwise.
+bool local_gather(const Shape& sh, bool interleave) {
+  return local_lds_bytes(sh.E, sh.n_inst, true, interleave, 16, false) > kTwoPerCu &&
+         local_lds_bytes(sh.E, sh.n_inst, true, interleave, 16, true) <= kTwoPerCu;
+}
+
+template <bool INTERLEAVE, bool LAYOUT, int W, bool GATHER = false>
 hipError_t launch_reroute_local_w(const Shape& sh, int64_t blocks, const int32_t* idx, const float* w,
                                   const Tiling& tl, const int32_t* tbase, const int32_t* plans,
                                   int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
                                   hipStream_t st) {
-  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, LAYOUT, INTERLEAVE, W);
-  const void* fn = reinterpret_cast<const void*>(&reroute_local_kernel<INTERLEAVE, LAYOUT, W>);
+  const size_t rl = local_lds_bytes(sh.E, sh.n_inst, LAYOUT, INTERLEAVE, W, GATHER);
+  const void* fn = reinterpret_cast<const void*>(&reroute_local_kernel<INTERLEAVE, LAYOUT, W, GATHER>);
   if (rl > 65536) {
     const hipError_t e =
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(rl));
     if (e != hipSuccess) return e;
   }
-  reroute_local_kernel<INTERLEAVE, LAYOUT, W>
+  reroute_local_kernel<INTERLEAVE, LAYOUT, W, GATHER>
       <<<dim3(static_cast<uint32_t>(blocks)), dim3(TileShape<W>::kThreads), rl, st>>>(
           idx, w, tl.N, tl.TK, tl.tpr, sh.E, sh.M, sh.S, tl.ntiles, tbase, plans, sh.lay.words,
           sh.lay.off[ULTRAEP_PLAN_INST_PTR], sh.lay.off[ULTRAEP_PLAN_INST_END],
@@ -2133,6 +2150,9 @@ hipError_t launch_reroute_local(const Shape& sh, int64_t blocks, const int32_t* 
                                 const Tiling& tl, const int32_t* tbase, const int32_t* plans,
                                 int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
                                 hipStream_t st) {
+  if (LAYOUT && local_gather(sh, INTERLEAVE))
+    return launch_reroute_local_w<INTERLEAVE, LAYOUT, 16, true>(sh, blocks, idx, w, tl, tbase, plans,
+                                                                phys_idx, pos, inv, w_perm, st);
   switch (local_waves(sh, LAYOUT)) {
     case 16:
       return launch_reroute_local_w<INTERLEAVE, LAYOUT, 16>(sh, blocks, idx, w, tl, tbase, plans,
