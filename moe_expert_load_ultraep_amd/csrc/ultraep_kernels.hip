@@ -178,6 +178,27 @@ __device__ void block_exclusive_scan2(int32_t* a, int na, int32_t* b, int nb, in
   __syncthreads();
 }
 
+// Exclusive scan of a[0, n) by the calling wave alone (a[n] receives the
+// total): each lane sums a contiguous run, the lanes scan their sums, and
+// each lane writes its run's prefixes.  For the short arrays of a tile's
+// runs one wave is enough, and the other waves skip the block scan's two
+// extra barriers.  The caller synchronises afterwards.
+__device__ void wave_exclusive_scan(int32_t* a, int n) {
+  const int lane = lane_id();
+  const int per = (n + 63) / 64;
+  const int b = min(lane * per, n), en = min(b + per, n);
+  int32_t s = 0;
+  for (int i = b; i < en; ++i) s += a[i];
+  const int32_t inc = wave_inclusive_scan(s);
+  int32_t run = inc - s;
+  for (int i = b; i < en; ++i) {
+    const int32_t v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  if (lane == 63) a[n] = inc;
+}
+
 // ------------------------------------------------------------------------
 // count: per-tile expert histogram ([README] intro: exact post-gating load)
 // ------------------------------------------------------------------------
@@ -1142,7 +1163,8 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
       S.ro0[i] = 0;
     }
     __syncthreads();
-    block_exclusive_scan<NT>(S.roff, n_inst, S.tmp);
+    if (wave == 0) wave_exclusive_scan(S.roff, n_inst);
+    __syncthreads();
     // ro0 becomes staging slot minus layout row of each run
     for (int i = threadIdx.x; i < n_inst; i += NT) S.ro0[i] = S.roff[i] - S.ibase[i] - S.ro0[i];
     __syncthreads();
@@ -1660,7 +1682,8 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
       S_.ro0[i] = 0;
     }
     __syncthreads();
-    block_exclusive_scan<NT>(S_.roff, n_inst + E, S_.tmp);
+    if (wave == 0) wave_exclusive_scan(S_.roff, n_inst + E);
+    __syncthreads();
     for (int r = threadIdx.x; r < n_inst + E; r += NT) S_.ro0[r] = S_.roff[r] - S_.ro0[r];
   }
   __syncthreads();
