@@ -66,6 +66,24 @@ __device__ __forceinline__ uint32_t wave_max_bcast(uint32_t x) {
   return readlane(x, 63);
 }
 
+// Three independent wave maxima, as wave_max_bcast, with each DPP stage
+// issued for all three values before the next stage: the stages of one
+// value depend on each other, so interleaving fills the DPP hazard slots
+// with the other values' work instead of wait states.
+__device__ __forceinline__ void wave_max3_bcast(uint32_t& a, uint32_t& b, uint32_t& c) {
+#define ULTRAEP_MAX3(F) a = max(a, F(a)); b = max(b, F(b)); c = max(c, F(c))
+  ULTRAEP_MAX3(dpp<0xB1>);
+  ULTRAEP_MAX3(dpp<0x4E>);
+  ULTRAEP_MAX3(dpp<0x141>);
+  ULTRAEP_MAX3(dpp<0x140>);
+  ULTRAEP_MAX3((dpp_rows<0x142, 0xA>));
+  ULTRAEP_MAX3((dpp_rows<0x143, 0xC>));
+#undef ULTRAEP_MAX3
+  a = readlane(a, 63);
+  b = readlane(b, 63);
+  c = readlane(c, 63);
+}
+
 __device__ __forceinline__ uint32_t wave_min(uint32_t x) {
   x = min(x, dpp<0xB1>(x));
   x = min(x, dpp<0x4E>(x));

@@ -539,16 +539,6 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     he[s] = -1;
     hq[s] = 0;
   }
-  auto place = [&](int who, int32_t e, int32_t x) {
-    const bool me = lane == who;
-#pragma unroll
-    for (int s = 0; s < SMAX; ++s) {
-      const bool here = me && s == nh;
-      he[s] = here ? e : he[s];
-      hq[s] = here ? x : hq[s];
-    }
-    nh += me ? 1 : 0;
-  };
 
   // the queue's pop key: the largest piece, ties to the lowest expert id
   auto queue_key = [&]() {
@@ -565,6 +555,14 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
   // left it; a chain grows the donor's piece (its key grows by the pairs
   // added, the tie bits stay) and may re-queue the rest of the popped piece
   // under its own tie bits; a fill re-queues the rest.
+  //
+  // The three outcomes share one update.  The receiver (lane kl) takes
+  // r_amt pairs: the whole piece on a fit, else its whole spare (0 when no
+  // rank has spare); the donor (lane dl, chains only) takes x more; the
+  // rest goes back to the owner's queue entry.  Receiver and donor are
+  // different ranks (a rank with spare queued nothing), so each lane places
+  // at most one instance per step, and the step has no branch but the exit
+  // and the rare failure.
   uint32_t km = wave_max_bcast(queue_key());
   const int max_steps = D * S + 1;
   for (int step = 0; step <= max_steps; ++step) {
@@ -579,71 +577,62 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
       }
       return true;
     }
-    const uint32_t t = TMASK - (km & TMASK);
+    const uint32_t own_tie = km & TMASK;
+    const uint32_t t = TMASK - own_tie;
     const int owner = static_cast<int>(t / MMAX), jsel = static_cast<int>(t % MMAX);
     const int32_t e = (d * D + owner) * M + jsel;
-    int32_t amt = static_cast<int32_t>(km >> TB);
-#pragma unroll
-    for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? 0 : pa[j];
+    const int32_t amt = static_cast<int32_t>(km >> TB);
+    const bool mine = lane == owner;
     bool hosts = false;
 #pragma unroll
     for (int s = 0; s < SMAX; ++s) hosts |= (he[s] == e);
-    const bool elig = lane != owner && nh < S && !hosts;
+    const bool elig = !mine && nh < S && !hosts;
     const uint32_t core = spare >= amt ? (kFitBit | (kFitBit - 1 - static_cast<uint32_t>(spare)))
                                        : static_cast<uint32_t>(spare);
     const uint32_t key = (elig && spare > 0) ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
-    uint32_t dk = 0;
+    uint32_t dk = 0, qk = 0;
 #pragma unroll
-    for (int j = 0; j < MMAX; ++j)
-      dk = max(dk, (elig && pa[j] > 0 && room[j] > 0)
-                       ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u);
-    const uint32_t kmax = wave_max_bcast(key);
-    const uint32_t dmax = wave_max_bcast(dk);
-    const uint32_t knext = wave_max_bcast(queue_key());
+    for (int j = 0; j < MMAX; ++j) {
+      // the popped piece is out of the queue for this step
+      const uint32_t kj = (pa[j] > 0 && !(mine && j == jsel))
+                              ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u;
+      qk = max(qk, kj);
+      dk = max(dk, (elig && room[j] > 0) ? kj : 0u);
+    }
+    uint32_t kmax = key, dmax = dk, knext = qk;
+    wave_max3_bcast(kmax, dmax, knext);
+    const bool fit = (kmax & (kFitBit << 6)) != 0;
+    if (!fit && kmax == 0 && dmax == 0) return false;
     const int kl = 63 - static_cast<int>(kmax & 63);
-    if (kmax & (kFitBit << 6)) {  // fit
-      spare -= lane == kl ? amt : 0;
-      place(kl, e, amt);
-      km = knext;
-      continue;
-    }
-    const uint32_t own_tie = km & TMASK;
-    km = knext;
-    const int32_t rmax = static_cast<int32_t>(kmax >> 6);  // roomiest spare (0: none)
-    if (dmax > 0) {  // chain through the donor's rank
-      const uint32_t dt = TMASK - (dmax & TMASK);
-      const int dl = static_cast<int>(dt / MMAX), djs = static_cast<int>(dt % MMAX);
-      if (rmax > 0) {
-        place(kl, e, rmax);
-        spare = lane == kl ? 0 : spare;
-        amt -= rmax;
-      }
-      int32_t myroom = 0;
+    const int32_t r_amt = fit ? amt : static_cast<int32_t>(kmax >> 6);
+    const uint32_t dt = TMASK - (dmax & TMASK);
+    const int dl = static_cast<int>(dt / MMAX) & 63, djs = static_cast<int>(dt % MMAX);
+    int32_t myroom = 0;
 #pragma unroll
-      for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
-      const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
-      const int32_t x = min(amt, droom);
-      place(dl, e, x);
+    for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
+    const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
+    const int32_t x = (!fit && dmax > 0) ? min(amt - r_amt, droom) : 0;
+    const int32_t left = amt - r_amt - x;
+    const bool rcv = lane == kl, don = lane == dl;
+    const int32_t give = (rcv ? r_amt : 0) + (don ? x : 0);
+    const bool put = give > 0;
 #pragma unroll
-      for (int j = 0; j < MMAX; ++j) {
-        const bool here = lane == dl && j == djs;
-        pa[j] += here ? x : 0;
-        room[j] -= here ? x : 0;
-      }
-      km = max(km, dmax + (static_cast<uint32_t>(x) << TB));
-      amt -= x;
-    } else if (rmax > 0) {  // fill the roomiest receiver
-      place(kl, e, rmax);
-      spare = lane == kl ? 0 : spare;
-      amt -= rmax;
-    } else {
-      return false;
+    for (int s = 0; s < SMAX; ++s) {
+      const bool here = put && s == nh;
+      he[s] = here ? e : he[s];
+      hq[s] = here ? give : hq[s];
     }
-    if (amt > 0) {
+    nh += put ? 1 : 0;
+    spare -= rcv ? r_amt : 0;
 #pragma unroll
-      for (int j = 0; j < MMAX; ++j) pa[j] = (lane == owner && j == jsel) ? amt : pa[j];
-      km = max(km, (static_cast<uint32_t>(amt) << TB) | own_tie);
+    for (int j = 0; j < MMAX; ++j) {
+      const int32_t add = (don && j == djs) ? x : 0;
+      pa[j] = (mine && j == jsel) ? left : pa[j] + add;
+      room[j] -= add;
     }
+    // a fit leaves dmax at most knext (the donor's piece is still queued)
+    km = max(knext, dmax + (static_cast<uint32_t>(x) << TB));
+    km = max(km, left > 0 ? (static_cast<uint32_t>(left) << TB) | own_tie : 0u);
   }
   return false;
 }
