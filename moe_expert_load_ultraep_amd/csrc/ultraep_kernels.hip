@@ -683,6 +683,52 @@ __device__ void tile_base_scan(const uint16_t* __restrict__ hist, int32_t* __res
   }
 }
 
+// Pairs per expert of one layer: c[e] += the sum of column e over the tile
+// histogram rows.  Thread (q, ch) reads W 32-bit words (2W experts) of rows
+// ch, ch + nch, ..., so each batch of loads reads whole rows; a batch of B
+// loads is issued before any is used.  W = 4 (16-byte loads, half the
+// batches of W = 1) needs rows of a multiple of 8 entries on a 16-byte
+// aligned base.  The chunk sums meet in LDS.
+template <int W>
+__device__ void sum_hist_rows(const uint16_t* __restrict__ H, int hs, int ntiles, int E, int32_t* c) {
+  constexpr int B = W == 4 ? 16 : 32;
+  const int tid = threadIdx.x;
+  const int nq = hs / (2 * W);
+  const int nch = kPlanThreads / nq;
+  const int q = tid % nq, ch = tid / nq;
+  if (ch >= nch || ntiles <= 0) return;
+  int32_t sum[2 * W];
+#pragma unroll
+  for (int i = 0; i < 2 * W; ++i) sum[i] = 0;
+  for (int tb = ch; tb < ntiles; tb += B * nch) {
+    uint32_t x[B][W];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int64_t row = min(tb + u * nch, ntiles - 1);
+      if constexpr (W == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(H + row * hs + 8 * q);
+        x[u][0] = v.x; x[u][1] = v.y; x[u][2] = v.z; x[u][3] = v.w;
+      } else {
+        x[u][0] = reinterpret_cast<const uint32_t*>(H)[row * (hs / 2) + q];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u)
+      if (tb + u * nch < ntiles) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          sum[2 * w] += static_cast<int32_t>(x[u][w] & 0xFFFFu);
+          sum[2 * w + 1] += static_cast<int32_t>(x[u][w] >> 16);
+        }
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 2 * W; ++i) {
+    const int e = 2 * W * q + i;
+    if (sum[i] && e < E) atomicAdd(&c[e], sum[i]);
+  }
+}
+
 // One launch per batch of layers: workgroup 0 of each layer's group solves
 // the plan; the other scan_wgs workgroups build the tile ordinal bases the
 // reroute kernel needs, on other CUs, while the plan is being solved.
@@ -714,62 +760,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
   if (tid < kScalars) L.scal[tid] = 0;
   for (int d = tid; d < a.ndom; d += kPlanThreads) L.dom[d] = 0;
 
-  // -- phase 0: pairs per expert = sum of the tile histograms.  Thread
-  // (ep, ch) reads experts 2ep and 2ep + 1 of tiles ch, ch + nch, ... as one
-  // 32-bit word, so each batch of loads reads whole histogram rows; batches
-  // of 32 loads are issued before any is used.  The chunk sums meet in LDS.
-  {
-    constexpr int B = 32;
-    const int npair = hs / 2;
-    const int nch = kPlanThreads / npair;
-    const int ep = tid % npair, ch = tid / npair;
-    const uint32_t* H2 = reinterpret_cast<const uint32_t*>(H);
-    for (int e = tid; e < E; e += kPlanThreads) L.c[e] = 0;
-    __syncthreads();
-    int32_t lo = 0, hi = 0;
-    if (ch < nch && a.ntiles > 0) {
-      for (int tb = ch; tb < a.ntiles; tb += B * nch) {
-        uint32_t x[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u)
-          x[u] = H2[static_cast<int64_t>(min(tb + u * nch, a.ntiles - 1)) * npair + ep];
-#pragma unroll
-        for (int u = 0; u < B; ++u)
-          if (tb + u * nch < a.ntiles) {
-            lo += static_cast<int32_t>(x[u] & 0xFFFFu);
-            hi += static_cast<int32_t>(x[u] >> 16);
-          }
-      }
-      if (lo) atomicAdd(&L.c[2 * ep], lo);
-      if (hi && 2 * ep + 1 < E) atomicAdd(&L.c[2 * ep + 1], hi);
-    }
-    __syncthreads();
-  }
+  // -- phase 0: pairs per expert = sum of the tile histograms.
+  for (int e = tid; e < E; e += kPlanThreads) L.c[e] = 0;
+  __syncthreads();
+  if (hs % 8 == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0)
+    sum_hist_rows<4>(H, hs, a.ntiles, E, L.c);
+  else
+    sum_hist_rows<1>(H, hs, a.ntiles, E, L.c);
+  __syncthreads();
   // -- phase 1: home loads, total, grid (wave 0, wave reductions only: LDS
   // atomics on one address would be serialised lane by lane).
   if (wave == 0) {
     uint32_t total = 0, qmax = 0, floor = 0, cmax = 0;
     for (int e0 = 0; e0 < E; e0 += 64)
       cmax = max(cmax, wave_max(e0 + lane < E ? static_cast<uint32_t>(L.c[e0 + lane]) : 0u));
+    // domain loads by LDS atomics (L.dom starts at zero): one instruction
+    // per 64 ranks instead of a serial sum per domain
     for (int r0 = 0; r0 < R; r0 += 64) {
       const int r = r0 + lane;
       int32_t h = 0;
       if (r < R) {
         for (int j = 0; j < M; ++j) h += L.c[r * M + j];
         L.H[r] = h;
+        atomicAdd(&L.dom[r / D], h);
       }
       total += wave_sum(static_cast<uint32_t>(h));
       qmax = max(qmax, wave_max(static_cast<uint32_t>(h)));
     }
     for (int d0 = 0; d0 < a.ndom; d0 += 64) {
       const int d = d0 + lane;
-      uint32_t fl = 0;
-      if (d < a.ndom) {
-        uint32_t dl = 0;
-        for (int q = 0; q < D; ++q) dl += static_cast<uint32_t>(L.H[d * D + q]);
-        fl = (dl + D - 1) / D;
-      }
-      floor = max(floor, wave_max(fl));
+      const uint32_t dl = d < a.ndom ? static_cast<uint32_t>(L.dom[d]) : 0u;
+      floor = max(floor, wave_max((dl + D - 1) / D));
     }
     if (lane == 0) {
       // lowest quota aimed at: the early-stop target times the mean (at
