@@ -1023,31 +1023,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
 // workgroups per CU.
 struct RerouteLds {
   unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids (pass 1)
+  i32x4* inst;     // [n_inst] per instance: quota end, physical expert, first
+                   // layout row, then (LAYOUT) staging slot minus layout row
+                   // of its run; one 16-byte read per instance in pass 2
+  uint32_t* bits;  // LAYOUT: [kTile / 32] bit j set where a non-empty run starts at slot j
   int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
   int32_t* tcnt;   // [E] the tile's ordinal base of e, then the tile's pairs of e
-  int32_t* kfirst; // [E] first instance of e that holds ordinals of this tile
+  uint32_t* ek;    // [E] first instance of e holding ordinals of this tile | last instance << 16
   int32_t* iptr;   // [E+1]
-  int32_t* iend;   // [n_inst]
-  int32_t* iphys;  // [n_inst]
-  int32_t* ibase;  // [n_inst]
-  int32_t* roff;   // [n_inst+1] run offsets inside the tile's staging area
-  int32_t* ro0;    // [n_inst] first ordinal of the run
-  int32_t* tmp;    // [waves + 1]
+  int32_t* roff;   // LAYOUT: [n_inst+1] run offsets inside the staging area | runs
+                   // before with pairs << 16
+  int32_t* nr;     // LAYOUT: [n_inst] staging slot minus layout row of the q-th non-empty run
   float* wst;      // [kTile] staged slot's routing weight (pass 2; shares its
                    // words with peers, which pass 1 is done with)
   uint16_t* sn;    // [kTile] staged slot's pair index inside the tile
 };
 
-// Words of the region that holds peers, and with the layout also sp.
+// Words of the region that holds peers, and with the layout also sp.  A
+// multiple of 4 words, so the instance records after it are 16-byte aligned.
 __host__ __device__ inline size_t reroute_shared_words(int E, bool layout, int waves) {
   const size_t peers = 2ull * waves * (E + 1);
   return layout && peers < static_cast<size_t>(kTile) ? kTile : peers;
 }
 
 __host__ __device__ inline size_t reroute_lds_bytes(int E, int n_inst, bool layout, int waves) {
-  size_t words = reroute_shared_words(E, layout, waves) + static_cast<size_t>(waves) * E + 2ull * E +
-                 (E + 1) + 3ull * n_inst;
-  if (layout) words += (n_inst + 1) + n_inst + (waves + 1) + kTile / 2;
+  size_t words = reroute_shared_words(E, layout, waves) + 4ull * n_inst + static_cast<size_t>(waves) * E +
+                 2ull * E + (E + 1);
+  if (layout) words += kTile / 32 + (n_inst + 1) + n_inst + kTile / 2;
   return 4 * words;
 }
 
@@ -1069,17 +1071,17 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
     S.peers = reinterpret_cast<unsigned long long*>(q);
     S.wst = reinterpret_cast<float*>(q);
     q += reroute_shared_words(E, LAYOUT, W);
+    S.inst = reinterpret_cast<i32x4*>(q); q += 4 * n_inst;
+    if (LAYOUT) {
+      S.bits = reinterpret_cast<uint32_t*>(q); q += kTile / 32;
+    }
     S.cntw = q; q += W * E;
     S.tcnt = q; q += E;
-    S.kfirst = q; q += E;
+    S.ek = reinterpret_cast<uint32_t*>(q); q += E;
     S.iptr = q; q += E + 1;
-    S.iend = q; q += n_inst;
-    S.iphys = q; q += n_inst;
-    S.ibase = q; q += n_inst;
     if (LAYOUT) {
       S.roff = q; q += n_inst + 1;
-      S.ro0 = q; q += n_inst;
-      S.tmp = q; q += W + 1;
+      S.nr = q; q += n_inst;
       S.sn = reinterpret_cast<uint16_t*>(q);
     }
   }
@@ -1101,11 +1103,10 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
   for (int i = threadIdx.x; i < W * (E + 1); i += NT) S.peers[i] = 0;
   for (int i = threadIdx.x; i < W * E; i += NT) S.cntw[i] = 0;
   for (int i = threadIdx.x; i <= E; i += NT) S.iptr[i] = plan[off_iptr + i];
-  for (int i = threadIdx.x; i < n_inst; i += NT) {
-    S.iend[i] = plan[off_iend + i];
-    S.iphys[i] = plan[off_iphys + i];
-    S.ibase[i] = plan[off_ibase + i];
-  }
+  for (int i = threadIdx.x; i < n_inst; i += NT)
+    S.inst[i] = i32x4{plan[off_iend + i], plan[off_iphys + i], plan[off_ibase + i], 0};
+  if (LAYOUT)
+    for (int i = threadIdx.x; i < kTile / 32; i += NT) S.bits[i] = 0;
   for (int e = threadIdx.x; e < E; e += NT) S.tcnt[e] = tb[e];
   __syncthreads();
 
@@ -1148,35 +1149,49 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
     // then at most a few steps further
     int k = S.iptr[e];
     const int last = S.iptr[e + 1] - 1;
-    while (k < last && b0 >= S.iend[k]) ++k;
-    S.kfirst[e] = k;
+    while (k < last && b0 >= S.inst[k].x) ++k;
+    S.ek[e] = static_cast<uint32_t>(k) | (static_cast<uint32_t>(last) << 16);
   }
   __syncthreads();
 
   if (LAYOUT) {
     // runs: instance i of expert e holds the tile's ordinals
-    // [max(start_i, b), min(end_i, b + count)) where b is the tile base of e
+    // [max(start_i, b), min(end_i, b + count)) where b is the tile base of e.
+    // The scan below sums the run lengths (low half) and the non-empty runs
+    // (high half) together; the first ordinal waits in the record's fourth word.
     for (int e = threadIdx.x; e < E; e += NT) {
       const int32_t b0 = S.cntw[e], b1 = b0 + S.tcnt[e];
       int32_t start = 0;
       for (int i = S.iptr[e]; i < S.iptr[e + 1]; ++i) {
-        const int32_t end = S.iend[i];
-        const int32_t lo = max(start, b0), hi = min(end, b1);
-        S.roff[i] = max(0, hi - lo);
-        S.ro0[i] = lo;
+        const int32_t end = S.inst[i].x;
+        const int32_t lo = max(start, b0), len = max(0, min(end, b1) - lo);
+        S.roff[i] = len | (len > 0 ? 1 << 16 : 0);
+        S.inst[i].w = lo;
         start = end;
       }
     }
     // instance entries beyond the plan's used ones are empty runs
     for (int i = S.iptr[E] + threadIdx.x; i < n_inst; i += NT) {
       S.roff[i] = 0;
-      S.ro0[i] = 0;
+      S.inst[i].w = 0;
     }
     __syncthreads();
     if (wave == 0) wave_exclusive_scan(S.roff, n_inst);
     __syncthreads();
-    // ro0 becomes staging slot minus layout row of each run
-    for (int i = threadIdx.x; i < n_inst; i += NT) S.ro0[i] = S.roff[i] - S.ibase[i] - S.ro0[i];
+    // the fourth word becomes staging slot minus layout row of each run;
+    // a non-empty run (the q-th) also marks its first slot and files the
+    // same offset under q
+    for (int i = threadIdx.x; i < n_inst; i += NT) {
+      const int32_t r0 = S.roff[i];
+      const int off = r0 & 0xFFFF, q = r0 >> 16, len = (S.roff[i + 1] - r0) & 0xFFFF;
+      const int32_t d = off - S.inst[i].z - S.inst[i].w;
+      S.inst[i].w = d;
+      // (the bounds only matter for a corrupted plan record)
+      if (len > 0 && off < kTile && q < n_inst) {
+        S.nr[q] = d;
+        atomicOr(&S.bits[off >> 5], 1u << (off & 31));
+      }
+    }
     __syncthreads();
   }
 
@@ -1192,6 +1207,10 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
     for (int c = 0; c < T::kChunks; ++c) v[c] = reinterpret_cast<const uint32_t*>(S.wst)[c * NT + threadIdx.x];
     __syncthreads();
   }
+  // phys and pos go out non-temporally: each wave store is whole lines and
+  // nothing here reads them back, so they need not stay in L2 (the scattered
+  // layout stores below keep the default policy, under which their partial
+  // lines merge in L2)
   const __amdgpu_buffer_rsrc_t r_phys = row_rsrc(phys_idx + first, static_cast<uint32_t>(n_here) * 4u);
   const __amdgpu_buffer_rsrc_t r_pos = row_rsrc(pos + first, static_cast<uint32_t>(n_here) * 4u);
 #pragma unroll
@@ -1201,53 +1220,52 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
     const int e = static_cast<int>(v[c] & 0x7FFu);
     if (e < E) {
       const int32_t o = my[e] + static_cast<int32_t>(v[c] >> 11);
-      int k = S.kfirst[e];
-      const int last = S.iptr[e + 1] - 1;
-      while (k < last && o >= S.iend[k]) ++k;
-      p = S.iphys[k];
-      row = S.ibase[k] + o;
+      const uint32_t ek = S.ek[e];
+      int k = static_cast<int>(ek & 0xFFFFu);
+      const int last = static_cast<int>(ek >> 16);
+      i32x4 rec = S.inst[k];
+      while (k < last && o >= rec.x) rec = S.inst[++k];
+      p = rec.y;
+      row = rec.z + o;
       if (LAYOUT) {
-        const int32_t sl = row + S.ro0[k];
+        const int32_t sl = row + rec.w;
         if (sl >= 0 && sl < kTile) {
           S.sn[sl] = static_cast<uint16_t>(i);
           S.wst[sl] = wl[c];
         }
       }
     }
-    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, kNonTemporal);
   }
   if (LAYOUT) {
     __syncthreads();
     // write the staged slots in order: consecutive threads take consecutive
-    // slots, which are consecutive layout rows inside each run.  A slot's
-    // run is the last one starting at or before it: a binary search over
-    // the run offsets in a fixed number of steps (instances number fewer
-    // than 4096), so the searches of a thread's slots interleave.  A tile
-    // holds at most n_here valid pairs; the checks only matter for a
+    // slots, which are consecutive layout rows inside each run.  A wave's 64
+    // slots are one aligned block b (lane = slot - 64 b), and a slot's run
+    // is the q-th non-empty one, q + 1 being the run starts at or before
+    // it: the starts in blocks before b (each wave scans the blocks' start
+    // counts itself, two blocks a lane) plus those in b up to the lane.
+    // A tile holds at most n_here valid pairs; the checks only matter for a
     // corrupted plan record.
     constexpr int kPer = kTile / NT;
-    constexpr int kSearchSteps = 12;
-    const int nt = min(S.roff[n_inst], n_here);
+    static_assert(kTile / 64 == 128, "two 64-slot blocks per lane");
+    const int nt = min(S.roff[n_inst] & 0xFFFF, n_here);
     const int32_t tile0 = span.tile0;
-    int lo[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) lo[u] = 0;
-#pragma unroll
-    for (int st = kSearchSteps - 1; st >= 0; --st) {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int j = u * NT + static_cast<int>(threadIdx.x);
-        const int mid = lo[u] + (1 << st);
-        if (mid < n_inst && S.roff[mid] <= j) lo[u] = mid;
-      }
-    }
+    const uint64_t upto = (2ull << lane) - 1;  // lanes 0..lane (all for lane 63)
+    const unsigned long long* bits64 = reinterpret_cast<const unsigned long long*>(S.bits);
+    const int c0 = __builtin_popcountll(bits64[2 * lane]), c1 = __builtin_popcountll(bits64[2 * lane + 1]);
+    const int incl = wave_inclusive_scan(c0 + c1);
+    const int before_even = incl - c0 - c1, before_odd = incl - c1;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int j = u * NT + static_cast<int>(threadIdx.x);
+      const int b = __builtin_amdgcn_readfirstlane(j >> 6);
+      const int pb = static_cast<int>(readlane(static_cast<uint32_t>((b & 1) ? before_odd : before_even), b >> 1));
       if (j < nt) {
+        const int q = min(pb + __builtin_popcountll(bits64[b] & upto) - 1, n_inst - 1);
         const int n = S.sn[j];
-        const int32_t row = j - S.ro0[lo[u]];
+        const int32_t row = j - S.nr[q];
         if (n < n_here && row >= 0 && row < N) {
           inv[lb + row] = tile0 + n;
           w_perm[lb + row] = S.wst[j];
@@ -1775,8 +1793,8 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
           if (!gather_w) S_.wst[sl] = wl[c];
         }
       }
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, kNonTemporal);
+      __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, kNonTemporal);
     }
   }
   if (INTERLEAVE && later != 0u) {
@@ -1844,8 +1862,8 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
             if (!gather_w) S_.wst[sl] = wl[c];
           }
         }
-        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(p), r_phys, i * 4, 0, kNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<uint32_t>(row), r_pos, i * 4, 0, kNonTemporal);
       }
     }
   }
