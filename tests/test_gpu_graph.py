@@ -20,8 +20,8 @@ def test_balance_graph_replays_equal_eager(mode):
     idx, wt = routing_cached(2, 0, 0, 1024)
     ctx = U.ultraep_create(w.E, w.R, w.S, w.D, reroute_mode=mode)
     buf = U.Buffers(ctx, 1, w.T, w.k, "cuda")
-    d_idx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
-    d_w = torch.from_numpy(np.ascontiguousarray(wt)).cuda()
+    d_idx = torch.from_numpy(np.array(idx, copy=True)).cuda()
+    d_w = torch.from_numpy(np.array(wt, copy=True)).cuda()
 
     def bal():
         U.ultraep_balance(ctx, d_idx, w.T, w.k, buf.workspace, buf.plans, buf.phys_idx, buf.pos,
