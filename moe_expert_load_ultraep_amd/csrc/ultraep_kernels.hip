@@ -1028,7 +1028,7 @@ struct RerouteLds {
                    // of its run; one 16-byte read per instance in pass 2
   uint32_t* bits;  // LAYOUT: [kTile / 32] bit j set where a non-empty run starts at slot j
   int32_t* cntw;   // [waves][E]: per-wave counters, then per-wave ordinal bases
-  int32_t* tcnt;   // [E] the tile's ordinal base of e, then the tile's pairs of e
+  int32_t* tcnt;   // [E] the tile's ordinal base of e
   uint32_t* ek;    // [E] first instance of e holding ordinals of this tile | last instance << 16
   int32_t* iptr;   // [E+1]
   int32_t* roff;   // LAYOUT: [n_inst+1] run offsets inside the staging area | runs
@@ -1130,10 +1130,15 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
   __syncthreads();
   // with the layout, the packed values wait out the steps up to pass 2 in
   // the staging words (pass 1 is done with its lane masks), so they hold no
-  // registers meanwhile
+  // registers meanwhile; the registers take the pairs' weights instead (one
+  // coalesced load per chunk), which arrive while the runs are set up
+  float wl[LAYOUT ? T::kChunks : 1];
   if (LAYOUT) {
 #pragma unroll
     for (int c = 0; c < T::kChunks; ++c) reinterpret_cast<uint32_t*>(S.wst)[c * NT + threadIdx.x] = v[c];
+#pragma unroll
+    for (int c = 0; c < T::kChunks; ++c)
+      wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
   }
   for (int e = threadIdx.x; e < E; e += NT) {
     const int32_t b0 = S.tcnt[e];
@@ -1144,38 +1149,37 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
       S.cntw[q * E + e] = run;
       run += t;
     }
-    S.tcnt[e] = run - b0;
     // the tile's ordinals of e start in this instance; a pair's instance is
     // then at most a few steps further
-    int k = S.iptr[e];
-    const int last = S.iptr[e + 1] - 1;
+    const int i0 = S.iptr[e], last = S.iptr[e + 1] - 1;
+    int k = i0;
     while (k < last && b0 >= S.inst[k].x) ++k;
     S.ek[e] = static_cast<uint32_t>(k) | (static_cast<uint32_t>(last) << 16);
-  }
-  __syncthreads();
-
-  if (LAYOUT) {
-    // runs: instance i of expert e holds the tile's ordinals
-    // [max(start_i, b), min(end_i, b + count)) where b is the tile base of e.
-    // The scan below sums the run lengths (low half) and the non-empty runs
-    // (high half) together; the first ordinal waits in the record's fourth word.
-    for (int e = threadIdx.x; e < E; e += NT) {
-      const int32_t b0 = S.cntw[e], b1 = b0 + S.tcnt[e];
+    if (LAYOUT) {
+      // runs: instance i of e holds the tile's ordinals [max(start_i, b0),
+      // min(end_i, b1)) of [b0, b1).  The scan below sums the run lengths
+      // (low half) and the non-empty runs (high half) together; the first
+      // ordinal waits in the record's fourth word.
       int32_t start = 0;
-      for (int i = S.iptr[e]; i < S.iptr[e + 1]; ++i) {
+      for (int i = i0; i <= last; ++i) {
         const int32_t end = S.inst[i].x;
-        const int32_t lo = max(start, b0), len = max(0, min(end, b1) - lo);
+        const int32_t lo = max(start, b0), len = max(0, min(end, run) - lo);
         S.roff[i] = len | (len > 0 ? 1 << 16 : 0);
         S.inst[i].w = lo;
         start = end;
       }
     }
+  }
+  if (LAYOUT) {
     // instance entries beyond the plan's used ones are empty runs
     for (int i = S.iptr[E] + threadIdx.x; i < n_inst; i += NT) {
       S.roff[i] = 0;
       S.inst[i].w = 0;
     }
-    __syncthreads();
+  }
+  __syncthreads();
+
+  if (LAYOUT) {
     if (wave == 0) wave_exclusive_scan(S.roff, n_inst);
     __syncthreads();
     // the fourth word becomes staging slot minus layout row of each run;
@@ -1196,13 +1200,8 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
   }
 
   // pass 2: instance, physical expert and layout row of each pair; with the
-  // layout, each pair's weight (one coalesced load per chunk, issued first)
-  // and index go to its run's slot
-  float wl[LAYOUT ? T::kChunks : 1];
+  // layout, each pair's weight and index go to its run's slot
   if (LAYOUT) {
-#pragma unroll
-    for (int c = 0; c < T::kChunks; ++c)
-      wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
 #pragma unroll
     for (int c = 0; c < T::kChunks; ++c) v[c] = reinterpret_cast<const uint32_t*>(S.wst)[c * NT + threadIdx.x];
     __syncthreads();
