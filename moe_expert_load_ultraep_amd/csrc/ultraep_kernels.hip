@@ -1142,33 +1142,46 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
   }
   for (int e = threadIdx.x; e < E; e += NT) {
     const int32_t b0 = S.tcnt[e];
+    // counts are read eight at a time before their bases are written: the
+    // reads then go out back to back instead of one round trip per wave
+    constexpr int kGroup = W < 8 ? W : 8;
     int32_t run = b0;
 #pragma unroll
-    for (int q = 0; q < W; ++q) {
-      const int32_t t = S.cntw[q * E + e];
-      S.cntw[q * E + e] = run;
-      run += t;
+    for (int q0 = 0; q0 < W; q0 += kGroup) {
+      int32_t t[kGroup];
+#pragma unroll
+      for (int q = 0; q < kGroup; ++q) t[q] = S.cntw[(q0 + q) * E + e];
+#pragma unroll
+      for (int q = 0; q < kGroup; ++q) {
+        S.cntw[(q0 + q) * E + e] = run;
+        run += t[q];
+      }
     }
-    // the tile's ordinals of e start in this instance; a pair's instance is
-    // then at most a few steps further
+    // k: the instance where the tile's ordinals of e start (the first whose
+    // quota end passes b0); a pair's instance is then at most a few steps
+    // further.  With the layout, the same walk sets up the runs: instance i
+    // holds the tile's ordinals [max(start_i, b0), min(end_i, b1)) of
+    // [b0, b1).  The scan below sums the run lengths (low half) and the
+    // non-empty runs (high half) together; the first ordinal waits in the
+    // record's fourth word.  The next end is read ahead, so the walk takes
+    // one LDS round trip per instance.
     const int i0 = S.iptr[e], last = S.iptr[e + 1] - 1;
-    int k = i0;
-    while (k < last && b0 >= S.inst[k].x) ++k;
-    S.ek[e] = static_cast<uint32_t>(k) | (static_cast<uint32_t>(last) << 16);
-    if (LAYOUT) {
-      // runs: instance i of e holds the tile's ordinals [max(start_i, b0),
-      // min(end_i, b1)) of [b0, b1).  The scan below sums the run lengths
-      // (low half) and the non-empty runs (high half) together; the first
-      // ordinal waits in the record's fourth word.
-      int32_t start = 0;
-      for (int i = i0; i <= last; ++i) {
-        const int32_t end = S.inst[i].x;
+    int k = -1;
+    int32_t start = 0, end = S.inst[i0].x;
+    for (int i = i0; i <= last; ++i) {
+      const int32_t next = i < last ? S.inst[i + 1].x : 0;
+      if (k < 0 && (b0 < end || i == last)) k = i;
+      if (LAYOUT) {
         const int32_t lo = max(start, b0), len = max(0, min(end, run) - lo);
         S.roff[i] = len | (len > 0 ? 1 << 16 : 0);
         S.inst[i].w = lo;
-        start = end;
+      } else if (k >= 0) {
+        break;
       }
+      start = end;
+      end = next;
     }
+    S.ek[e] = static_cast<uint32_t>(k) | (static_cast<uint32_t>(last) << 16);
   }
   if (LAYOUT) {
     // instance entries beyond the plan's used ones are empty runs
