@@ -129,6 +129,41 @@ def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero, fused):
     check_plan_invariants(pl, pl.c, allow_zero)
 
 
+def _degenerate_routing(kind, E, R, T, k):
+    """Routing patterns with extreme structure: every pair on one expert
+    (one run covers whole tiles), two experts alternating (every chunk holds
+    both), every pair on the experts of rank 0 (the other ranks all spare),
+    and every id invalid (no load at all)."""
+    g = np.arange(R * T, dtype=np.int64)[:, None]
+    j = np.arange(k, dtype=np.int64)[None, :]
+    if kind == "one_expert":
+        idx = np.full((R * T, k), 3, dtype=np.int64)
+    elif kind == "two_experts":
+        idx = np.where((g + j) % 2 == 0, 0, 5) + 0 * g
+    elif kind == "rank0_experts":
+        M = E // R
+        idx = (g * k + j) % M
+    elif kind == "all_invalid":
+        idx = np.where((g + j) % 3 == 0, -1, E) + 0 * g
+    else:
+        raise ValueError(kind)
+    return idx.astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["one_expert", "two_experts", "rank0_experts", "all_invalid"])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("fused", [True, False])
+def test_degenerate_routing(kind, mode, fused):
+    E, R, S, D, T, k = 16, 4, 2, 4, 5000, 4  # 20,000 pairs per rank: three tiles, the last ragged
+    say(f"degenerate {kind} mode={mode} fused={fused}")
+    idx = _degenerate_routing(kind, E, R, T, k)
+    wt = np.random.default_rng(11).random((R * T, k)).astype(np.float32)
+    ctx = U.ultraep_create(E, R, S, D, reroute_mode=mode)
+    got = run_balance(ctx, idx[None], wt[None], T, k, fused=fused)
+    pl, phys, pos = assert_layer_equal(ctx, got, 0, idx, wt, E, R, S, D)
+    check_plan_invariants(pl, pl.c, False)
+
+
 @pytest.mark.parametrize("thr", [(101, 100), (105, 100), (3, 2)])
 def test_threshold_single_layer(thr):
     """The early-stop target above 1 on the single-layer workload (1024
