@@ -182,17 +182,22 @@ __device__ void block_exclusive_scan2(int32_t* a, int na, int32_t* b, int nb, in
 // total): each lane sums a contiguous run, the lanes scan their sums, and
 // each lane writes its run's prefixes.  For the short arrays of a tile's
 // runs one wave is enough, and the other waves skip the block scan's two
-// extra barriers.  The caller synchronises afterwards.
+// extra barriers.  The caller synchronises afterwards.  With COUNT, each
+// value x (a run length below 2^16) is taken as x + 2^16 [x > 0], so the
+// prefixes hold the offset in the low half and the non-empty runs before
+// in the high half.
+template <bool COUNT = false>
 __device__ void wave_exclusive_scan(int32_t* a, int n) {
   const int lane = lane_id();
   const int per = (n + 63) / 64;
   const int b = min(lane * per, n), en = min(b + per, n);
+  auto val = [](int32_t x) { return COUNT ? x + (x > 0 ? 1 << 16 : 0) : x; };
   int32_t s = 0;
-  for (int i = b; i < en; ++i) s += a[i];
+  for (int i = b; i < en; ++i) s += val(a[i]);
   const int32_t inc = wave_inclusive_scan(s);
   int32_t run = inc - s;
   for (int i = b; i < en; ++i) {
-    const int32_t v = a[i];
+    const int32_t v = val(a[i]);
     a[i] = run;
     run += v;
   }
@@ -1352,11 +1357,11 @@ struct LocalLds {
   int32_t* ia;     // [n4] local take
   int32_t* irho;   // [n4] remaining quota after the local take
   int32_t* iptr;   // [E+1]
-  int32_t* roff;   // [n_inst+E+1] LAYOUT: run offsets in the staging area
-                   // (instance i's pool run at i, e's local run at n_inst + e)
+  int32_t* roff;   // [n_inst+E+1] LAYOUT: run lengths, then their offsets in the
+                   // staging area | non-empty runs before << 16 (instance i's
+                   // pool run at i, e's local run at n_inst + e)
   int32_t* ro0;    // [n_inst+E] LAYOUT: first layout row of the run, then
                    // staging slot minus layout row
-  int32_t* tmp;    // [waves+1]
   int32_t* phdr;   // INTERLEAVE: [kPhaseHeaders][4] later phases the tile reaches
   int32_t* pent;   // INTERLEAVE: [kPhaseEntries][2] their instances, in order
   int32_t* pcnt;   // INTERLEAVE: [4] headers and entries handed out
@@ -1377,6 +1382,17 @@ constexpr int kErCount = 0, kErBlk = 1, kErPool = 2, kErLoc = 3;
 
 __host__ __device__ inline int local_n4(int n_inst) { return (n_inst + 3) & ~3; }
 
+// The write-out's words: the start bits of the tile's slots and one offset
+// per run.  The words free after pass 2 (per-wave bases, expert records,
+// the interleave's phase pool and the instance tables) usually hold them.
+__host__ __device__ inline size_t local_wo_words(int E, int n_inst) {
+  return kTile / 32 + static_cast<size_t>(n_inst) + E;
+}
+__host__ __device__ inline size_t local_dead_words(int E, int n_inst, bool interleave, int waves) {
+  return static_cast<size_t>(waves) * E + static_cast<size_t>(kErWords) * E +
+         (interleave ? 4 * kPhaseHeaders + 2 * kPhaseEntries + 4 : 0) + 9ull * local_n4(n_inst);
+}
+
 // gather: the write-out reads the weights from w instead of LDS, which
 // frees the words of the staged weights for the pair indices.
 __host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout, bool interleave,
@@ -1386,8 +1402,22 @@ __host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout
   size_t words = reroute_shared_words(E, true, waves) + static_cast<size_t>(waves) * E +
                  static_cast<size_t>(kErWords) * E + 9 * n4 + (E + 1);
   if (interleave) words += 4 * kPhaseHeaders + 2 * kPhaseEntries + 4;
-  if (layout) words += (gather ? 0 : kTile / 2) + 2ull * (n_inst + E) + 1 + (waves + 1);
+  if (layout) {
+    words += (gather ? 0 : kTile / 2) + 2ull * (n_inst + E) + 1;
+    if (local_dead_words(E, n_inst, interleave, waves) < local_wo_words(E, n_inst)) words += local_wo_words(E, n_inst);
+  }
   return 4 * words;
+}
+
+// Where the write-out's start bits and per-run offsets go: the words of the
+// per-wave bases and the expert and instance tables (done with after pass
+// 2; they start 16-byte aligned), or past the end of the allocation when
+// those are too few (small shapes only).
+__host__ __device__ inline int32_t* local_wo_base(int32_t* lds, int E, int n_inst, bool interleave,
+                                                  int waves, bool gather) {
+  const size_t shared = reroute_shared_words(E, true, waves) + (gather ? 0 : kTile / 2);
+  if (local_dead_words(E, n_inst, interleave, waves) >= local_wo_words(E, n_inst)) return lds + shared;
+  return lds + local_lds_bytes(E, n_inst, true, interleave, waves, gather) / 4 - local_wo_words(E, n_inst);
 }
 
 // Round and place of pool pair u of the expert whose sorted tables are the
@@ -1461,7 +1491,6 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
     if (LAYOUT) {
       S_.roff = q; q += n_inst + E + 1;
       S_.ro0 = q; q += n_inst + E;
-      S_.tmp = q;
     }
   }
   const int64_t blkid = blockIdx.x;
@@ -1722,9 +1751,9 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
       S_.ro0[i] = 0;
     }
     __syncthreads();
-    if (wave == 0) wave_exclusive_scan(S_.roff, n_inst + E);
+    if (wave == 0) wave_exclusive_scan<true>(S_.roff, n_inst + E);
     __syncthreads();
-    for (int r = threadIdx.x; r < n_inst + E; r += NT) S_.ro0[r] = S_.roff[r] - S_.ro0[r];
+    for (int r = threadIdx.x; r < n_inst + E; r += NT) S_.ro0[r] = (S_.roff[r] & 0xFFFF) - S_.ro0[r];
   }
   __syncthreads();
 
@@ -1883,34 +1912,49 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
     __syncthreads();
     // the staged slots in order: consecutive threads take consecutive slots,
     // which are consecutive layout rows inside each run.  A slot's run is
-    // the last one starting at or before it: a binary search over the run
-    // offsets in a fixed number of steps (runs number fewer than 4096), so
-    // the searches of a thread's slots interleave.  The checks only matter
-    // for a corrupted plan record.
+    // the q-th non-empty one, q + 1 being the run starts at or before it.
+    // Pass 2 is done with the per-wave bases and the expert and instance
+    // tables, so their words take the start bits of the slots (cleared, then
+    // set by one atomic OR per non-empty run) and each non-empty run's
+    // staging offset filed under q.  Then a wave's 64 slots are one aligned
+    // block: q is the starts in the blocks before (each wave scans the
+    // blocks' start counts itself, two blocks a lane) plus those in the
+    // block up to the lane.  The checks only matter for a corrupted plan
+    // record.
     constexpr int kPer = kTile / NT;
-    constexpr int kSearchSteps = 12;
+    static_assert(kTile / 64 == 128, "two 64-slot blocks per lane");
     const int nruns = n_inst + E;
-    const int nt = min(S_.roff[nruns], n_here);
-    const int32_t tile0 = span.tile0;
-    int lo[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) lo[u] = 0;
-    // invariant: roff[lo] <= j; the step sizes halve from 2^11
-#pragma unroll
-    for (int st = kSearchSteps - 1; st >= 0; --st) {
-#pragma unroll
-      for (int u = 0; u < kPer; ++u) {
-        const int j = u * NT + static_cast<int>(threadIdx.x);
-        const int mid = lo[u] + (1 << st);
-        if (mid < nruns && S_.roff[mid] <= j) lo[u] = mid;
-      }
+    uint32_t* sbits = reinterpret_cast<uint32_t*>(local_wo_base(lds, E, n_inst, INTERLEAVE, W, gather_w));
+    int32_t* nr = reinterpret_cast<int32_t*>(sbits) + kTile / 32;
+    for (int d = threadIdx.x; d < kTile / 32; d += NT) sbits[d] = 0;
+    for (int r = threadIdx.x; r < nruns; r += NT) {
+      const int32_t r0 = S_.roff[r];
+      const int q = r0 >> 16;
+      if (((S_.roff[r + 1] - r0) & 0xFFFF) > 0 && q < nruns) nr[q] = S_.ro0[r];
     }
+    __syncthreads();
+    for (int r = threadIdx.x; r < nruns; r += NT) {
+      const int32_t r0 = S_.roff[r];
+      const int off = r0 & 0xFFFF;
+      if (((S_.roff[r + 1] - r0) & 0xFFFF) > 0 && off < kTile) atomicOr(&sbits[off >> 5], 1u << (off & 31));
+    }
+    __syncthreads();
+    const int nt = min(S_.roff[nruns] & 0xFFFF, n_here);
+    const int32_t tile0 = span.tile0;
+    const uint64_t upto = (2ull << lane) - 1;  // lanes 0..lane (all for lane 63)
+    const unsigned long long* bits64 = reinterpret_cast<const unsigned long long*>(sbits);
+    const int c0 = __builtin_popcountll(bits64[2 * lane]), c1 = __builtin_popcountll(bits64[2 * lane + 1]);
+    const int incl = wave_inclusive_scan(c0 + c1);
+    const int before_even = incl - c0 - c1, before_odd = incl - c1;
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int j = u * NT + static_cast<int>(threadIdx.x);
+      const int b = __builtin_amdgcn_readfirstlane(j >> 6);
+      const int pb = static_cast<int>(readlane(static_cast<uint32_t>((b & 1) ? before_odd : before_even), b >> 1));
       if (j < nt) {
+        const int q = min(pb + __builtin_popcountll(bits64[b] & upto) - 1, nruns - 1);
         const int n = S_.sn[j];
-        const int32_t row = j - S_.ro0[lo[u]];
+        const int32_t row = j - nr[q];
         if (n < n_here && row >= 0 && row < N) {
           inv[lb + row] = tile0 + n;
           w_perm[lb + row] = gather_w ? w[first + n] : S_.wst[j];
