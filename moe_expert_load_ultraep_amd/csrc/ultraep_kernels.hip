@@ -279,6 +279,8 @@ struct PlanLds {
   int32_t* slotE;  // [R*S]
   int32_t* slotQ;  // [R*S]
   int32_t* instp;  // [E+R*S] physical expert of each instance entry
+  int32_t* iq;     // [E+R*S+1] its quota, then the exclusive prefix of the quotas
+  int32_t* iex;    // [E+R*S] its expert
 };
 
 // The scan workgroups use only the first kPlanThreads words of the same
@@ -287,7 +289,7 @@ __host__ __device__ inline size_t plan_lds_words(int E, int R, int S, int D, int
                                                  int items) {
   return static_cast<size_t>(E) + R + kPlanThreads + ndom + kScalars + items +
          2ull * items * D * S + E + 2ull * E + (E + 1) + (P + 1) + 2ull * R * S +
-         (static_cast<size_t>(E) + static_cast<size_t>(R) * S);
+         3 * (static_cast<size_t>(E) + static_cast<size_t>(R) * S) + 1;
 }
 
 __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
@@ -308,7 +310,9 @@ __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
   L.pload = p; p += a.P + 1;
   L.slotE = p; p += a.R * a.S;
   L.slotQ = p; p += a.R * a.S;
-  L.instp = p;
+  L.instp = p; p += a.E + a.R * a.S;
+  L.iq = p; p += a.E + a.R * a.S + 1;
+  L.iex = p;
   return L;
 }
 
@@ -940,22 +944,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     const uint64_t m = (L.rmask[e] | (1ull << (home % D))) & in_domain;
     const int i = L.iptr[e] + __builtin_popcountll(m & ((1ull << (r % D)) - 1));
     L.instp[i] = p;
+    L.iq[i] = q;
+    L.iex[i] = e;
     inst_phys[i] = p;
     int32_t own = 0;
     for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * hs + e];
     inst_local[i] = min(q, own);
   }
   __syncthreads();
-  for (int e = tid; e < E; e += kPlanThreads) {
-    int32_t end = 0;
-    for (int i = L.iptr[e]; i < L.iptr[e + 1]; ++i) {
-      const int p = L.instp[i];
-      const int j = p % (M + S);
-      const int32_t q = j < M ? L.mq[e] : L.slotQ[(p / (M + S)) * S + (j - M)];
-      end += q;
-      inst_end[i] = end;
-      inst_base[i] = L.pload[p] - (end - q);
-    }
+  // quota ends and first rows: the instances' quotas are scanned once across
+  // all experts (e's instances are contiguous), so each instance's end is
+  // its inclusive prefix minus the prefix at e's first instance
+  const int n_used = L.iptr[E];
+  if (wave == 0) wave_exclusive_scan(L.iq, n_used);
+  __syncthreads();
+  for (int i = tid; i < n_used; i += kPlanThreads) {
+    const int e = L.iex[i];
+    const int32_t q = L.iq[i + 1] - L.iq[i];
+    const int32_t end = L.iq[i + 1] - L.iq[L.iptr[e]];
+    inst_end[i] = end;
+    inst_base[i] = L.pload[L.instp[i]] - (end - q);
   }
   // unused instance entries and the padding between fields get fixed values,
   // so a record is a pure function of its inputs
