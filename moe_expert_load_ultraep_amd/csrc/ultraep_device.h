@@ -84,14 +84,6 @@ __device__ __forceinline__ void wave_max3_bcast(uint32_t& a, uint32_t& b, uint32
   c = readlane(c, 63);
 }
 
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-  x = min(x, dpp<0xB1>(x));
-  x = min(x, dpp<0x4E>(x));
-  x = min(x, dpp<0x141>(x));
-  x = min(x, dpp<0x140>(x));
-  return min(min(readlane(x, 0), readlane(x, 16)), min(readlane(x, 32), readlane(x, 48)));
-}
-
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   x += dpp<0xB1>(x);
   x += dpp<0x4E>(x);

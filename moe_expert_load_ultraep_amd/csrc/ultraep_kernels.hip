@@ -86,9 +86,7 @@ __device__ __forceinline__ void load_tile_ids(const int32_t* __restrict__ src, i
   }
 }
 
-// Exclusive scan of a[0..n) in LDS by a workgroup of NT threads; a[n]
-// receives the total.  tmp holds NT/64 + 1 words.  Wave-level scans use
-// cross-lane shuffles, so only two barriers are needed.
+// Inclusive scan across the wave's lanes (cross-lane shuffles).
 __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
   const int lane = lane_id();
 #pragma unroll
@@ -99,36 +97,9 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
   return x;
 }
 
-template <int NT>
-__device__ void block_exclusive_scan(int32_t* a, int n, int32_t* tmp) {
-  constexpr int W = NT / 64;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int per = (n + NT - 1) / NT;
-  const int b = min(tid * per, n), en = min(b + per, n);
-  int32_t s = 0;
-  for (int i = b; i < en; ++i) s += a[i];
-  const int32_t inc = wave_inclusive_scan(s);
-  if (lane == 63) tmp[wave] = inc;
-  __syncthreads();
-  if (wave == 0) {
-    const int32_t t = lane < W ? tmp[lane] : 0;
-    const int32_t ti = wave_inclusive_scan(t);
-    if (lane < W) tmp[lane] = ti - t;
-    if (lane == W - 1) tmp[W] = ti;
-  }
-  __syncthreads();
-  int32_t run = tmp[wave] + inc - s;
-  for (int i = b; i < en; ++i) {
-    const int32_t v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  if (tid == 0) a[n] = tmp[W];
-  __syncthreads();
-}
-
-// Exclusive scans of two independent arrays with the barriers shared
-// (a[na] and b[nb] receive the totals); tmp holds 2 * (NT / 64 + 1) words.
+// Exclusive scans of two independent arrays in LDS by a workgroup of NT
+// threads, sharing their two barriers (a[na] and b[nb] receive the
+// totals); tmp holds 2 * (NT / 64 + 1) words.
 template <int NT>
 __device__ void block_exclusive_scan2(int32_t* a, int na, int32_t* b, int nb, int32_t* tmp) {
   constexpr int W = NT / 64;
@@ -1022,8 +993,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
 // Same tiling as count.  A pair's ordinal among its expert's pairs is the
 // tile's base (from the plan launch's scan workgroups) + the pairs of earlier
 // waves in the tile + the pair's rank inside its wave, which the wave tracks
-// with ballot groups and per-wave LDS counters, so no sort is needed and the
-// result does not depend on scheduling.
+// with groups of equal ids (found through LDS lane masks) and per-wave LDS
+// counters, so no sort is needed and the result does not depend on
+// scheduling.
 //
 // With LAYOUT the kernel also writes the inverse index and permuted weights.
 // Inside one tile, the pairs that land on one instance have consecutive
@@ -1032,7 +1004,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
 // then written out with consecutive lanes on consecutive rows, instead of
 // one 4-byte scatter per pair.  The staged weights reuse the words of the
 // grouping masks and the indices are 16-bit, which keeps the tables (about
-// 63 KiB at E = 128, 75 KiB at E = 256) small enough for two 16-wave
+// 65 KiB at E = 128, 77 KiB at E = 256) small enough for two 16-wave
 // workgroups per CU.
 struct RerouteLds {
   unsigned long long* peers;  // [waves][E+1] lane masks for grouping equal ids (pass 1)
@@ -1052,8 +1024,9 @@ struct RerouteLds {
   uint16_t* sn;    // [kTile] staged slot's pair index inside the tile
 };
 
-// Words of the region that holds peers, and with the layout also sp.  A
-// multiple of 4 words, so the instance records after it are 16-byte aligned.
+// Words of the region that holds peers, and with the layout also the staged
+// weights.  A multiple of 4 words, so the instance records after it are
+// 16-byte aligned.
 __host__ __device__ inline size_t reroute_shared_words(int E, bool layout, int waves) {
   const size_t peers = 2ull * waves * (E + 1);
   return layout && peers < static_cast<size_t>(kTile) ? kTile : peers;
