@@ -36,7 +36,7 @@ def bf16_normal(rng, shape):
 
 
 def to_dev(a):
-    a = np.ascontiguousarray(a)
+    a = np.array(a, copy=True, order="C")  # writable: torch shares the buffer
     if a.dtype == np.uint16:
         a = a.view(np.int16)
     return torch.from_numpy(a).to(DEV)
