@@ -14,7 +14,7 @@ import moe_expert_load_ultraep_amd as U  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode", [0, 2])
+@pytest.mark.parametrize("mode", [0, 1, 2])
 def test_balance_graph_replays_equal_eager(mode):
     w = W.CONFIGS[2].with_(T=1024)
     idx, wt = routing_cached(2, 0, 0, 1024)

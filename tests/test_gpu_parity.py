@@ -164,6 +164,21 @@ def test_degenerate_routing(kind, mode, fused):
     check_plan_invariants(pl, pl.c, False)
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_degenerate_layers_in_one_call(mode):
+    """Four layers of different structure in one batched call: each layer's
+    plan, replica map and layout must come out as if it were balanced alone."""
+    E, R, S, D, T, k = 16, 4, 2, 4, 3000, 4
+    say(f"degenerate layers mode={mode}")
+    kinds = ["all_invalid", "one_expert", "two_experts", "rank0_experts"]
+    idx = np.stack([_degenerate_routing(kd, E, R, T, k) for kd in kinds])
+    wt = np.random.default_rng(12).random(idx.shape).astype(np.float32)
+    ctx = U.ultraep_create(E, R, S, D, reroute_mode=mode)
+    got = run_balance(ctx, idx, wt, T, k)
+    for l in range(len(kinds)):
+        assert_layer_equal(ctx, got, l, idx[l], wt[l], E, R, S, D)
+
+
 @pytest.mark.parametrize("thr", [(101, 100), (105, 100), (3, 2)])
 def test_threshold_single_layer(thr):
     """The early-stop target above 1 on the single-layer workload (1024
