@@ -511,6 +511,12 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
   if (!shed_pieces<MMAX>(Q, act, r, Hr, a, L, pa, room)) return false;
 
   const uint32_t tie0 = TMASK - static_cast<uint32_t>(lane * MMAX);
+  // the pieces are kept as their queue keys (0: none), so a step's keys
+  // need no packing
+  uint32_t qk[MMAX];
+#pragma unroll
+  for (int j = 0; j < MMAX; ++j)
+    qk[j] = pa[j] > 0 ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u;
   int32_t spare = act ? max(0, Q - Hr) : 0;
   int32_t nh = act ? 0 : S;  // filled slots; inactive lanes look full
   int32_t he[SMAX], hq[SMAX];
@@ -524,8 +530,7 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
   auto queue_key = [&]() {
     uint32_t mk = 0;
 #pragma unroll
-    for (int j = 0; j < MMAX; ++j)
-      mk = max(mk, pa[j] > 0 ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u);
+    for (int j = 0; j < MMAX; ++j) mk = max(mk, qk[j]);
     return mk;
   };
 
@@ -570,16 +575,15 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     const uint32_t core = spare >= amt ? (kFitBit | (kFitBit - 1 - static_cast<uint32_t>(spare)))
                                        : static_cast<uint32_t>(spare);
     const uint32_t key = (elig && spare > 0) ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
-    uint32_t dk = 0, qk = 0;
+    uint32_t dk = 0, qn = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
       // the popped piece is out of the queue for this step
-      const uint32_t kj = (pa[j] > 0 && !(mine && j == jsel))
-                              ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u;
-      qk = max(qk, kj);
+      const uint32_t kj = (mine && j == jsel) ? 0u : qk[j];
+      qn = max(qn, kj);
       dk = max(dk, (elig && room[j] > 0) ? kj : 0u);
     }
-    uint32_t kmax = key, dmax = dk, knext = qk;
+    uint32_t kmax = key, dmax = dk, knext = qn;
     wave_max3_bcast(kmax, dmax, knext);
     const bool fit = (kmax & (kFitBit << 6)) != 0;
     if (!fit && kmax == 0 && dmax == 0) return false;
@@ -604,15 +608,16 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     }
     nh += put ? 1 : 0;
     spare -= rcv ? r_amt : 0;
+    const uint32_t requeue = left > 0 ? (static_cast<uint32_t>(left) << TB) | own_tie : 0u;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
       const int32_t add = (don && j == djs) ? x : 0;
-      pa[j] = (mine && j == jsel) ? left : pa[j] + add;
+      qk[j] = (mine && j == jsel) ? requeue : qk[j] + (static_cast<uint32_t>(add) << TB);
       room[j] -= add;
     }
     // a fit leaves dmax at most knext (the donor's piece is still queued)
     km = max(knext, dmax + (static_cast<uint32_t>(x) << TB));
-    km = max(km, left > 0 ? (static_cast<uint32_t>(left) << TB) | own_tie : 0u);
+    km = max(km, requeue);
   }
   return false;
 }
