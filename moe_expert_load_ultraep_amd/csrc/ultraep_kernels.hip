@@ -894,8 +894,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
   // domain.  One thread per master or filled slot places its instance: the
   // index is e's first index + e's instances on lower ranks (the set bits of
   // e's rank mask below its own); its local take is min(quota, pairs of e
-  // from its rank's tiles).  Then one thread per expert accumulates the
-  // quota ends and first rows over e's instances.
+  // from its rank's tiles).  Then the quota ends and first rows come from
+  // one scan of the instances' quotas.
   int32_t* inst_phys = rec + a.off[ULTRAEP_PLAN_INST_PHYS];
   int32_t* inst_end = rec + a.off[ULTRAEP_PLAN_INST_END];
   int32_t* inst_base = rec + a.off[ULTRAEP_PLAN_INST_BASE];
