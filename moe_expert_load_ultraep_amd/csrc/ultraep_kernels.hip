@@ -1390,7 +1390,10 @@ __host__ __device__ inline size_t local_lds_bytes(int E, int n_inst, bool layout
   if (interleave) words += 4 * kPhaseHeaders + 2 * kPhaseEntries + 4;
   if (layout) {
     words += (gather ? 0 : kTile / 2) + 2ull * (n_inst + E) + 1;
-    if (local_dead_words(E, n_inst, interleave, waves) < local_wo_words(E, n_inst)) words += local_wo_words(E, n_inst);
+    // the write-out's own words, 16-byte aligned at the end, when the words
+    // freed after pass 2 are too few
+    if (local_dead_words(E, n_inst, interleave, waves) < local_wo_words(E, n_inst))
+      words = ((words + 3) & ~size_t{3}) + ((local_wo_words(E, n_inst) + 3) & ~size_t{3});
   }
   return 4 * words;
 }
@@ -1403,7 +1406,8 @@ __host__ __device__ inline int32_t* local_wo_base(int32_t* lds, int E, int n_ins
                                                   int waves, bool gather) {
   const size_t shared = reroute_shared_words(E, true, waves) + (gather ? 0 : kTile / 2);
   if (local_dead_words(E, n_inst, interleave, waves) >= local_wo_words(E, n_inst)) return lds + shared;
-  return lds + local_lds_bytes(E, n_inst, true, interleave, waves, gather) / 4 - local_wo_words(E, n_inst);
+  return lds + local_lds_bytes(E, n_inst, true, interleave, waves, gather) / 4 -
+         ((local_wo_words(E, n_inst) + 3) & ~size_t{3});
 }
 
 // Round and place of pool pair u of the expert whose sorted tables are the

@@ -111,6 +111,7 @@ def test_hand_worked_plans_on_gpu():
     (1024, 1024, 1, 64, 16, 8, 0.0, False),    # E = 1024 and R*S = 1024 together
     (512, 512, 1, 8, 32, 8, 0.0, False),       # 64 domains: more items than waves
     (160, 40, 3, 8, 1000, 8, 0.0, False),
+    (3, 3, 2, 3, 3000, 2, 0.02, False),    # odd expert count, two experts per token
 ])
 @pytest.mark.parametrize("fused", [True, False])
 def test_edge_shapes(E, R, S, D, T, k, invalid, allow_zero, fused):
@@ -403,6 +404,8 @@ def test_locality_reroute_workloads(mode, cfg, T, fused):
     (64, 64, 1, 64, 20000, 1, 0.0, False),   # several tiles per rank (T*k > 8192)
     (512, 64, 4, 64, 512, 8, 0.0, False),    # fused layout in 8-wave workgroups
     (1024, 64, 1, 64, 256, 8, 0.01, False),  # fused layout in 4-wave workgroups
+    (4, 2, 2, 2, 3000, 2, 0.0, False),       # tables too small to hold the write-out's words
+    (3, 3, 2, 3, 3000, 2, 0.02, False),      # the same with an odd expert count
 ])
 def test_locality_reroute_edge_shapes(mode, E, R, S, D, T, k, invalid, allow_zero):
     say(f"locality edge mode={mode} E={E} R={R} S={S} D={D} T={T} k={k}")
