@@ -671,12 +671,12 @@ __device__ void tile_base_scan(const uint16_t* __restrict__ hist, int32_t* __res
 // Pairs per expert of one layer: c[e] += the sum of column e over the tile
 // histogram rows.  Thread (q, ch) reads W 32-bit words (2W experts) of rows
 // ch, ch + nch, ..., so each batch of loads reads whole rows; a batch of B
-// loads is issued before any is used.  W = 4 (16-byte loads, half the
-// batches of W = 1) needs rows of a multiple of 8 entries on a 16-byte
+// loads is issued before any is used (B no larger than a thread's rows
+// need: the loads past the last row repeat it).  W = 4 (16-byte loads, half
+// the batches of W = 1) needs rows of a multiple of 8 entries on a 16-byte
 // aligned base.  The chunk sums meet in LDS.
-template <int W>
+template <int W, int B>
 __device__ void sum_hist_rows(const uint16_t* __restrict__ H, int hs, int ntiles, int E, int32_t* c) {
-  constexpr int B = W == 4 ? 16 : 32;
   const int tid = threadIdx.x;
   const int nq = hs / (2 * W);
   const int nch = kPlanThreads / nq;
@@ -748,10 +748,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
   // -- phase 0: pairs per expert = sum of the tile histograms.
   for (int e = tid; e < E; e += kPlanThreads) L.c[e] = 0;
   __syncthreads();
-  if (hs % 8 == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0)
-    sum_hist_rows<4>(H, hs, a.ntiles, E, L.c);
-  else
-    sum_hist_rows<1>(H, hs, a.ntiles, E, L.c);
+  if (hs % 8 == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0) {
+    const int rows = (a.ntiles + kPlanThreads / (hs / 8) - 1) / (kPlanThreads / (hs / 8));
+    if (rows <= 4)
+      sum_hist_rows<4, 4>(H, hs, a.ntiles, E, L.c);
+    else if (rows <= 8)
+      sum_hist_rows<4, 8>(H, hs, a.ntiles, E, L.c);
+    else
+      sum_hist_rows<4, 16>(H, hs, a.ntiles, E, L.c);
+  } else {
+    sum_hist_rows<1, 32>(H, hs, a.ntiles, E, L.c);
+  }
   __syncthreads();
   // -- phase 1: home loads, total, grid (wave 0, wave reductions only: LDS
   // atomics on one address would be serialised lane by lane).
