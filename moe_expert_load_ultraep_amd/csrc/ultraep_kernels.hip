@@ -930,8 +930,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     L.iq[i] = q;
     L.iex[i] = e;
     inst_phys[i] = p;
+    // pairs of e from rank r's tiles, eight loads in flight at a time
     int32_t own = 0;
-    for (int t = r * a.tpr; t < (r + 1) * a.tpr; ++t) own += H[static_cast<int64_t>(t) * hs + e];
+    const int t1 = (r + 1) * a.tpr;
+    for (int t0 = r * a.tpr; t0 < t1; t0 += 8) {
+      int32_t x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = H[static_cast<int64_t>(min(t0 + u, t1 - 1)) * hs + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) own += t0 + u < t1 ? x[u] : 0;
+    }
     inst_local[i] = min(q, own);
   }
   __syncthreads();
