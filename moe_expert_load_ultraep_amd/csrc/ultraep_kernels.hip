@@ -879,17 +879,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     if (lane == 0) L.scal[kReplicas] = static_cast<int32_t>(filled);
   }
   __syncthreads();
+  // physical loads (recorded as they are written: the scan below turns them
+  // into offsets) and rank loads, both from the final quotas
   for (int p = tid; p < P; p += kPlanThreads) {
     const int r = p / (M + S), j = p % (M + S);
-    L.pload[p] = j < M ? L.mq[r * M + j] : L.slotQ[r * S + (j - M)];
+    const int32_t q = j < M ? L.mq[r * M + j] : L.slotQ[r * S + (j - M)];
+    L.pload[p] = q;
+    rec[a.off[ULTRAEP_PLAN_PHYS_LOAD] + p] = q;
   }
   for (int e = tid; e < E; e += kPlanThreads) L.iptr[e] = 1 + __builtin_popcountll(L.rmask[e]);
-  __syncthreads();
-  // record the loads before the scans overwrite them
-  for (int p = tid; p < P; p += kPlanThreads) rec[a.off[ULTRAEP_PLAN_PHYS_LOAD] + p] = L.pload[p];
   for (int r = tid; r < R; r += kPlanThreads) {
     int32_t s = 0;
-    for (int j = 0; j < M + S; ++j) s += L.pload[r * (M + S) + j];
+    for (int j = 0; j < M; ++j) s += L.mq[r * M + j];
+    for (int j = 0; j < S; ++j) s += L.slotQ[r * S + j];
     rec[a.off[ULTRAEP_PLAN_RANK_AFTER] + r] = s;
     rec[a.off[ULTRAEP_PLAN_RANK_BEFORE] + r] = L.H[r];
   }
