@@ -6,6 +6,8 @@
  *   ultraep_balance          count the exact load per expert, solve the quota
  *                            plan, and give every (token, k) pair its replica
  *                            and its row in the replica-contiguous layout
+ *   ultraep_balance_static   the same without a caller workspace (for callers
+ *                            that cannot allocate)
  *   ultraep_dispatch_layout  the layout's inverse index and permuted weights
  *   ultraep_permute          gather bf16 hidden rows into the layout
  *   ultraep_combine          after the experts: each token's k output rows,
@@ -39,7 +41,8 @@
  *   - Load is counted in pairs.
  *   - Device pointers are caller-owned (any device allocator); the library
  *     allocates no device memory and keeps no device state ([README]
- *     principles: no dynamic allocation at runtime).  The context is host
+ *     principles: no dynamic allocation at runtime), except the fixed static
+ *     workspace of ultraep_balance_static.  The context is host
  *     memory, immutable after create, usable from several streams at once
  *     as long as each call gets its own workspace and outputs.
  *   - Every call is ordered on the given stream (a hipStream_t passed as
@@ -68,6 +71,7 @@ extern "C" {
 #define ULTRAEP_EUNSUPPORTED (-2) /* legal but beyond this build's limits or alignment */
 #define ULTRAEP_ELAUNCH (-3)      /* a HIP launch or runtime call failed */
 #define ULTRAEP_EWORKSPACE (-4)   /* workspace smaller than ultraep_workspace_bytes */
+#define ULTRAEP_ESCRATCH (-5)     /* ultraep_balance_static: more than the static workspace */
 
 /* Limits of this build. */
 #define ULTRAEP_MAX_EXPERTS 1024      /* E */
@@ -263,6 +267,31 @@ int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
                     const float* topk_w, int64_t T, int32_t k, void* workspace,
                     size_t workspace_bytes, void* plans, int32_t* phys_idx, int32_t* pos,
                     int32_t* inv, float* w_perm, void* stream);
+
+/* Allocation-free ultraep_balance, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments (less the workspace), results and errors
+ * as ultraep_balance; the workspace is a static device buffer of
+ * ULTRAEP_STATIC_WORKSPACE_BYTES that every device the library runs on holds
+ * from the time the library's code is loaded there until the process ends.
+ * Its device address is looked up once per device, on the first call with
+ * that device current; the call runs on the device current on the calling
+ * thread, and the stream must belong to it.
+ * Limit: ultraep_workspace_bytes(L, T, k) must not exceed
+ * ULTRAEP_STATIC_WORKSPACE_BYTES (32 MiB: e.g. 64 layers of the E = 128,
+ * R = 64, 8192 x top-8 shape, or 61 layers of E = 256, R = 64, 4096 x
+ * top-8); a larger call fails with ULTRAEP_ESCRATCH before anything is
+ * launched.
+ * Sharing: all calls on one device use the same buffer, which keeps the last
+ * call's contents (nothing in it needs clearing: a call reads only words it
+ * wrote itself).  Two calls that overlap in time on one device race (two
+ * streams, or two host threads without ordering between them); order them
+ * on one stream.  No hipMalloc, hipFree or other allocating call is made. */
+#define ULTRAEP_STATIC_WORKSPACE_BYTES (32u << 20)
+int ultraep_balance_static(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
+                           const float* topk_w, int64_t T, int32_t k, void* plans,
+                           int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                           void* stream);
 
 /* Inverse index and permuted routing weights of the dispatch layout
  * ([README] Interface, "Forward and backward": tokens are dispatched to the

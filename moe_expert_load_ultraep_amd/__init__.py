@@ -8,6 +8,7 @@ status.  There is no fallback: if ``libultraep.so`` is missing the first call
 raises, telling the user to build it.
 
 Names follow the C ABI: ``ultraep_create``, ``ultraep_balance``,
+``ultraep_balance_static``,
 ``ultraep_dispatch_layout``, ``ultraep_permute``, ``ultraep_combine``,
 ``ultraep_combine_backward``, ``ultraep_weight_sync_plan``,
 ``ultraep_weight_sync``, ``ultraep_fold_grads``.
@@ -34,7 +35,9 @@ HEADER_WORDS = ("magic", "E", "R", "S", "D", "M", "P", "N", "total", "dropped", 
 PLAN_MAGIC = 0x55455031
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape, size or alignment",
-          -3: "HIP launch or runtime error", -4: "workspace too small"}
+          -3: "HIP launch or runtime error", -4: "workspace too small",
+          -5: "needs more than the static workspace"}
+STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 class UltraEPError(RuntimeError):
@@ -68,6 +71,7 @@ _SIGNATURES = {
     "ultraep_plan_field": (_I32, [_P, _I32, ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]),
     "ultraep_workspace_bytes": (_I32, [_P, _I32, _I64, _I32, ctypes.POINTER(_SZ)]),
     "ultraep_balance": (_I32, [_P, _I32, _P, _P, _I64, _I32, _P, _SZ, _P, _P, _P, _P, _P, _P]),
+    "ultraep_balance_static": (_I32, [_P, _I32, _P, _P, _I64, _I32, _P, _P, _P, _P, _P, _P]),
     "ultraep_dispatch_layout": (_I32, [_P, _I32, _I64, _I32, _P, _P, _P, _P, _P]),
     "ultraep_permute": (_I32, [_P, _P, _P, _I32, _P, _I64, _I32, _I32, _I32, _P, _I64, _P]),
     "ultraep_fold_grads": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _P]),
@@ -178,6 +182,19 @@ def ultraep_balance(ctx: Context, topk_idx, T: int, k: int, workspace, plans, ph
                                workspace.numel() * workspace.element_size(), _ptr(plans),
                                _ptr(phys_idx), _ptr(pos), _ptr(inv), _ptr(w_perm), _stream(stream))
     _check("ultraep_balance", st)
+
+
+def ultraep_balance_static(ctx: Context, topk_idx, T: int, k: int, plans, phys_idx, pos,
+                           topk_w=None, inv=None, w_perm=None, L: Optional[int] = None,
+                           stream=None) -> None:
+    """ultraep_balance with the library's static device workspace (no
+    workspace argument; at most STATIC_WORKSPACE_BYTES of it)."""
+    if L is None:
+        L = topk_idx.shape[0] if topk_idx.dim() == 3 else 1
+    st = lib().ultraep_balance_static(ctx.handle, L, _ptr(topk_idx), _ptr(topk_w), T, k, _ptr(plans),
+                                      _ptr(phys_idx), _ptr(pos), _ptr(inv), _ptr(w_perm),
+                                      _stream(stream))
+    _check("ultraep_balance_static", st)
 
 
 def ultraep_dispatch_layout(ctx: Context, T: int, k: int, pos, topk_w, inv, w_perm,

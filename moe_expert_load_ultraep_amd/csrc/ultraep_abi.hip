@@ -6,6 +6,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "ultraep.h"
@@ -60,6 +61,40 @@ int pairs_per_layer(const ultraep_ctx* ctx, int64_t T, int32_t k, int32_t* N) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? ULTRAEP_OK : ULTRAEP_ELAUNCH; }
+
+// Workspace of ultraep_balance_static.  Every device the library runs on
+// holds its own copy from the time the code object is loaded there until the
+// process ends.  On the host the name is only a stand-in for the device
+// symbol, never an address: host code takes the device address from
+// hipGetSymbolAddress, looked up once per device on the first call there.
+static __device__ __align__(256) unsigned char scratch[ULTRAEP_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int static_workspace(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ULTRAEP_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return ULTRAEP_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ULTRAEP_ELAUNCH;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ULTRAEP_OK;
+}
+
+// ultraep_balance with a caller's workspace, or (static_ws) with `scratch`.
+// Every check runs before the workspace is looked up or anything launched.
+int balance_impl(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx, const float* topk_w,
+                 int64_t T, int32_t k, void* workspace, size_t workspace_bytes, bool static_ws,
+                 void* plans, int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                 void* stream);
 
 }  // namespace
 
@@ -149,27 +184,16 @@ int ultraep_balance(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
                     const float* topk_w, int64_t T, int32_t k, void* workspace,
                     size_t workspace_bytes, void* plans, int32_t* phys_idx, int32_t* pos,
                     int32_t* inv, float* w_perm, void* stream) {
-  if (!ctx || L < 0) return ULTRAEP_EINVAL;
-  int32_t N = 0;
-  int st = pairs_per_layer(ctx, T, k, &N);
-  if (st != ULTRAEP_OK) return st;
-  if (L == 0) return ULTRAEP_OK;
-  if (!plans || !workspace) return ULTRAEP_EINVAL;
-  if (N > 0 && (!topk_idx || !phys_idx || !pos)) return ULTRAEP_EINVAL;
-  const bool layout = inv || w_perm || topk_w;
-  if (layout && N > 0 && (!inv || !w_perm || !topk_w)) return ULTRAEP_EINVAL;
-  if (!aligned(topk_idx, 4) || !aligned(phys_idx, 4) || !aligned(pos, 4) || !aligned(plans, 4) ||
-      !aligned(workspace, 4) || !aligned(topk_w, 4) || !aligned(inv, 4) || !aligned(w_perm, 4))
-    return ULTRAEP_EUNSUPPORTED;
-  size_t need = 0;
-  st = ultraep_workspace_bytes(ctx, L, T, k, &need);
-  if (st != ULTRAEP_OK) return st;
-  if (workspace_bytes < need) return ULTRAEP_EWORKSPACE;
-  return from_hip(ultraep::launch_balance(ctx->sh, L, topk_idx, topk_w, static_cast<int32_t>(T * k),
-                                          static_cast<int32_t*>(workspace),
-                                          static_cast<int32_t*>(plans), phys_idx, pos,
-                                          layout ? inv : nullptr, w_perm,
-                                          static_cast<hipStream_t>(stream)));
+  return balance_impl(ctx, L, topk_idx, topk_w, T, k, workspace, workspace_bytes, false, plans,
+                      phys_idx, pos, inv, w_perm, stream);
+}
+
+int ultraep_balance_static(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx,
+                           const float* topk_w, int64_t T, int32_t k, void* plans,
+                           int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                           void* stream) {
+  return balance_impl(ctx, L, topk_idx, topk_w, T, k, nullptr, 0, true, plans, phys_idx, pos, inv,
+                      w_perm, stream);
 }
 
 int ultraep_dispatch_layout(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_t k,
@@ -299,8 +323,46 @@ const char* ultraep_status_string(int status) {
     case ULTRAEP_EUNSUPPORTED: return "unsupported shape, size or alignment";
     case ULTRAEP_ELAUNCH: return "HIP launch or runtime error";
     case ULTRAEP_EWORKSPACE: return "workspace too small";
+    case ULTRAEP_ESCRATCH: return "needs more than the static workspace";
     default: return "unknown status";
   }
 }
 
 }  // extern "C"
+
+namespace {
+
+int balance_impl(const ultraep_ctx* ctx, int32_t L, const int32_t* topk_idx, const float* topk_w,
+                 int64_t T, int32_t k, void* workspace, size_t workspace_bytes, bool static_ws,
+                 void* plans, int32_t* phys_idx, int32_t* pos, int32_t* inv, float* w_perm,
+                 void* stream) {
+  if (!ctx || L < 0) return ULTRAEP_EINVAL;
+  int32_t N = 0;
+  int st = pairs_per_layer(ctx, T, k, &N);
+  if (st != ULTRAEP_OK) return st;
+  if (L == 0) return ULTRAEP_OK;
+  if (!plans || (!static_ws && !workspace)) return ULTRAEP_EINVAL;
+  if (N > 0 && (!topk_idx || !phys_idx || !pos)) return ULTRAEP_EINVAL;
+  const bool layout = inv || w_perm || topk_w;
+  if (layout && N > 0 && (!inv || !w_perm || !topk_w)) return ULTRAEP_EINVAL;
+  if (!aligned(topk_idx, 4) || !aligned(phys_idx, 4) || !aligned(pos, 4) || !aligned(plans, 4) ||
+      !aligned(workspace, 4) || !aligned(topk_w, 4) || !aligned(inv, 4) || !aligned(w_perm, 4))
+    return ULTRAEP_EUNSUPPORTED;
+  size_t need = 0;
+  st = ultraep_workspace_bytes(ctx, L, T, k, &need);
+  if (st != ULTRAEP_OK) return st;
+  if (static_ws) {
+    if (need > ULTRAEP_STATIC_WORKSPACE_BYTES) return ULTRAEP_ESCRATCH;
+    st = static_workspace(&workspace);
+    if (st != ULTRAEP_OK) return st;
+  } else if (workspace_bytes < need) {
+    return ULTRAEP_EWORKSPACE;
+  }
+  return from_hip(ultraep::launch_balance(ctx->sh, L, topk_idx, topk_w, static_cast<int32_t>(T * k),
+                                          static_cast<int32_t*>(workspace),
+                                          static_cast<int32_t*>(plans), phys_idx, pos,
+                                          layout ? inv : nullptr, w_perm,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace

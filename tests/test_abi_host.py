@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_function():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(U.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -132,6 +132,28 @@ def test_balance_argument_checks():
     assert call(T=1 << 28, k=8) == -2      # N >= 2^31
     assert call(ctxh=None) == -1
     assert call(L=0, idx=None, ws=None, plans=None, phys=None, pos=None) == 0   # L = 0: no-op
+
+
+def test_balance_static_argument_checks():
+    """The allocation-free balance checks everything, its size limit
+    included, before it looks up its workspace or launches anything."""
+    ctx = U.ultraep_create(128, 64, 2, 64)
+    f = U.lib().ultraep_balance_static
+    h, F = ctx.handle, FAKE
+
+    def call(L=1, idx=F, w=None, T=8192, k=8, plans=F, phys=F, pos=F, inv=None, wp=None):
+        return f(h, L, idx, w, T, k, plans, phys, pos, inv, wp, None)
+
+    assert call(L=65) == -5                # 65 x 512 KiB: beyond the static workspace
+    assert call(L=1 << 20, T=1) == -5
+    assert call(L=-1) == -1
+    assert call(k=0) == -1
+    assert call(plans=None) == -1
+    assert call(w=F) == -1                 # layout outputs given only in part
+    assert call(idx=F + 2) == -2
+    assert call(T=1 << 28) == -2           # N >= 2^31
+    assert call(L=0, idx=None, plans=None, phys=None, pos=None) == 0
+    assert U.status_string(-5) == "needs more than the static workspace"
 
 
 def test_permute_and_fold_argument_checks():
