@@ -7,15 +7,10 @@
 #include <cstdint>
 
 #include "ultraep.h"
+#include "ultraep_geometry.h"
 
 namespace ultraep {
 
-// Pairs handled by one count / reroute workgroup.  The workgroup's waves
-// split the tile into equal stretches (see TileShape in the kernels).
-constexpr int kTile = 8192;
-// The plan solver runs in one workgroup of 16 waves per layer.
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kHeaderWords = ULTRAEP_HDR_WORDS;
 
 struct PlanLayout {
@@ -33,12 +28,6 @@ struct Shape {
   int32_t min_tokens;                    // smallest replica quota kept
   PlanLayout lay;
 };
-
-// Tiles never straddle two ranks: each rank's TK = T*k pairs split into
-// ceil(TK / kTile) tiles, the last one ragged, so a tile's pairs all come
-// from one rank's tokens.
-inline int64_t tiles_per_rank(int64_t TK) { return (TK + kTile - 1) / kTile; }
-inline int64_t ntiles_of(int64_t R, int64_t TK) { return R * tiles_per_rank(TK); }
 
 // Launchers.  All work is queued on `st`; none of them synchronises.
 // ws: 2*L*ntiles*E int32 (tile histograms, tile ordinal bases); TK = T*k

@@ -48,22 +48,6 @@ struct Tiling {
   int32_t N, TK, tpr, ntiles;
 };
 
-// Where tile `tile` of a layer lies: tiles are numbered rank by rank, TK
-// pairs per rank in tiles of kTile (the last one of a rank ragged).  tile0
-// is the layer-relative index of its first pair.
-struct TileSpan {
-  int64_t first;  // index of the first pair in the [L][N] arrays
-  int32_t tile0;  // index of the first pair inside the layer
-  int32_t n;      // pairs in the tile
-};
-
-__device__ __forceinline__ TileSpan tile_span(int64_t layer, int32_t tile, int32_t N, int32_t TK,
-                                              int32_t tpr) {
-  const int32_t r = tile / tpr, q = tile % tpr;
-  const int32_t tile0 = r * TK + q * kTile;
-  return {layer * N + tile0, tile0, min(kTile, TK - q * kTile)};
-}
-
 // Expert ids of one wave's stretch of a tile: chunk c, lane l holds pair
 // base + 64c + l.  Every load is issued unconditionally (indices past the
 // tile are clamped to its last pair and masked afterwards) so all C loads
@@ -188,8 +172,6 @@ __device__ void wave_exclusive_scan(int32_t* a, int n) {
 // half the bytes is half its wait.
 using CountTile = TileShape<16>;
 
-__host__ __device__ inline int32_t hist_stride(int32_t E) { return (E + 1) & ~1; }
-
 __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
     const int32_t* __restrict__ idx, int32_t N, int32_t TK, int32_t tpr, int32_t E, int32_t ntiles,
     uint16_t* __restrict__ hist) {
@@ -232,7 +214,7 @@ struct PlanParams {
 };
 
 enum Scalar {
-  kTotal = 0, kQmax, kFloor, kQlb, kTol, kK, kWin, kReplicas, kCmax, kScalars = 16
+  kTotal = 0, kQmax, kFloor, kQlb, kTol, kK, kWin, kReplicas, kCmax, kScalars = kPlanScalars
 };
 
 struct PlanLds {
@@ -254,36 +236,30 @@ struct PlanLds {
   int32_t* iex;    // [E+R*S] its expert
 };
 
-// The scan workgroups use only the first kPlanThreads words of the same
-// allocation.
 __host__ __device__ inline size_t plan_lds_words(int E, int R, int S, int D, int P, int ndom,
                                                  int items) {
-  return static_cast<size_t>(E) + R + kPlanThreads + ndom + kScalars + items +
-         2ull * items * D * S + E + 2ull * E + (E + 1) + (P + 1) + 2ull * R * S +
-         3 * (static_cast<size_t>(E) + static_cast<size_t>(R) * S) + 1;
+  return static_cast<size_t>(plan_tables(E, R, S, D, P, ndom, items).off[kT_end]);
 }
 
 __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
+  const PlanTables t = plan_tables(a.E, a.R, a.S, a.D, a.P, a.ndom, a.items);
   PlanLds L;
-  int32_t* p = lds;
-  // 64-bit words first: the allocation is 16-byte aligned, so they are
-  // naturally aligned for the 64-bit LDS atomics
-  L.rmask = reinterpret_cast<unsigned long long*>(p); p += 2 * a.E;
-  L.c = p; p += a.E;
-  L.H = p; p += a.R;
-  L.part = p; p += kPlanThreads;
-  L.dom = p; p += a.ndom;
-  L.scal = p; p += kScalars;
-  L.ok = p; p += a.items;
-  L.res = p; p += 2 * a.items * a.D * a.S;
-  L.mq = p; p += a.E;
-  L.iptr = p; p += a.E + 1;
-  L.pload = p; p += a.P + 1;
-  L.slotE = p; p += a.R * a.S;
-  L.slotQ = p; p += a.R * a.S;
-  L.instp = p; p += a.E + a.R * a.S;
-  L.iq = p; p += a.E + a.R * a.S + 1;
-  L.iex = p;
+  L.rmask = reinterpret_cast<unsigned long long*>(lds + t.off[kT_rmask]);
+  L.c = lds + t.off[kT_c];
+  L.H = lds + t.off[kT_H];
+  L.part = lds + t.off[kT_part];
+  L.dom = lds + t.off[kT_dom];
+  L.scal = lds + t.off[kT_scal];
+  L.ok = lds + t.off[kT_ok];
+  L.res = lds + t.off[kT_res];
+  L.mq = lds + t.off[kT_mq];
+  L.iptr = lds + t.off[kT_iptr];
+  L.pload = lds + t.off[kT_pload];
+  L.slotE = lds + t.off[kT_slotE];
+  L.slotQ = lds + t.off[kT_slotQ];
+  L.instp = lds + t.off[kT_instp];
+  L.iq = lds + t.off[kT_iq];
+  L.iex = lds + t.off[kT_iex];
   return L;
 }
 
@@ -622,45 +598,42 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
   return false;
 }
 
-// Tile ordinal bases for the experts [e0, e0 + ew) of one layer: base[t][e]
+// Tile ordinal bases for the experts of tile-base workgroup `role` (see
+// scan_thread) of one layer: base[t][e]
 // = number of pairs of e in tiles before t.  Thread (el, ch) sums a
 // contiguous run of tiles of one expert, the runs are scanned in LDS, and the
 // run is re-read and written out as running prefixes.  Loads go in batches
 // of 16 with clamped indices so each batch is one round trip.
 __device__ void tile_base_scan(const uint16_t* __restrict__ hist, int32_t* __restrict__ base,
-                               int32_t ntiles, int32_t E, int32_t e0, int32_t ew, int32_t* part) {
+                               int32_t ntiles, int32_t E, int32_t role, int32_t ew, int32_t* part) {
   const int32_t hs = hist_stride(E);
-  constexpr int B = 16;
+  constexpr int B = kScanBatch;
   const int tid = threadIdx.x;
-  const int nch = kPlanThreads / ew;
-  const int el = tid % ew, ch = tid / ew;
-  const bool act = ch < nch && e0 + el < E && ntiles > 0;
-  const int clen = (ntiles + nch - 1) / nch;
-  const int t0 = min(ch * clen, ntiles), t1 = min(t0 + clen, ntiles);
-  const int e = e0 + el;
+  const ScanThread th = scan_thread(tid, role, ew, ntiles, E);
+  const int e = th.e;
   int32_t sum = 0;
-  if (act) {
-    for (int tb = t0; tb < t1; tb += B) {
+  if (th.act) {
+    for (int tb = th.t0; tb < th.t1; tb += B) {
       int32_t x[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * hs + e];
+      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(scan_row(tb, u, ntiles)) * hs + e];
 #pragma unroll
       for (int u = 0; u < B; ++u)
-        if (tb + u < t1) sum += x[u];
+        if (tb + u < th.t1) sum += x[u];
     }
   }
   part[tid] = sum;
   __syncthreads();
-  if (act) {
+  if (th.act) {
     int32_t run = 0;
-    for (int q = 0; q < ch; ++q) run += part[q * ew + el];
-    for (int tb = t0; tb < t1; tb += B) {
+    for (int q = 0; q < th.ch; ++q) run += part[q * ew + th.el];
+    for (int tb = th.t0; tb < th.t1; tb += B) {
       int32_t x[B];
 #pragma unroll
-      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(min(tb + u, ntiles - 1)) * hs + e];
+      for (int u = 0; u < B; ++u) x[u] = hist[static_cast<int64_t>(scan_row(tb, u, ntiles)) * hs + e];
 #pragma unroll
       for (int u = 0; u < B; ++u)
-        if (tb + u < t1) {
+        if (tb + u < th.t1) {
           base[static_cast<int64_t>(tb + u) * E + e] = run;
           run += x[u];
         }
@@ -677,19 +650,17 @@ __device__ void tile_base_scan(const uint16_t* __restrict__ hist, int32_t* __res
 // aligned base.  The chunk sums meet in LDS.
 template <int W, int B>
 __device__ void sum_hist_rows(const uint16_t* __restrict__ H, int hs, int ntiles, int E, int32_t* c) {
-  const int tid = threadIdx.x;
-  const int nq = hs / (2 * W);
-  const int nch = kPlanThreads / nq;
-  const int q = tid % nq, ch = tid / nq;
-  if (ch >= nch || ntiles <= 0) return;
+  const SumThread th = sum_thread(threadIdx.x, hs, W, ntiles);
+  if (!th.act) return;
+  const int q = th.q, nch = th.nch;
   int32_t sum[2 * W];
 #pragma unroll
   for (int i = 0; i < 2 * W; ++i) sum[i] = 0;
-  for (int tb = ch; tb < ntiles; tb += B * nch) {
+  for (int tb = th.ch; tb < ntiles; tb += B * nch) {
     uint32_t x[B][W];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
-      const int64_t row = min(tb + u * nch, ntiles - 1);
+      const int64_t row = sum_row(tb, u, nch, ntiles);
       if constexpr (W == 4) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(H + row * hs + 8 * q);
         x[u][0] = v.x; x[u][1] = v.y; x[u][2] = v.z; x[u][3] = v.w;
@@ -723,15 +694,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
                                                             int32_t* __restrict__ plans,
                                                             PlanParams a) {
   extern __shared__ __align__(16) int32_t lds[];
-  const int group = 1 + a.scan_wgs;
-  const int layer = blockIdx.x / group;
-  const int role = blockIdx.x % group;
+  const PlanRole pr = plan_role(blockIdx.x, a.scan_wgs);
+  const int layer = pr.layer;
   const int E = a.E, R = a.R, S = a.S, D = a.D, M = a.M, P = a.P;
   const int32_t hs = hist_stride(E);
   const uint16_t* H = hist + static_cast<int64_t>(layer) * a.ntiles * hs;
-  if (role > 0) {
-    const int e0 = (role - 1) * a.scan_ew;
-    tile_base_scan(H, tile_base + static_cast<int64_t>(layer) * a.ntiles * E, a.ntiles, E, e0,
+  if (pr.role > 0) {
+    tile_base_scan(H, tile_base + static_cast<int64_t>(layer) * a.ntiles * E, a.ntiles, E, pr.role,
                    a.scan_ew, lds);
     return;
   }
@@ -748,11 +717,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
   // -- phase 0: pairs per expert = sum of the tile histograms.
   for (int e = tid; e < E; e += kPlanThreads) L.c[e] = 0;
   __syncthreads();
-  if (hs % 8 == 0 && (reinterpret_cast<uintptr_t>(H) & 15) == 0) {
-    const int rows = (a.ntiles + kPlanThreads / (hs / 8) - 1) / (kPlanThreads / (hs / 8));
-    if (rows <= 4)
+  if (sum_vector_form(hs, reinterpret_cast<uintptr_t>(H))) {
+    const int batch = sum_batch(hs, a.ntiles);
+    if (batch == 4)
       sum_hist_rows<4, 4>(H, hs, a.ntiles, E, L.c);
-    else if (rows <= 8)
+    else if (batch == 8)
       sum_hist_rows<4, 8>(H, hs, a.ntiles, E, L.c);
     else
       sum_hist_rows<4, 16>(H, hs, a.ntiles, E, L.c);
@@ -935,12 +904,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     // pairs of e from rank r's tiles, eight loads in flight at a time
     int32_t own = 0;
     const int t1 = (r + 1) * a.tpr;
-    for (int t0 = r * a.tpr; t0 < t1; t0 += 8) {
-      int32_t x[8];
+    for (int t0 = r * a.tpr; t0 < t1; t0 += kLocalBatch) {
+      int32_t x[kLocalBatch];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = H[static_cast<int64_t>(min(t0 + u, t1 - 1)) * hs + e];
+      for (int u = 0; u < kLocalBatch; ++u) x[u] = H[static_cast<int64_t>(local_row(t0, u, t1)) * hs + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) own += t0 + u < t1 ? x[u] : 0;
+      for (int u = 0; u < kLocalBatch; ++u) own += t0 + u < t1 ? x[u] : 0;
     }
     inst_local[i] = min(q, own);
   }
@@ -1978,14 +1947,15 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
                                                      const float* __restrict__ w, int32_t L,
                                                      int32_t N, int32_t* __restrict__ inv,
                                                      float* __restrict__ w_perm) {
-  const int32_t stride = gridDim.x * blockDim.x;
+  // 64-bit index: N may come within a stride of 2^31
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int32_t layer = 0; layer < L; ++layer) {
     const int64_t lb = static_cast<int64_t>(layer) * N;
-    for (int32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < N; i += stride) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < N; i += stride) {
       const int32_t p = __builtin_nontemporal_load(pos + lb + i);
       const float wt = __builtin_nontemporal_load(w + lb + i);
       if (p >= 0 && p < N) {
-        inv[lb + p] = i;
+        inv[lb + p] = static_cast<int32_t>(i);
         w_perm[lb + p] = wt;
       }
     }
@@ -2160,13 +2130,10 @@ hipError_t launch_plan_m(int M, const PlanParams& pp, int32_t L, size_t lds, con
   return launch_plan_t<16, SMAX>(pp, L, lds, hist, tbase, plans, st);
 }
 
-// Grid quotas per probe round: enough (quota, domain) items for one wave
-// per SIMD.  More probe waves than SIMDs only share issue slots: the probes
-// of a round run in lock step, and the first one usually succeeds.
 void plan_rounds(const Shape& sh, int32_t* G, int32_t* items) {
-  constexpr int kSimds = 4;
-  *G = sh.ndom < kSimds ? kSimds / sh.ndom : 1;
-  *items = *G * sh.ndom;
+  const PlanRounds pr = plan_rounds_of(sh.ndom);
+  *G = pr.G;
+  *items = pr.items;
 }
 
 // Waves per reroute workgroup: the most whose per-wave grouping tables still
@@ -2323,12 +2290,10 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den; pp.min_tokens = sh.min_tokens;
   pp.rec_words = sh.lay.words;
   plan_rounds(sh, &pp.G, &pp.items);
-  // scan workgroups: enough that each thread's run of tiles is about one
-  // batch of loads, at most one per expert
   {
-    const int64_t ew = ntiles > 0 ? (16ll * kPlanThreads) / ntiles : sh.E;
-    pp.scan_ew = static_cast<int32_t>(ew < 1 ? 1 : (ew > sh.E ? sh.E : ew));
-    pp.scan_wgs = ntiles > 0 ? (sh.E + pp.scan_ew - 1) / pp.scan_ew : 0;
+    const PlanGrid g = plan_grid(sh.E, ntiles);
+    pp.scan_ew = g.scan_ew;
+    pp.scan_wgs = g.scan_wgs;
   }
   for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
     pp.off[f] = sh.lay.off[f];
