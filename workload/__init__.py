@@ -5,10 +5,10 @@ arithmetic (no counting, planning, rerouting, permuting or folding), so the
 CPU oracle and the HIP path can both be fed from it without sharing any of
 the computation they are compared on.
 
-The pages give no dataset for this path: the project README's "Tests"
-section describes single-GPU solving runs on synthesized Zipf-distributed
-expert loads at target rank-level imbalance ratios, and these generators play
-that role.  The five workloads below follow the routing shapes named there
+The pages give no dataset for this path.  The project README's "Tests"
+section runs its solver on one GPU over made-up, Zipf-skewed expert loads
+tuned to chosen max/mean rank imbalances; these generators stand in for
+those inputs.  The five workloads below follow the routing shapes named there
 (256 experts, top-8, EP64, 8k tokens per rank) and the model scales the news
 pages list (106B to 671B parameter MoE models, EP40/EP64 prefill).
 
