@@ -150,7 +150,8 @@ def quota_grid(total: int, H: List[int], R: int, D: int, eps_num: int, eps_den: 
 
 
 def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
-             allow_zero_master: bool = False) -> Optional[Dict[int, List[Tuple[int, int]]]]:
+             allow_zero_master: bool = False,
+             min_tokens: int = 1) -> Optional[Dict[int, List[Tuple[int, int]]]]:
     """Try to bring every rank's load to at most Q with <= S replicas per rank.
 
     Returns, per rank, the replicas it hosts as (expert, quota) in arrival
@@ -176,7 +177,19 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
        c. else fill the roomiest receiver and queue the remainder;
        d. else fail.
        Every step fills one slot, so a domain takes at most D*S steps.
+
+    Minimum tokens per replica m ([README] "Replication planning": a replica
+    is allocated at least a minimal load; R34).  Every amount the greedy
+    moves is at least m: a shed piece below m is raised to m when its expert
+    has room for m (the rank then ends below Q) and dropped when it has not;
+    a receiver takes part of a piece only with a spare of at least m, and a
+    queued piece serves as chain donor only with room for m more; a partial
+    placement leaves at least m queued (the roomiest receiver takes
+    min(spare, a - m), skipped in a chain when that is below m; the donor's
+    part is cut so the rest is 0 or at least m); a placement below m fails
+    the probe.  With m = 1 every rule is the plain greedy's.
     """
+    m = max(1, int(min_tokens))
     M = E // R
     H = [sum(c[r * M:(r + 1) * M]) for r in range(R)]
 
@@ -193,10 +206,15 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
             if X <= 0:
                 continue
             for e in sorted(range(r * M, (r + 1) * M), key=lambda f: (-c[f], f)):
-                t = min(X, c[e] - keep(e))
+                if X <= 0:
+                    break
+                avail = c[e] - keep(e)
+                t = min(X, avail)
+                if t < m:                      # a piece is never below the minimum
+                    t = m if avail >= m else 0
                 if t > 0:
                     piece[e] = t
-                    room[e] = c[e] - keep(e) - t
+                    room[e] = avail - t
                     X -= t
             if X > 0:
                 return None
@@ -204,7 +222,7 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
         free = {r: S for r in ranks}
 
         def place(e: int, r: int, x: int) -> None:
-            assert x > 0 and free[r] > 0
+            assert x >= m and free[r] > 0
             hosted[r].append((e, x))
             free[r] -= 1
 
@@ -216,24 +234,29 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
             def elig(r: int) -> bool:
                 return r != home and free[r] > 0 and all(x != e for x, _ in hosted[r])
 
-            rec = [r for r in ranks if elig(r) and spare[r] > 0]
+            rec = [r for r in ranks if elig(r) and spare[r] >= m]
             fit = [r for r in rec if spare[r] >= a]
             if fit:
                 r = min(fit, key=lambda q: (spare[q], q))
                 place(e, r, a)
                 spare[r] -= a
                 continue
-            don = [f for f in piece if elig(f // M) and room[f] > 0]
+            don = [f for f in piece if elig(f // M) and room[f] >= m]
             if don:
                 f = max(don, key=lambda g: (piece[g], -g))
                 if rec:
                     r2 = max(rec, key=lambda q: (spare[q], -q))
                     assert r2 != f // M
-                    x = spare[r2]
-                    place(e, r2, x)
-                    spare[r2] = 0
-                    a -= x
+                    x = min(spare[r2], a - m)
+                    if x >= m:
+                        place(e, r2, x)
+                        spare[r2] -= x
+                        a -= x
                 x = min(a, room[f])
+                if 0 < a - x < m:              # what stays queued is at least m
+                    x = a - m
+                if x < m:
+                    return None
                 place(e, f // M, x)
                 piece[f] += x
                 room[f] -= x
@@ -242,9 +265,11 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
                     piece[e] = a
             elif rec:
                 r = max(rec, key=lambda q: (spare[q], -q))
-                x = spare[r]
+                x = min(spare[r], a - m)
+                if x < m:
+                    return None
                 place(e, r, x)
-                spare[r] = 0
+                spare[r] -= x
                 piece[e] = a - x
             else:
                 return None
@@ -263,9 +288,9 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     [start_i, start_i + quota_i) of that expert's pairs, cumulatively.
 
     [README] "Replication planning": a minimal load is allocated to a
-    replica (default 1024 there).  Read as (R34): a replica the greedy gives
-    fewer than ``min_tokens`` pairs is not created; its slot stays empty and
-    its pairs stay with the expert's master (so that rank may end above Q*).
+    replica (default 1024 there).  ``feasible`` enforces it inside the greedy
+    (R34), so Q* is the first grid quota reachable with every replica at
+    ``min_tokens`` pairs or more, and every rank still ends at Q* or below.
     The default 1 changes nothing.
     """
     if E % R or R % D or S < 0:
@@ -277,7 +302,7 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     H = [sum(c[r * M:(r + 1) * M]) for r in range(R)]
     grid, Q_lb, Q_max, tol, floor = quota_grid(total, H, R, D, eps_num, eps_den, thr_num, thr_den)
     for gi, Q in enumerate(grid):
-        hosted = feasible(c, Q, E, R, S, D, allow_zero_master)
+        hosted = feasible(c, Q, E, R, S, D, allow_zero_master, min_tokens)
         if hosted is not None:
             break
     assert hosted is not None, "no replication at Q_max must always be feasible"
@@ -286,8 +311,6 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     slot_quota = np.zeros(R * S, dtype=np.int64)
     for r in range(R):
         for s, (e, x) in enumerate(hosted[r]):
-            if x < min_tokens:
-                continue
             slot_expert[r * S + s] = e
             slot_quota[r * S + s] = x
     master_quota = np.array(c, dtype=np.int64)

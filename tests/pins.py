@@ -146,8 +146,7 @@ def check_plan_invariants(pl, c, allow_zero_master=False, min_tokens=1):
     assert pl.phys_load.sum() == pl.total
     assert pl.phys_off[0] == 0 and np.array_equal(np.diff(pl.phys_off), pl.phys_load)
     assert np.array_equal(pl.rank_after, pl.phys_load.reshape(R, M + S).sum(axis=1))
-    if min_tokens <= 1:
-        assert int(pl.rank_after.max(initial=0)) <= pl.Q_star
+    assert int(pl.rank_after.max(initial=0)) <= pl.Q_star
     # instances: each expert's master plus its replicas, ascending physical id
     for e in range(E):
         inst = pl.instances(e)

@@ -26,7 +26,13 @@ MUTATIONS = [
     ("ordinal off by one", 'run_start = np.searchsorted(key[order], key[order], side="left")',
      'run_start = np.searchsorted(key[order], key[order], side="right")'),
     ("no domain floor", "Q_lb = min(max(Q_mean, floor), Q_max)", "Q_lb = min(Q_mean, Q_max)"),
-    ("minimum tokens ignored", "            if x < min_tokens:\n                continue", "            if x < 0:\n                continue"),
+    ("minimum ignored", "    m = max(1, int(min_tokens))", "    m = 1"),
+    ("minimum: small shed dropped, not raised", "t = m if avail >= m else 0", "t = 0"),
+    ("minimum: fill takes the whole spare", "                x = min(spare[r], a - m)\n                if x < m:",
+     "                x = spare[r]\n                if x < m:"),
+    ("minimum: chain fill takes the whole spare", "x = min(spare[r2], a - m)", "x = spare[r2]"),
+    ("minimum: donor may leave less than the minimum",
+     "                if 0 < a - x < m:              # what stays queued is at least m\n                    x = a - m\n", ""),
     ("target ignored", "Q_mean = _ceil_div(total * thr_num, R * thr_den)", "Q_mean = _ceil_div(total, R)"),
     ("tolerance not per rank", "tol = max(1, (total * eps_num) // (R * eps_den))",
      "tol = max(1, (total * eps_num) // eps_den)"),
@@ -87,6 +93,7 @@ PIN_SUBSET = [
     (P.test_plan_uniform_home_load, {}),
     (P.test_plan_threshold_stops_at_the_target, {"which": 1, "thr": (105, 100)}),
     (P.test_plan_minimum_tokens_per_replica, {"cfg": 2, "mt": 1024}),
+    (P.test_plan_minimum_single_hot_expert_wraps, {"N": 50, "R": 8, "m": 6}),
     (P.test_plan_no_replication_possible, {"seed": 0, "S": 0, "D": 4}),
     (P.test_plan_invariants_random_shapes, {"seed": 3}),
     (P.test_layout_properties_workloads, {"cfg": 1, "layer": 0}),

@@ -404,21 +404,65 @@ def test_plan_threshold_stops_at_the_target(which, thr):
 @pytest.mark.parametrize("cfg", [2, 6, 8])
 @pytest.mark.parametrize("mt", [1024, 4096])
 def test_plan_minimum_tokens_per_replica(cfg, mt):
-    """Every replica carries at least the minimum; the replicas kept are the
-    unconstrained plan's replicas that reach it, in the same slots; the rest
-    of their expert's pairs stay with its master; a minimum above every
-    replica's quota replicates nothing."""
+    """[README] "Replication planning": a replica gets at least a minimal
+    load.  Every replica carries at least the minimum, every rank still
+    ends at Q* or below, the earlier grid quotas are out of the greedy's
+    reach under the same minimum, and a minimum above every expert's load
+    replicates nothing (Q* is then the max home load)."""
     w = W.CONFIGS[cfg]
     idx, _, _ = W.routing(w)
     c, _ = O.count(idx, w.E)
-    free = _plan_of(c, w.E, w.R, w.S, w.D)
     pl = O.plan(c, w.E, w.R, w.S, w.D, min_tokens=mt)
     check_plan_invariants(pl, c, False, mt)
-    keep = free.slot_quota >= mt
-    assert np.array_equal(pl.slot_expert, np.where(keep, free.slot_expert, -1))
-    assert pl.Q_star == free.Q_star
-    dropped = np.bincount(free.slot_expert[~keep & (free.slot_expert >= 0)],
-                          weights=free.slot_quota[~keep & (free.slot_expert >= 0)], minlength=w.E)
-    assert np.array_equal(pl.master_quota, free.master_quota + dropped.astype(np.int64))
-    top = O.plan(c, w.E, w.R, w.S, w.D, min_tokens=int(free.slot_quota.max()) + 1)
-    assert top.n_replicas == 0
+    assert (pl.slot_quota[pl.slot_expert >= 0] >= mt).all()
+    assert pl.imbalance_after() <= 1.04
+    grid, *_ = O.quota_grid(pl.total, pl.rank_before.tolist(), w.R, w.D, 1, 100)
+    for Q in grid[:pl.grid_index]:
+        assert O.feasible([int(x) for x in c], Q, w.E, w.R, w.S, w.D, min_tokens=mt) is None
+    top = O.plan(c, w.E, w.R, w.S, w.D, min_tokens=int(c.max()) + 1)
+    assert top.n_replicas == 0 and top.Q_star == top.Q_max
+
+
+def _wrap_with_minimum(N, R, m):
+    """One hot expert wrapped over the other ranks (McNaughton's rule) with
+    a minimum m per replica, worked out directly: at quota Q the home rank
+    sheds a = N - Q pairs (raised to m when fewer, which leaves it below Q);
+    every other rank has spare Q, so each takes a whole Q while at least m
+    would remain after it, else all but m, and the last part fits whole.  A
+    part below m, or more parts than other ranks, rules Q out."""
+    Q = -(-N // R)
+    while True:
+        if Q >= N:
+            return Q, []
+        a = max(N - Q, m)
+        parts = []
+        while a > Q:
+            part = Q if a - Q >= m else a - m
+            if part < m:
+                break
+            parts.append(part)
+            a -= part
+        else:
+            parts.append(a)
+            if len(parts) <= R - 1:
+                return Q, parts
+        Q += 1
+
+
+@pytest.mark.parametrize("N,R,m", [(77, 5, 1), (77, 5, 10), (77, 5, 15), (50, 8, 6), (50, 8, 7),
+                                   (30, 4, 8), (100, 3, 40), (23, 6, 5), (40, 5, 9), (9, 4, 3)])
+def test_plan_minimum_single_hot_expert_wraps(N, R, m):
+    """k = 1, every pair on expert 0, one expert and one slot per rank,
+    D = R: the plan is the wrap above (Q* the first quota it allows, the
+    replicas on ranks 1, 2, ... in order)."""
+    assert N < 100 * R  # grid step 1
+    c = np.zeros(R, dtype=np.int64)
+    c[0] = N
+    Q, parts = _wrap_with_minimum(N, R, m)
+    pl = O.plan(c, R, R, 1, R, min_tokens=m)
+    assert pl.Q_star == Q
+    want = np.full(R, -1)
+    want[1:1 + len(parts)] = 0
+    assert pl.slot_expert.tolist() == want.tolist()
+    assert pl.slot_quota[1:1 + len(parts)].tolist() == parts
+    check_plan_invariants(pl, c, False, m)
