@@ -107,9 +107,16 @@ typedef struct ultraep_ctx ultraep_ctx;
  *   instance's layout rows hold its local pairs (pair order), then the rest
  *   (in the order dealt), and a fused layout is written by a scatter pass.
  * min_tokens_per_replica ([README] "Replication planning": the minimal load
- *   allocated to a replica; 0 means 1): a replica the greedy gives fewer
- *   pairs is not created, its slot stays empty and its pairs stay with the
- *   expert's master (whose rank may then end above Q*). */
+ *   allocated to a replica; 0 means 1): m, a rule of the greedy (step 3 of
+ *   ultraep_balance), so every replica serves at least m pairs and every
+ *   rank still ends at Q* or below.  Every amount the greedy moves is at
+ *   least m: a shed piece below m is raised to m when its expert has room
+ *   for m (the rank then ends below Q) and is not shed when it has not;
+ *   only receivers with spare >= m and donors with room >= m more take part
+ *   of a piece; a split leaves at least m queued (the roomiest receiver
+ *   takes min(spare, piece - m), skipped in a chain when below m; the
+ *   donor's part is cut so that 0 or at least m stays queued); a placement
+ *   below m fails the probe.  m = 1 is the plain greedy. */
 #define ULTRAEP_REROUTE_RANGES 0
 #define ULTRAEP_REROUTE_LOCAL 1
 #define ULTRAEP_REROUTE_INTERLEAVE 2

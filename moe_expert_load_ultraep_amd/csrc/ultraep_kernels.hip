@@ -299,6 +299,7 @@ template <int MMAX>
 __device__ bool shed_pieces(int32_t Q, bool act, int r, int32_t Hr, const PlanParams& a,
                             const PlanLds& L, int32_t (&pa)[MMAX], int32_t (&room)[MMAX]) {
   const int M = a.M;
+  const int32_t mt = a.min_tokens;
 #pragma unroll
   for (int j = 0; j < MMAX; ++j) {
     pa[j] = 0;
@@ -322,13 +323,17 @@ __device__ bool shed_pieces(int32_t Q, bool act, int r, int32_t Hr, const PlanPa
         }
       used |= 1u << bj;
       const int32_t keep = (bc > 0 && !a.allow_zero) ? 1 : 0;
-      const int32_t t = min(X, bc - keep);
+      const int32_t avail = bc - keep;
+      int32_t t = min(X, avail);
+      // a piece is never below the minimum: raised to it when the expert
+      // has room (the rank then ends below Q), else not shed
+      if (t < mt) t = (X > 0 && avail >= mt) ? mt : 0;
       if (t > 0) {
 #pragma unroll
         for (int j = 0; j < MMAX; ++j)
           if (j == bj) {
             pa[j] = t;
-            room[j] = bc - keep - t;
+            room[j] = avail - t;
           }
         X -= t;
       }
@@ -343,6 +348,7 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
                              int32_t* res_e, int32_t* res_q) {
   const int lane = lane_id();
   const int D = a.D, M = a.M, S = a.S;
+  const int32_t mt = a.min_tokens;
   const bool act = lane < D;
   const int r = d * D + lane;
   const int32_t Hr = act ? L.H[r] : 0;
@@ -407,16 +413,19 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
     // piece gets the top bit and the inverted spare (the largest key is the
     // tightest fit, ties to the lowest lane); otherwise the key is the spare
     // itself (the largest key is the roomiest receiver).
-    const uint32_t key = (elig && spare > 0)
+    // (a receiver needs a spare of at least the minimum; a whole piece is
+    // never below it, so a fit always has that much)
+    const uint32_t key = (elig && spare >= mt)
                              ? (spare >= amt ? (0x80000000u | (0x7FFFFFFFu - static_cast<uint32_t>(spare)))
                                              : static_cast<uint32_t>(spare))
                              : 0u;
-    // donor: largest queued piece on an eligible rank with room left
+    // donor: largest queued piece on an eligible rank with room for the
+    // minimum more
     uint32_t dbest = 0;
     int dj = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
-      const bool cand = elig && pa[j] > 0 && room[j] > 0 && static_cast<uint32_t>(pa[j]) > dbest;
+      const bool cand = elig && pa[j] > 0 && room[j] >= mt && static_cast<uint32_t>(pa[j]) > dbest;
       dbest = cand ? static_cast<uint32_t>(pa[j]) : dbest;
       dj = cand ? j : dj;
     }
@@ -429,20 +438,26 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
       continue;
     }
     const uint32_t rmax = kmax;  // roomiest receiver's spare (0: none)
+    // the roomiest receiver's part leaves at least the minimum queued and
+    // is not placed below it
+    int32_t part = min(static_cast<int32_t>(rmax), amt - mt);
+    part = part < mt ? 0 : part;
     if (dmax > 0) {              // chain through the donor's rank
       const int dl = lowest_lane(ballot(dbest == dmax));
       const int djs = static_cast<int>(readlane(static_cast<uint32_t>(dj), dl));
-      if (rmax > 0) {
+      if (part > 0) {
         const int r2 = lowest_lane(ballot(key == rmax));
-        place(r2, e, static_cast<int32_t>(rmax));
-        spare = lane == r2 ? 0 : spare;
-        amt -= static_cast<int32_t>(rmax);
+        place(r2, e, part);
+        spare -= lane == r2 ? part : 0;
+        amt -= part;
       }
       int32_t myroom = 0;
 #pragma unroll
       for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
       const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
-      const int32_t x = min(amt, droom);
+      int32_t x = min(amt, droom);
+      if (amt - x > 0 && amt - x < mt) x = amt - mt;  // what stays queued is at least mt
+      if (x < mt) return false;
       place(dl, e, x);
 #pragma unroll
       for (int j = 0; j < MMAX; ++j) {
@@ -451,11 +466,11 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
         room[j] -= here ? x : 0;
       }
       amt -= x;
-    } else if (rmax > 0) {  // fill the roomiest receiver
+    } else if (part > 0) {  // fill the roomiest receiver
       const int r2 = lowest_lane(ballot(key == rmax));
-      place(r2, e, static_cast<int32_t>(rmax));
-      spare = lane == r2 ? 0 : spare;
-      amt -= static_cast<int32_t>(rmax);
+      place(r2, e, part);
+      spare -= lane == r2 ? part : 0;
+      amt -= part;
     } else {
       return false;
     }
@@ -480,6 +495,7 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
   constexpr uint32_t kFitBit = 1u << 25;
   const int lane = lane_id();
   const int D = a.D, M = a.M, S = a.S;
+  const int32_t mt = a.min_tokens;
   const bool act = lane < D;
   const int r = d * D + lane;
   const int32_t Hr = act ? L.H[r] : 0;
@@ -550,28 +566,38 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     const bool elig = !mine && nh < S && !hosts;
     const uint32_t core = spare >= amt ? (kFitBit | (kFitBit - 1 - static_cast<uint32_t>(spare)))
                                        : static_cast<uint32_t>(spare);
-    const uint32_t key = (elig && spare > 0) ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
+    // receivers need a spare of at least the minimum (a whole piece is never
+    // below it), donors room for the minimum more
+    const uint32_t key = (elig && spare >= mt) ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
     uint32_t dk = 0, qn = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
       // the popped piece is out of the queue for this step
       const uint32_t kj = (mine && j == jsel) ? 0u : qk[j];
       qn = max(qn, kj);
-      dk = max(dk, (elig && room[j] > 0) ? kj : 0u);
+      dk = max(dk, (elig && room[j] >= mt) ? kj : 0u);
     }
     uint32_t kmax = key, dmax = dk, knext = qn;
     wave_max3_bcast(kmax, dmax, knext);
     const bool fit = (kmax & (kFitBit << 6)) != 0;
-    if (!fit && kmax == 0 && dmax == 0) return false;
     const int kl = 63 - static_cast<int>(kmax & 63);
-    const int32_t r_amt = fit ? amt : static_cast<int32_t>(kmax >> 6);
+    // without a fit the roomiest receiver takes its spare, but leaves at
+    // least the minimum queued and takes nothing below it; the donor's part
+    // is cut so that what stays queued is 0 or at least the minimum
+    int32_t r_amt = fit ? amt : min(static_cast<int32_t>(kmax >> 6), amt - mt);
+    r_amt = (!fit && r_amt < mt) ? 0 : r_amt;
     const uint32_t dt = TMASK - (dmax & TMASK);
     const int dl = static_cast<int>(dt / MMAX) & 63, djs = static_cast<int>(dt % MMAX);
     int32_t myroom = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
     const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
-    const int32_t x = (!fit && dmax > 0) ? min(amt - r_amt, droom) : 0;
+    const bool chain = !fit && dmax > 0;
+    const int32_t rest = amt - r_amt;
+    int32_t x = min(rest, droom);
+    x = (rest - x > 0 && rest - x < mt) ? rest - mt : x;
+    x = chain ? x : 0;
+    if ((!fit && r_amt == 0 && dmax == 0) || (chain && x < mt)) return false;
     const int32_t left = amt - r_amt - x;
     const bool rcv = lane == kl, don = lane == dl;
     const int32_t give = (rcv ? r_amt : 0) + (don ? x : 0);
@@ -822,9 +848,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
       const int item = (winner - wg0) * a.ndom + d;
       e = L.res[static_cast<size_t>(item) * D * S + lr * S + j];
       q = L.res[static_cast<size_t>(a.items + item) * D * S + lr * S + j];
-      // a replica below the minimum is not created: its pairs stay with
-      // the master (the master quota below is what the slots leave)
-      if (e >= 0 && q < a.min_tokens) e = -1;
     }
     L.slotE[s] = e;
     L.slotQ[s] = e >= 0 ? q : 0;

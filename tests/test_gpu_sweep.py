@@ -53,6 +53,8 @@ def sweep_case(i):
         opts["thr_num"], opts["thr_den"] = [(101, 100), (11, 10), (3, 2)][int(rng.integers(3))]
     if rng.random() < 0.2:
         opts["eps_num"], opts["eps_den"] = [(0, 1), (1, 20), (1, 1000)][int(rng.integers(3))]
+    if rng.random() < 0.25:
+        opts["min_tokens"] = int(rng.choice([2, 3, 8, 50, 400]))
     return dict(E=E, R=R, S=S, D=D, k=k, T=T, idx=idx.reshape(R * T, k), wt=wt.reshape(R * T, k),
                 opts=opts)
 
@@ -62,7 +64,8 @@ def _ctx(c, mode):
     return U.ultraep_create(c["E"], c["R"], c["S"], c["D"],
                             eps=(o.get("eps_num", 1), o.get("eps_den", 100)),
                             allow_zero_master=o["allow_zero_master"],
-                            threshold=(o.get("thr_num", 1), o.get("thr_den", 1)), reroute_mode=mode)
+                            threshold=(o.get("thr_num", 1), o.get("thr_den", 1)), reroute_mode=mode,
+                            min_tokens=o.get("min_tokens", 1))
 
 
 @pytest.mark.parametrize("chunk", range(CHUNKS))
@@ -73,7 +76,7 @@ def test_random_shape_sweep(chunk):
         E, R, S, D, k, T = c["E"], c["R"], c["S"], c["D"], c["k"], c["T"]
         tag = f"case {i}: E={E} R={R} S={S} D={D} k={k} T={T} opts={c['opts']}"
         pl, _, _ = O.balance(c["idx"], E, R, S, D, **c["opts"])
-        check_plan_invariants(pl, pl.c, c["opts"]["allow_zero_master"])
+        check_plan_invariants(pl, pl.c, c["opts"]["allow_zero_master"], c["opts"].get("min_tokens", 1))
         for mode in (0, 1, 2):
             ctx = _ctx(c, mode)
             got = run_balance(ctx, c["idx"][None], c["wt"][None], T, k, fused=(i + mode) % 3 != 0)
