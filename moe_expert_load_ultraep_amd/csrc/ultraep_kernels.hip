@@ -484,7 +484,10 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
 
 constexpr int ilog2_c(int x) { return x <= 1 ? 0 : 1 + ilog2_c(x / 2); }
 
-template <int MMAX, int SMAX>
+// MIN: a minimum above one pair per replica is in force.  Without it the
+// step is compiled without the minimum's rules (each one is then a no-op),
+// so the common case keeps the shortest dependent chain.
+template <int MMAX, int SMAX, bool MIN>
 __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const PlanLds& L,
                                     int32_t* res_e, int32_t* res_q) {
   // queue keys: pairs << TB | (TMASK - (lane * MMAX + j)); the largest key
@@ -495,7 +498,7 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
   constexpr uint32_t kFitBit = 1u << 25;
   const int lane = lane_id();
   const int D = a.D, M = a.M, S = a.S;
-  const int32_t mt = a.min_tokens;
+  const int32_t mt = MIN ? a.min_tokens : 1;
   const bool act = lane < D;
   const int r = d * D + lane;
   const int32_t Hr = act ? L.H[r] : 0;
@@ -568,36 +571,47 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
                                        : static_cast<uint32_t>(spare);
     // receivers need a spare of at least the minimum (a whole piece is never
     // below it), donors room for the minimum more
-    const uint32_t key = (elig && spare >= mt) ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
+    const uint32_t key = (elig && (MIN ? spare >= mt : spare > 0))
+                             ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
     uint32_t dk = 0, qn = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
       // the popped piece is out of the queue for this step
       const uint32_t kj = (mine && j == jsel) ? 0u : qk[j];
       qn = max(qn, kj);
-      dk = max(dk, (elig && room[j] >= mt) ? kj : 0u);
+      dk = max(dk, (elig && (MIN ? room[j] >= mt : room[j] > 0)) ? kj : 0u);
     }
     uint32_t kmax = key, dmax = dk, knext = qn;
     wave_max3_bcast(kmax, dmax, knext);
     const bool fit = (kmax & (kFitBit << 6)) != 0;
+    int32_t r_amt, x;
     const int kl = 63 - static_cast<int>(kmax & 63);
-    // without a fit the roomiest receiver takes its spare, but leaves at
-    // least the minimum queued and takes nothing below it; the donor's part
-    // is cut so that what stays queued is 0 or at least the minimum
-    int32_t r_amt = fit ? amt : min(static_cast<int32_t>(kmax >> 6), amt - mt);
-    r_amt = (!fit && r_amt < mt) ? 0 : r_amt;
     const uint32_t dt = TMASK - (dmax & TMASK);
     const int dl = static_cast<int>(dt / MMAX) & 63, djs = static_cast<int>(dt % MMAX);
     int32_t myroom = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
     const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
-    const bool chain = !fit && dmax > 0;
-    const int32_t rest = amt - r_amt;
-    int32_t x = min(rest, droom);
-    x = (rest - x > 0 && rest - x < mt) ? rest - mt : x;
-    x = chain ? x : 0;
-    if ((!fit && r_amt == 0 && dmax == 0) || (chain && x < mt)) return false;
+    if constexpr (MIN) {
+      // without a fit the roomiest receiver takes its spare, but leaves at
+      // least the minimum queued and takes nothing below it; the donor's
+      // part is cut so that what stays queued is 0 or at least the minimum
+      // (bitwise logic: short-circuit tests let the compiler sink the donor
+      // and queue reductions behind the receiver's)
+      r_amt = fit ? amt : min(static_cast<int32_t>(kmax >> 6), amt - mt);
+      r_amt = (!fit & (r_amt < mt)) ? 0 : r_amt;
+      const bool chain = !fit & (dmax > 0);
+      const int32_t rest = amt - r_amt;
+      x = min(rest, droom);
+      x = ((rest - x > 0) & (rest - x < mt)) ? rest - mt : x;
+      x = chain ? x : 0;
+      if ((!fit & (r_amt == 0) & (dmax == 0)) | (chain & (x < mt))) return false;
+    } else {
+      // the receiver takes the whole piece on a fit, else its whole spare
+      if (!fit && kmax == 0 && dmax == 0) return false;
+      r_amt = fit ? amt : static_cast<int32_t>(kmax >> 6);
+      x = (!fit && dmax > 0) ? min(amt - r_amt, droom) : 0;
+    }
     const int32_t left = amt - r_amt - x;
     const bool rcv = lane == kl, don = lane == dl;
     const int32_t give = (rcv ? r_amt : 0) + (don ? x : 0);
@@ -818,9 +832,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
         int32_t* re = L.res + static_cast<size_t>(item) * D * S;
         int32_t* rq = L.res + static_cast<size_t>(a.items + item) * D * S;
         constexpr uint32_t kPieceLimit = 1u << (26 - ilog2_c(MMAX));
-        okv = (static_cast<uint32_t>(cmax) < kPieceLimit && Q < (1 << 25))
-                  ? greedy_probe_packed<MMAX, SMAX>(Q, d, a, L, re, rq)
-                  : greedy_probe<MMAX, SMAX>(Q, d, a, L, re, rq);
+        const bool packed = static_cast<uint32_t>(cmax) < kPieceLimit && Q < (1 << 25);
+        okv = !packed              ? greedy_probe<MMAX, SMAX>(Q, d, a, L, re, rq)
+              : a.min_tokens > 1 ? greedy_probe_packed<MMAX, SMAX, true>(Q, d, a, L, re, rq)
+                                 : greedy_probe_packed<MMAX, SMAX, false>(Q, d, a, L, re, rq);
       }
       if (lane == 0) L.ok[item] = okv ? 1 : 0;
     }
