@@ -15,8 +15,14 @@ one and its roofline is reported against the 8 TB/s HBM peak.
 Beside the timed steps, the balance call is timed warm (back to back on the
 same input) and cold (a 1 GiB scratch write before each repetition evicts the
 256 MB Infinity Cache and the L2s); permute and fold are timed cold the same
-way.  The CPU oracle is timed stage by stage on the host on the same workload
-(cpu_baseline).  Prints ONE JSON line.
+way; every cold figure also comes as mean, median, p99 and max
+(cold_distribution_us).  The balance is timed again at the pages' default
+knobs (locality-aware decomposition with interleave, at least 1024 pairs per
+replica: pages_defaults).  The CPU oracle is timed stage by stage on the host
+on the same workload (cpu_baseline).  Workloads of several layers or
+microbatches also report each instance's max/mean before and after
+(load_trace; --load-trace writes every rank and expert load).  Prints ONE
+JSON line.
 
 Workloads (--config):
   2  single layer, E=128 R=64 S=2 D=64 T=8192 top-8 (the default)
@@ -70,7 +76,13 @@ def parse():
     ap.add_argument("--no-combine", action="store_true",
                     help="skip the combine / combine-backward timing (needs two layout-sized buffers)")
     ap.add_argument("--copy-mib", type=int, default=1024,
-                    help="size of the device-to-device copy that measures the HBM copy ceiling")
+                    help="size of the runtime device-to-device copy timed for context")
+    ap.add_argument("--no-pages-defaults", action="store_true",
+                    help="skip the balance timing at the pages' default knobs (locality with "
+                         "interleave, minimum 1024 pairs per replica)")
+    ap.add_argument("--load-trace", default="",
+                    help="write per-(layer, microbatch) rank and expert loads before and after "
+                         "balancing to this file (JSON lines)")
     return ap.parse_args()
 
 
@@ -107,11 +119,11 @@ def recorded_traffic(config):
     return float(m_val.group(1))
 
 
-def copy_ceiling(torch, dev, mib):
-    """Device-to-device copy rate (read + write bytes / time), the best of a
-    few relative placements of source and destination: the practical HBM
-    ceiling a streaming kernel is compared with.  (The rate of one copy
-    depends on how its two buffers fall on the memory channels.)"""
+def device_copy_rate(torch, dev, mib):
+    """Rate of the runtime's own device-to-device copy (torch copy_, read +
+    write bytes / time), the best of a few relative placements of source
+    and destination.  Context only: it is not a ceiling (the permute kernel
+    moves rows faster than this copy)."""
     n = mib << 20
     pad = 8 << 20
     buf = torch.empty(2 * n + pad, dtype=torch.uint8, device=dev)
@@ -133,6 +145,14 @@ def copy_ceiling(torch, dev, mib):
         best = max(best, 2 * n / (ev[0].elapsed_time(ev[1]) / reps * 1e-3) / 1e9)
     del buf, a, b
     return best
+
+
+def dist_us(ms, per=1):
+    """Mean, median, p99 and max (in µs, divided by per) of a run of timings
+    in ms, so a bimodal or heavy-tailed run shows beside its mean."""
+    us = np.asarray(ms, dtype=np.float64) * 1e3 / per
+    return {"mean": float(us.mean()), "median": float(np.median(us)),
+            "p99": float(np.percentile(us, 99)), "max": float(us.max()), "n": int(us.size)}
 
 
 def host_info():
@@ -443,6 +463,38 @@ def main():
     perm_cold = timed(lambda r: permute(), args.cold_reps, True)
     fold_cold = timed(lambda r: fold(), args.cold_reps, True)
 
+    # ---- the pages' default knobs ([README] "Replication planning": the
+    # locality-aware quota decomposition and the reroute interleave on, and a
+    # minimum of 1024 pairs per replica): the same balance call on the same
+    # inputs, timed cold and warm, with its plan quality and dispatch traffic
+    pdef = None
+    if not args.no_pages_defaults:
+        ctx_p = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr, reroute_mode=U.REROUTE_INTERLEAVE,
+                                 min_tokens=1024)
+        buf_p = U.Buffers(ctx_p, L, w.T, w.k, dev)
+
+        def balance_p(i):
+            U.ultraep_balance(ctx_p, d_idx[i], w.T, w.k, buf_p.workspace, buf_p.plans, buf_p.phys_idx,
+                              buf_p.pos, topk_w=d_w[i], inv=buf_p.inv, w_perm=buf_p.w_perm, L=L)
+
+        plans_p = []
+        for i in range(n_inst):
+            balance_p(i)
+            host = buf_p.plans.cpu().numpy()
+            plans_p.append([ctx_p.decode_plan(host[l]) for l in range(L)])
+        p_cold = timed(lambda r: balance_p(r % n_inst), n_inst if args.config == 4 else args.cold_reps, True)
+        p_warm = timed(lambda r: balance_p(0), args.cold_reps, False)
+        balance_p(0)
+        torch.cuda.synchronize()
+        pdef = {"reroute_mode": U.REROUTE_INTERLEAVE, "min_tokens_per_replica": 1024,
+                "threshold": f"{thr[0]}/{thr[1]}",
+                "balance_reroute_us_per_layer": float(np.mean(p_cold)) * 1e3 / L,
+                "balance_reroute_us_per_layer_warm": float(np.mean(p_warm)) * 1e3 / L,
+                "cold_distribution_us": dist_us(p_cold, L)}
+        pdef.update(quality(ctx_p, [p[l] for p in plans_p for l in range(L)], w))
+        pdef["dispatch_traffic"] = dispatch_traffic(buf_p.phys_idx[0].cpu().numpy(), w)
+        del buf_p
+
     # ---- combine and its backward (after the experts; not part of the step):
     # the tokens of the permuted rank against the whole layout of the first
     # layer, expert outputs and output gradients drawn on the GPU
@@ -478,7 +530,8 @@ def main():
                 "combine_GBps": gbps_fn(cf_bytes, float(np.mean(t_cf))),
                 "combine_backward_us": float(np.mean(t_cb)) * 1e3,
                 "combine_backward_GBps": gbps_fn(cb_bytes, float(np.mean(t_cb))),
-                "combine_bytes": cf_bytes, "combine_backward_bytes": cb_bytes}
+                "combine_bytes": cf_bytes, "combine_backward_bytes": cb_bytes,
+                "cold_distribution_us": {"combine": dist_us(t_cf), "combine_backward": dist_us(t_cb)}}
         comb["combine_frac_of_peak"] = comb["combine_GBps"] / HBM_PEAK_GBPS
         comb["combine_backward_frac_of_peak"] = comb["combine_backward_GBps"] / HBM_PEAK_GBPS
         del x_rows, g_rows, dy, y, gw
@@ -526,7 +579,9 @@ def main():
                  "all_slots_GBps": gbps_fn(b_all, float(np.mean(t_all))),
                  "all_slots_relay_us": float(np.mean(t_rel)) * 1e3,
                  "relayed_slots": int((rel[1] == 2).sum()), "filled_slots": int((rel[1] > 0).sum()),
-                 "rank_slots_bytes": b_rank, "all_slots_bytes": b_all}
+                 "rank_slots_bytes": b_rank, "all_slots_bytes": b_all,
+                 "cold_distribution_us": {"rank_slots": dist_us(t_rank), "all_slots": dist_us(t_all),
+                                          "all_slots_relay": dist_us(t_rel)}}
         wsync["all_slots_frac_of_peak"] = wsync["all_slots_GBps"] / HBM_PEAK_GBPS
         wsync["rank_slots_frac_of_peak"] = wsync["rank_slots_GBps"] / HBM_PEAK_GBPS
         del mast, ptrs, reps_w, relay
@@ -542,7 +597,7 @@ def main():
     fold_b = np.array([fold_bytes[i] for i in step_insts], dtype=np.float64)
     perm_gbps = float(perm_b.sum() / (t_perm.sum() * 1e-3) / 1e9)
     fold_gbps = float(fold_b.sum() / (t_fold.sum() * 1e-3) / 1e9)
-    ceiling = copy_ceiling(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
+    copy_rate = device_copy_rate(torch, dev, args.copy_mib) if args.copy_mib > 0 else None
     bal_cold_us = float(np.mean(bal_cold)) * 1e3 / L
     result = {
         "metric": METRIC,
@@ -577,8 +632,9 @@ def main():
         "fold_GBps": fold_gbps,
         "fold_GBps_cold": gbps(fold_bytes[0], float(np.mean(fold_cold))),
         "fold_frac_of_peak": fold_gbps / HBM_PEAK_GBPS,
-        "hbm_copy_ceiling_GBps": ceiling,
-        "permute_frac_of_copy_ceiling": perm_gbps / ceiling if ceiling else None,
+        "device_copy_GBps": copy_rate,
+        "cold_distribution_us": {"balance_per_layer": dist_us(bal_cold, L), "permute": dist_us(perm_cold),
+                                 "fold": dist_us(fold_cold)},
         "roofline": {"bound": "hbm", "kernel": "permute_kernel", "achieved": perm_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": perm_gbps / HBM_PEAK_GBPS,
                      "traffic": recorded_traffic(args.config),
@@ -603,6 +659,25 @@ def main():
     if args.config == 4 and n_inst > 1:
         stale = [stale_plan_imbalance(plans[i - 1][0], plans[i][0], w) for i in range(1, n_inst)]
         result["stale_plan_imbalance_median_max"] = [float(np.median(stale)), float(np.max(stale))]
+    if pdef is not None:
+        result["pages_defaults"] = pdef
+    # per-(layer, microbatch) loads before and after balancing (the pages'
+    # load profiler records the same per microbatch: [README] "Load profiler
+    # and viewer"): max/mean per instance in the line, every rank and expert
+    # load in --load-trace
+    flat = [(insts[i * L + l], plans[i][l]) for i in range(n_inst) for l in range(L)]
+    if len(flat) > 1:
+        result["load_trace"] = [
+            {"layer": lm[0], "mb": lm[1], "before": float(p["rank_before"].max() * w.R / max(1, p["total"])),
+             "after": float(p["rank_after"].max() * w.R / max(1, p["total"])), "replicas": p["replicas"]}
+            for lm, p in flat]
+    if args.load_trace:
+        with open(args.load_trace, "w") as f:
+            for lm, p in flat:
+                f.write(json.dumps({"layer": lm[0], "mb": lm[1], "expert_load": p["counts"].tolist(),
+                                    "rank_before": p["rank_before"].tolist(),
+                                    "rank_after": p["rank_after"].tolist(),
+                                    "phys_load": p["phys_load"].tolist()}) + "\n")
     if args.config in PAGES_TABLE:
         result["pages_table_context"] = PAGES_TABLE[args.config]
     if not args.no_cpu_baseline:
