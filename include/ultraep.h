@@ -315,7 +315,12 @@ int ultraep_dispatch_layout(const ultraep_ctx* ctx, int32_t L, int64_t T, int32_
 
 /* Gather the bf16 hidden rows of physical experts [p_begin, p_end) of one
  * layer into the layout order (one rank's receive segment when the range is
- * [r*(M+S), (r+1)*(M+S))).
+ * [r*(M+S), (r+1)*(M+S))): the one-GPU form of the dispatch that follows
+ * reroute ([README] Interface, "Forward and backward": the tokens are
+ * dispatched to the physical experts reroute chose, before the grouped
+ * expert GEMM; principles, "Self-contained codebase": UltraEP itself is
+ * independent of the token dispatcher, so this build supplies the row
+ * movement the dispatch needs).
  * In:  plan (one record), inv [N] of that layer, hidden [hidden_rows][H] bf16
  *      (raw 16-bit patterns, never converted)
  * Out: out [rows][H] with rows = phys_off[p_end] - phys_off[p_begin]; row i is
