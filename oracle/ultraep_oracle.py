@@ -150,8 +150,8 @@ def quota_grid(total: int, H: List[int], R: int, D: int, eps_num: int, eps_den: 
 
 
 def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
-             allow_zero_master: bool = False,
-             min_tokens: int = 1) -> Optional[Dict[int, List[Tuple[int, int]]]]:
+             allow_zero_master: bool = False, min_tokens: int = 1,
+             lean: bool = False) -> Optional[Dict[int, List[Tuple[int, int]]]]:
     """Try to bring every rank's load to at most Q with <= S replicas per rank.
 
     Returns, per rank, the replicas it hosts as (expert, quota) in arrival
@@ -188,6 +188,13 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
     min(spare, a - m), skipped in a chain when that is below m; the donor's
     part is cut so the rest is 0 or at least m); a placement below m fails
     the probe.  With m = 1 every rule is the plain greedy's.
+
+    Replica-lean planning (``lean``, R35): step b is left out, so only ranks
+    with spare take replicas; a piece that fits no receiver goes in part to
+    the roomiest one (step c).  Each chain splits a piece over two ranks and
+    grows the donor's piece; without them the large domains need about a
+    third fewer replicas at the same quota, while small ones may need a
+    higher quota.
     """
     m = max(1, int(min_tokens))
     M = E // R
@@ -241,7 +248,7 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
                 place(e, r, a)
                 spare[r] -= a
                 continue
-            don = [f for f in piece if elig(f // M) and room[f] >= m]
+            don = [] if lean else [f for f in piece if elig(f // M) and room[f] >= m]
             if don:
                 f = max(don, key=lambda g: (piece[g], -g))
                 if rec:
@@ -278,7 +285,7 @@ def feasible(c: List[int], Q: int, E: int, R: int, S: int, D: int,
 
 def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
          eps_num: int = 1, eps_den: int = 100, allow_zero_master: bool = False,
-         thr_num: int = 1, thr_den: int = 1, min_tokens: int = 1) -> Plan:
+         thr_num: int = 1, thr_den: int = 1, min_tokens: int = 1, lean: bool = False) -> Plan:
     """Replication plan from the exact per-expert load ([README] Interface /
     "Forward and backward": ``update_placement``).
 
@@ -292,6 +299,8 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     (R34), so Q* is the first grid quota reachable with every replica at
     ``min_tokens`` pairs or more, and every rank still ends at Q* or below.
     The default 1 changes nothing.
+
+    ``lean`` plans without the greedy's chain step (R35; see ``feasible``).
     """
     if E % R or R % D or S < 0:
         raise ValueError("bad shape")
@@ -302,7 +311,7 @@ def plan(c: np.ndarray, E: int, R: int, S: int, D: int, *, dropped: int = 0,
     H = [sum(c[r * M:(r + 1) * M]) for r in range(R)]
     grid, Q_lb, Q_max, tol, floor = quota_grid(total, H, R, D, eps_num, eps_den, thr_num, thr_den)
     for gi, Q in enumerate(grid):
-        hosted = feasible(c, Q, E, R, S, D, allow_zero_master, min_tokens)
+        hosted = feasible(c, Q, E, R, S, D, allow_zero_master, min_tokens, lean)
         if hosted is not None:
             break
     assert hosted is not None, "no replication at Q_max must always be feasible"

@@ -27,6 +27,9 @@ MUTATIONS = [
      'run_start = np.searchsorted(key[order], key[order], side="right")'),
     ("no domain floor", "Q_lb = min(max(Q_mean, floor), Q_max)", "Q_lb = min(Q_mean, Q_max)"),
     ("minimum ignored", "    m = max(1, int(min_tokens))", "    m = 1"),
+    ("lean plan still chains", "don = [] if lean else [f for f in piece", "don = [] if False else [f for f in piece"),
+    ("lean option ignored", "hosted = feasible(c, Q, E, R, S, D, allow_zero_master, min_tokens, lean)",
+     "hosted = feasible(c, Q, E, R, S, D, allow_zero_master, min_tokens)"),
     ("minimum: small shed dropped, not raised", "t = m if avail >= m else 0", "t = 0"),
     ("minimum: fill takes the whole spare", "                x = min(spare[r], a - m)\n                if x < m:",
      "                x = spare[r]\n                if x < m:"),
@@ -94,6 +97,7 @@ PIN_SUBSET = [
     (P.test_plan_threshold_stops_at_the_target, {"which": 1, "thr": (105, 100)}),
     (P.test_plan_minimum_tokens_per_replica, {"cfg": 2, "mt": 1024}),
     (P.test_plan_minimum_single_hot_expert_wraps, {"N": 50, "R": 8, "m": 6}),
+    (P.test_plan_lean_invariants_random_shapes, {"seed": 0}),
     (P.test_plan_no_replication_possible, {"seed": 0, "S": 0, "D": 4}),
     (P.test_plan_invariants_random_shapes, {"seed": 3}),
     (P.test_layout_properties_workloads, {"cfg": 1, "layer": 0}),

@@ -51,7 +51,7 @@ def test_plan_hand_worked(case):
     thr = case.get("threshold", [1, 1])
     pl = O.plan(np.array(case["c"]), case["E"], case["R"], case["S"], case["D"],
                 allow_zero_master=case.get("allow_zero_master", False), thr_num=thr[0], thr_den=thr[1],
-                min_tokens=case.get("min_tokens", 1))
+                min_tokens=case.get("min_tokens", 1), lean=case.get("lean", False))
     assert pl.Q_star == case["Q_star"] and pl.grid_index == case["grid_index"]
     for key in ("slot_expert", "slot_quota", "master_quota", "phys_load", "phys_off",
                 "inst_ptr", "inst_phys", "inst_end", "rank_after"):
@@ -466,3 +466,42 @@ def test_plan_minimum_single_hot_expert_wraps(N, R, m):
     assert pl.slot_expert.tolist() == want.tolist()
     assert pl.slot_quota[1:1 + len(parts)].tolist() == parts
     check_plan_invariants(pl, c, False, m)
+
+
+# ------------------------------------------------------- replica-lean ----
+TABLE = load_golden("pages_ep64_table.json")
+
+
+@pytest.mark.parametrize("cfg", [6, 7, 8])
+def test_plan_lean_at_the_pages_table_shape(cfg):
+    """[README] "Tests", EP64 table: 256 experts, 4 + 2 per rank, top-8, 8k
+    tokens per rank, initial max/mean 1.51 / 2.01 / 3.03 reach 1.01 with
+    38 / 46 / 51 replicas (at most 4 / 5 / 6 per expert).  At the pages'
+    planning defaults (target 1.0, eps 0.01, at least 1024 pairs per replica)
+    the lean plan reaches max/mean 1.01 or below with at most 1.15 times the
+    table's replicas, and uses fewer than the default plan."""
+    w = W.CONFIGS[cfg]
+    idx, _, _ = W.routing(w)
+    c, _ = O.count(idx, w.E)
+    pl = O.plan(c, w.E, w.R, w.S, w.D, min_tokens=1024, lean=True)
+    check_plan_invariants(pl, c, False, 1024)
+    assert pl.imbalance_after() <= TABLE["final_imbalance"][cfg - 6] + 1e-9
+    assert pl.n_replicas <= 1.15 * TABLE["replicas_total"][cfg - 6]
+    assert pl.n_replicas < O.plan(c, w.E, w.R, w.S, w.D, min_tokens=1024).n_replicas
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_plan_lean_invariants_random_shapes(seed):
+    """Lean plans keep every invariant; no rank of a lean plan hosts a
+    replica while being above its own home-load quota (no chain makes a
+    shedding rank a host)."""
+    rng = np.random.default_rng([77, seed])
+    for _ in range(40):
+        R = int(rng.choice([2, 4, 8])); M = int(rng.choice([1, 2, 3])); E = R * M
+        D = int(rng.choice([d for d in (1, 2, 4, 8) if R % d == 0])); S = int(rng.integers(0, 4))
+        c = rng.multinomial(int(rng.integers(0, 5000)), rng.dirichlet(np.full(E, 0.3)))
+        pl = O.plan(c, E, R, S, D, lean=True)
+        check_plan_invariants(pl, c, False)
+        for s in range(R * S):
+            if pl.slot_expert[s] >= 0:
+                assert pl.rank_before[s // S] < pl.Q_star
