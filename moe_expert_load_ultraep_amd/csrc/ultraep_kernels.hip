@@ -205,6 +205,7 @@ struct PlanParams {
   int32_t eps_num, eps_den, allow_zero;
   int32_t thr_num, thr_den;
   int32_t min_tokens;
+  int32_t lean;
   int32_t rec_words;
   int32_t G, items;  // grid quotas per probe round, (quota, domain) items per round
   int32_t scan_wgs;  // workgroups per layer that build the tile ordinal bases
@@ -425,7 +426,7 @@ __device__ bool greedy_probe(int32_t Q, int d, const PlanParams& a, const PlanLd
     int dj = 0;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
-      const bool cand = elig && pa[j] > 0 && room[j] >= mt && static_cast<uint32_t>(pa[j]) > dbest;
+      const bool cand = !a.lean && elig && pa[j] > 0 && room[j] >= mt && static_cast<uint32_t>(pa[j]) > dbest;
       dbest = cand ? static_cast<uint32_t>(pa[j]) : dbest;
       dj = cand ? j : dj;
     }
@@ -486,8 +487,9 @@ constexpr int ilog2_c(int x) { return x <= 1 ? 0 : 1 + ilog2_c(x / 2); }
 
 // MIN: a minimum above one pair per replica is in force.  Without it the
 // step is compiled without the minimum's rules (each one is then a no-op),
-// so the common case keeps the shortest dependent chain.
-template <int MMAX, int SMAX, bool MIN>
+// so the common case keeps the shortest dependent chain.  LEAN: no chain
+// step (no queued piece serves as donor).
+template <int MMAX, int SMAX, bool MIN, bool LEAN>
 __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const PlanLds& L,
                                     int32_t* res_e, int32_t* res_q) {
   // queue keys: pairs << TB | (TMASK - (lane * MMAX + j)); the largest key
@@ -579,7 +581,7 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
       // the popped piece is out of the queue for this step
       const uint32_t kj = (mine && j == jsel) ? 0u : qk[j];
       qn = max(qn, kj);
-      dk = max(dk, (elig && (MIN ? room[j] >= mt : room[j] > 0)) ? kj : 0u);
+      dk = max(dk, (!LEAN && elig && (MIN ? room[j] >= mt : room[j] > 0)) ? kj : 0u);
     }
     uint32_t kmax = key, dmax = dk, knext = qn;
     wave_max3_bcast(kmax, dmax, knext);
@@ -833,9 +835,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
         int32_t* rq = L.res + static_cast<size_t>(a.items + item) * D * S;
         constexpr uint32_t kPieceLimit = 1u << (26 - ilog2_c(MMAX));
         const bool packed = static_cast<uint32_t>(cmax) < kPieceLimit && Q < (1 << 25);
-        okv = !packed              ? greedy_probe<MMAX, SMAX>(Q, d, a, L, re, rq)
-              : a.min_tokens > 1 ? greedy_probe_packed<MMAX, SMAX, true>(Q, d, a, L, re, rq)
-                                 : greedy_probe_packed<MMAX, SMAX, false>(Q, d, a, L, re, rq);
+        if (!packed)
+          okv = greedy_probe<MMAX, SMAX>(Q, d, a, L, re, rq);
+        else if (a.lean)
+          okv = a.min_tokens > 1 ? greedy_probe_packed<MMAX, SMAX, true, true>(Q, d, a, L, re, rq)
+                                 : greedy_probe_packed<MMAX, SMAX, false, true>(Q, d, a, L, re, rq);
+        else
+          okv = a.min_tokens > 1 ? greedy_probe_packed<MMAX, SMAX, true, false>(Q, d, a, L, re, rq)
+                                 : greedy_probe_packed<MMAX, SMAX, false, false>(Q, d, a, L, re, rq);
       }
       if (lane == 0) L.ok[item] = okv ? 1 : 0;
     }
@@ -2009,12 +2016,15 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
 // for a row that must be zero-filled: loads past the size return zeros and
 // stores past it are dropped, so ragged row tails and invalid rows need no
 // per-lane branches.  Loads and stores are non-temporal (each row is streamed
-// once).  A launch-shape sweep on a full-size segment (H = 4096) put one row
-// per wave with 4 vectors per lane in flight ahead of several rows per wave
-// or more vectors per lane: many small independent streams keep more of
-// HBM's channels busy than a few deep ones.
+// once).  Launch-shape sweeps on a full-size segment (H = 4096) put one row
+// per wave with 2 vectors per lane in flight ahead of 4 or 8, of several
+// rows per wave, and of persistent waves (with the tokens of 64 rows in one
+// load, and with the next row's loads issued before the current row's
+// stores): many small independent streams keep more of HBM's channels busy
+// than a few deep ones.  Rows of 4096, 5120 and 7168 elements are whole
+// multiples of the 128 vectors one round moves.
 constexpr int kPermThreads = 256;
-constexpr int kPermUnroll = 4;
+constexpr int kPermUnroll = 2;
 
 __device__ __forceinline__ int32_t perm_token(int32_t n, int32_t k, int64_t hidden_rows) {
   const int32_t t = n >= 0 ? n / k : -1;
@@ -2072,54 +2082,90 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
   const int32_t s0 = slot_begin + static_cast<int32_t>(blockIdx.y);
   const int32_t e = slot_expert[s0];
   if (e < 0) return;
-  if (threadIdx.x == 0) {
+  // Whenever this workgroup does e's work, its own slot s0 is the first
+  // replica summed (the lowest of e's slots in the range), so the first
+  // round of s0's gradient and of e's master is loaded before the list below
+  // is known: the data loads then wait on one dependent load (the master
+  // pointer), not on the chain slot -> instance range -> instances.
+  const int64_t n4 = numel / 4;
+  const f32x4* r4 = reinterpret_cast<const f32x4*>(reps);
+  float* m = masters[e];
+  const bool vec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(reps) & 15) == 0) &&
+                   ((reinterpret_cast<uintptr_t>(m) & 15) == 0);
+  const int64_t span = static_cast<int64_t>(kFoldVecs) * kFoldThreads;
+  const int64_t i00 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x;
+  f32x4 g0[kFoldVecs], a0[kFoldVecs];
+  if (vec && m != nullptr) {
+    const f32x4* rq = r4 + static_cast<int64_t>(s0 - slot_begin) * n4;
+    const f32x4* m4 = reinterpret_cast<const f32x4*>(m);
+#pragma unroll
+    for (int u = 0; u < kFoldVecs; ++u) {
+      const int64_t i = i00 + static_cast<int64_t>(u) * kFoldThreads;
+      a0[u] = i < n4 ? __builtin_nontemporal_load(m4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+      g0[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  if (threadIdx.x < 64) {
     // e's instances are in ascending physical id, i.e. ascending slot id for
-    // its replicas; keep those in the range.
+    // its replicas: wave 0 reads them 64 at a time and keeps, in order, those
+    // in the range; the workgroups of the lowest of them do e's work
+    const int lane = threadIdx.x;
+    const int32_t i0 = inst_ptr[e], i1 = inst_ptr[e + 1];
     int n = 0;
     bool first = true;
-    for (int32_t i = inst_ptr[e]; i < inst_ptr[e + 1]; ++i) {
-      const int32_t p = inst_phys[i];
-      const int32_t j = p % (M + S);
-      if (j < M) continue;
-      const int32_t s = (p / (M + S)) * S + (j - M);
-      if (s < slot_begin || s >= slot_end) continue;
-      if (n == 0 && s != s0) first = false;
-      if (n < kFoldMaxReps) s_list[n] = s - slot_begin;
-      ++n;
+    for (int32_t b = i0; b < i1; b += 64) {
+      const int32_t i = b + lane;
+      int32_t s = -1;
+      if (i < i1) {
+        const int32_t p = inst_phys[i];
+        const int32_t j = p % (M + S);
+        const int32_t q = (p / (M + S)) * S + (j - M);
+        s = (j >= M && q >= slot_begin && q < slot_end) ? q : -1;
+      }
+      const uint64_t mk = ballot(s >= 0);
+      if (n == 0 && mk != 0)
+        first = static_cast<int32_t>(readlane(static_cast<uint32_t>(s), lowest_lane(mk))) == s0;
+      const int at = n + count_below(mk);
+      if (s >= 0 && at < kFoldMaxReps) s_list[at] = s - slot_begin;
+      n += __builtin_popcountll(mk);
     }
-    s_n = first ? n : 0;
+    if (lane == 0) s_n = first ? n : 0;
   }
   __syncthreads();
   const int n = min(s_n, kFoldMaxReps);
-  float* m = masters[e];
   if (n == 0 || m == nullptr) return;
 
   const int64_t tstride = static_cast<int64_t>(gridDim.x) * kFoldThreads;
-  const bool vec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(m) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(reps) & 15) == 0);
   if (vec) {
     // each thread takes kFoldVecs 16-byte vectors a block-width apart, and
     // every load of a replica round is issued before any add or store (the
     // masters and the replica gradients are distinct buffers)
-    const int64_t n4 = numel / 4;
     f32x4* m4 = reinterpret_cast<f32x4*>(m);
-    const f32x4* r4 = reinterpret_cast<const f32x4*>(reps);
-    const int64_t span = static_cast<int64_t>(kFoldVecs) * kFoldThreads;
-    for (int64_t i0 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x; i0 < n4;
-         i0 += static_cast<int64_t>(gridDim.x) * span) {
+    for (int64_t i0 = i00; i0 < n4; i0 += static_cast<int64_t>(gridDim.x) * span) {
       f32x4 acc[kFoldVecs];
+      if (i0 == i00) {
 #pragma unroll
-      for (int u = 0; u < kFoldVecs; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
-        acc[u] = i < n4 ? __builtin_nontemporal_load(m4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      for (int q = 0; q < n; ++q) {
-        const f32x4* rq = r4 + static_cast<int64_t>(s_list[q]) * n4;
-        f32x4 g[kFoldVecs];
+        for (int u = 0; u < kFoldVecs; ++u) acc[u] = a0[u];
+      } else {
 #pragma unroll
         for (int u = 0; u < kFoldVecs; ++u) {
           const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
-          g[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[u] = i < n4 ? __builtin_nontemporal_load(m4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      for (int q = 0; q < n; ++q) {
+        f32x4 g[kFoldVecs];
+        if (q == 0 && i0 == i00) {
+          // s_list[0] is s0: its first round is already loaded
+#pragma unroll
+          for (int u = 0; u < kFoldVecs; ++u) g[u] = g0[u];
+        } else {
+          const f32x4* rq = r4 + static_cast<int64_t>(s_list[q]) * n4;
+#pragma unroll
+          for (int u = 0; u < kFoldVecs; ++u) {
+            const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
+            g[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
 #pragma unroll
         for (int u = 0; u < kFoldVecs; ++u) {
@@ -2325,7 +2371,7 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   pp.E = sh.E; pp.R = sh.R; pp.S = sh.S; pp.D = sh.D; pp.M = sh.M; pp.P = sh.P;
   pp.ndom = sh.ndom; pp.n_inst = sh.n_inst; pp.N = N; pp.ntiles = ntiles; pp.tpr = tl.tpr;
   pp.eps_num = sh.eps_num; pp.eps_den = sh.eps_den; pp.allow_zero = sh.allow_zero;
-  pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den; pp.min_tokens = sh.min_tokens;
+  pp.thr_num = sh.thr_num; pp.thr_den = sh.thr_den; pp.min_tokens = sh.min_tokens; pp.lean = sh.lean;
   pp.rec_words = sh.lay.words;
   plan_rounds(sh, &pp.G, &pp.items);
   {
