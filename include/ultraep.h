@@ -116,7 +116,14 @@ typedef struct ultraep_ctx ultraep_ctx;
  *   of a piece; a split leaves at least m queued (the roomiest receiver
  *   takes min(spare, piece - m), skipped in a chain when below m; the
  *   donor's part is cut so that 0 or at least m stays queued); a placement
- *   below m fails the probe.  m = 1 is the plain greedy. */
+ *   below m fails the probe.  m = 1 is the plain greedy.
+ * replica_lean (the pages' EP64 table, [README] "Tests", reaches max/mean
+ *   1.01 with few replicas; their planner's rule is not given): 1 plans
+ *   without the chain step of the greedy (step 3 of ultraep_balance): only
+ *   ranks with spare take replicas, a piece that fits no receiver goes in
+ *   part to the roomiest one and the rest is queued again.  On large domains
+ *   this needs about a third fewer replicas at the same quota; small domains
+ *   may need a higher quota.  0 (default) keeps the chain. */
 #define ULTRAEP_REROUTE_RANGES 0
 #define ULTRAEP_REROUTE_LOCAL 1
 #define ULTRAEP_REROUTE_INTERLEAVE 2
@@ -128,7 +135,7 @@ typedef struct ultraep_options {
   int32_t threshold_den;
   int32_t reroute_mode;
   int32_t min_tokens_per_replica;
-  int32_t reserved[1]; /* must be zero */
+  int32_t replica_lean; /* 0 (default) or 1 */
 } ultraep_options;
 
 /* Weight-distribution plan of ultraep_weight_sync_plan ([README]

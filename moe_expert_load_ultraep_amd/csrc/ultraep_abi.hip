@@ -109,10 +109,10 @@ int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
   if (E > ULTRAEP_MAX_EXPERTS || E / R > ULTRAEP_MAX_MASTERS || slots_per_rank > ULTRAEP_MAX_SLOTS ||
       D > ULTRAEP_MAX_DOMAIN || static_cast<int64_t>(R) * slots_per_rank > ULTRAEP_MAX_TOTAL_SLOTS)
     return ULTRAEP_EUNSUPPORTED;
-  ultraep_options o{1, 100, 0, 1, 1, ULTRAEP_REROUTE_RANGES, 1, {0}};
+  ultraep_options o{1, 100, 0, 1, 1, ULTRAEP_REROUTE_RANGES, 1, 0};
   if (opt) {
     o = *opt;
-    if (o.reserved[0] != 0 || o.min_tokens_per_replica < 0) return ULTRAEP_EINVAL;
+    if ((o.replica_lean != 0 && o.replica_lean != 1) || o.min_tokens_per_replica < 0) return ULTRAEP_EINVAL;
     if (o.min_tokens_per_replica == 0) o.min_tokens_per_replica = 1;
     if (o.reroute_mode < ULTRAEP_REROUTE_RANGES || o.reroute_mode > ULTRAEP_REROUTE_INTERLEAVE)
       return ULTRAEP_EINVAL;
@@ -141,6 +141,7 @@ int ultraep_create(int32_t E, int32_t R, int32_t slots_per_rank, int32_t D,
   sh.thr_den = o.threshold_den;
   sh.reroute_mode = o.reroute_mode;
   sh.min_tokens = o.min_tokens_per_replica;
+  sh.lean = o.replica_lean;
   build_layout(&sh);
   if (ultraep::plan_lds_bytes(sh) > 160 * 1024 || ultraep::rerouting_lds_bytes(sh, true) > 160 * 1024) {
     delete c;

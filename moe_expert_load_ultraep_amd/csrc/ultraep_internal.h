@@ -25,7 +25,8 @@ struct Shape {
   int32_t eps_num, eps_den, allow_zero;
   int32_t thr_num, thr_den;              // early-stop target of the quota search
   int32_t reroute_mode;                  // ULTRAEP_REROUTE_*
-  int32_t min_tokens;                    // smallest replica quota kept
+  int32_t min_tokens;                    // minimum pairs per replica (>= 1)
+  int32_t lean;                          // 1: the greedy without its chain step
   PlanLayout lay;
 };
 

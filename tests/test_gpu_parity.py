@@ -85,7 +85,7 @@ def test_hand_worked_plans_on_gpu():
         idx[:ids.size] = np.random.default_rng(0).permutation(ids)
         ctx = U.ultraep_create(E, R, S, D, allow_zero_master=case.get("allow_zero_master", False),
                                threshold=tuple(case.get("threshold", (1, 1))),
-                               min_tokens=case.get("min_tokens", 1))
+                               min_tokens=case.get("min_tokens", 1), replica_lean=case.get("lean", False))
         got = run_balance(ctx, idx.reshape(1, R * T, k), None, T, k)
         g = ctx.decode_plan(got["plans"][0])
         assert g["Q_star"] == case["Q_star"] and g["grid_index"] == case["grid_index"], case["name"]
@@ -200,6 +200,25 @@ def test_minimum_tokens_per_replica(cfg, T, mt):
     got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
     pl, _, _ = assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D, min_tokens=mt)
     check_plan_invariants(pl, pl.c, False, mt)
+
+
+@pytest.mark.parametrize("cfg,T,mt", [(2, None, 1), (2, None, 1024), (6, None, 1024), (7, None, 1024),
+                                      (8, None, 1024), (5, 2048, 1)])
+def test_replica_lean(cfg, T, mt):
+    """The lean planner (no chain step) at full size: plan record, replica
+    map and fused layout equal to the oracle's; at the pages' table shape
+    within 1.15 times the table's replicas at max/mean 1.01."""
+    w = W.CONFIGS[cfg] if T is None else W.CONFIGS[cfg].with_(T=T)
+    say(f"lean cfg={cfg} T={w.T} min={mt}")
+    idx, wt = routing_cached(cfg, 0, 0, T)
+    ctx = _ctx(w, min_tokens=mt, replica_lean=True)
+    got = run_balance(ctx, idx[None], wt[None], w.T, w.k)
+    pl, _, _ = assert_layer_equal(ctx, got, 0, idx, wt, w.E, w.R, w.S, w.D, min_tokens=mt, lean=True)
+    check_plan_invariants(pl, pl.c, False, mt)
+    if cfg in (6, 7, 8):
+        table = load_golden("pages_ep64_table.json")
+        assert pl.imbalance_after() <= 1.01 + 1e-9
+        assert pl.n_replicas <= 1.15 * table["replicas_total"][cfg - 6]
 
 
 @pytest.mark.parametrize("mode", [1, 2])

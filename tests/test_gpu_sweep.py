@@ -55,6 +55,8 @@ def sweep_case(i):
         opts["eps_num"], opts["eps_den"] = [(0, 1), (1, 20), (1, 1000)][int(rng.integers(3))]
     if rng.random() < 0.25:
         opts["min_tokens"] = int(rng.choice([2, 3, 8, 50, 400]))
+    if rng.random() < 0.25:
+        opts["lean"] = True
     return dict(E=E, R=R, S=S, D=D, k=k, T=T, idx=idx.reshape(R * T, k), wt=wt.reshape(R * T, k),
                 opts=opts)
 
@@ -65,7 +67,7 @@ def _ctx(c, mode):
                             eps=(o.get("eps_num", 1), o.get("eps_den", 100)),
                             allow_zero_master=o["allow_zero_master"],
                             threshold=(o.get("thr_num", 1), o.get("thr_den", 1)), reroute_mode=mode,
-                            min_tokens=o.get("min_tokens", 1))
+                            min_tokens=o.get("min_tokens", 1), replica_lean=o.get("lean", False))
 
 
 @pytest.mark.parametrize("chunk", range(CHUNKS))
