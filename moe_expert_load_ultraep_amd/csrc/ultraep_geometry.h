@@ -170,7 +170,8 @@ enum PlanTable {
   kT_rmask = 0,  // [E] 64-bit: domain ranks holding a replica of e
   kT_c,          // [E] pairs per expert
   kT_H,          // [R] home loads
-  kT_part,       // [kPlanThreads] per-thread partials
+  kT_part,       // [kPlanThreads] unused by the planner: it keeps the allocation large
+                 // enough for the tile-base workgroups' partials (its first kPlanThreads words)
   kT_dom,        // [ndom] domain loads
   kT_scal,       // [kPlanScalars]
   kT_ok,         // [items] probe outcomes

@@ -81,63 +81,12 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
   return x;
 }
 
-// Exclusive scans of two independent arrays in LDS by a workgroup of NT
-// threads, sharing their two barriers (a[na] and b[nb] receive the
-// totals); tmp holds 2 * (NT / 64 + 1) words.
-template <int NT>
-__device__ void block_exclusive_scan2(int32_t* a, int na, int32_t* b, int nb, int32_t* tmp) {
-  constexpr int W = NT / 64;
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const int pa = (na + NT - 1) / NT, pb = (nb + NT - 1) / NT;
-  const int ba = min(tid * pa, na), ea = min(ba + pa, na);
-  const int bb = min(tid * pb, nb), eb = min(bb + pb, nb);
-  int32_t sa = 0, sb = 0;
-  for (int i = ba; i < ea; ++i) sa += a[i];
-  for (int i = bb; i < eb; ++i) sb += b[i];
-  const int32_t ia = wave_inclusive_scan(sa), ib = wave_inclusive_scan(sb);
-  if (lane == 63) {
-    tmp[wave] = ia;
-    tmp[W + 1 + wave] = ib;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int32_t t = lane < W ? tmp[lane] : 0;
-    const int32_t u = lane < W ? tmp[W + 1 + lane] : 0;
-    const int32_t ti = wave_inclusive_scan(t), ui = wave_inclusive_scan(u);
-    if (lane < W) {
-      tmp[lane] = ti - t;
-      tmp[W + 1 + lane] = ui - u;
-    }
-    if (lane == W - 1) {
-      tmp[W] = ti;
-      tmp[2 * W + 1] = ui;
-    }
-  }
-  __syncthreads();
-  int32_t ra = tmp[wave] + ia - sa;
-  for (int i = ba; i < ea; ++i) {
-    const int32_t v = a[i];
-    a[i] = ra;
-    ra += v;
-  }
-  int32_t rb = tmp[W + 1 + wave] + ib - sb;
-  for (int i = bb; i < eb; ++i) {
-    const int32_t v = b[i];
-    b[i] = rb;
-    rb += v;
-  }
-  if (tid == 0) {
-    a[na] = tmp[W];
-    b[nb] = tmp[2 * W + 1];
-  }
-  __syncthreads();
-}
-
 // Exclusive scan of a[0, n) by the calling wave alone (a[n] receives the
 // total): each lane sums a contiguous run, the lanes scan their sums, and
 // each lane writes its run's prefixes.  For the short arrays of a tile's
-// runs one wave is enough, and the other waves skip the block scan's two
-// extra barriers.  The caller synchronises afterwards.  With COUNT, each
+// runs and the planner's offsets one wave is enough, where a scan across the
+// workgroup would need two more barriers.  The caller synchronises
+// afterwards.  With COUNT, each
 // value x (a run length below 2^16) is taken as x + 2^16 [x > 0], so the
 // prefixes hold the offset in the low half and the non-empty runs before
 // in the high half.
@@ -221,7 +170,6 @@ enum Scalar {
 struct PlanLds {
   int32_t* c;      // [E]
   int32_t* H;      // [R]
-  int32_t* part;   // [kPlanThreads]
   int32_t* dom;    // [ndom]
   int32_t* scal;   // [kScalars]
   int32_t* ok;     // [items]
@@ -248,7 +196,6 @@ __device__ inline PlanLds carve(int32_t* lds, const PlanParams& a) {
   L.rmask = reinterpret_cast<unsigned long long*>(lds + t.off[kT_rmask]);
   L.c = lds + t.off[kT_c];
   L.H = lds + t.off[kT_H];
-  L.part = lds + t.off[kT_part];
   L.dom = lds + t.off[kT_dom];
   L.scal = lds + t.off[kT_scal];
   L.ok = lds + t.off[kT_ok];
@@ -798,12 +745,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     if (lane == 0) {
       // lowest quota aimed at: the early-stop target times the mean (at
       // least the domain floor, at most the max home load)
-      const int64_t tden = static_cast<int64_t>(R) * a.thr_den;
-      const int64_t qmean = (static_cast<int64_t>(total) * a.thr_num + tden - 1) / tden;
+      // (64-bit division is a long software sequence: both quotients take
+      // the 32-bit form whenever their operands fit, as they do for the
+      // default target and tolerance)
+      const uint64_t tden = static_cast<uint64_t>(R) * a.thr_den;
+      const uint64_t qnum = static_cast<uint64_t>(total) * a.thr_num + tden - 1;
+      const uint64_t eden = static_cast<uint64_t>(R) * a.eps_den;
+      const uint64_t enum_ = static_cast<uint64_t>(total) * a.eps_num;
+      const int64_t qmean = static_cast<int64_t>(
+          (qnum >> 32) == 0 && (tden >> 32) == 0 ? static_cast<uint32_t>(qnum) / static_cast<uint32_t>(tden)
+                                                 : qnum / tden);
       const int64_t qlb64 = min(max(qmean, static_cast<int64_t>(floor)), static_cast<int64_t>(qmax));
       const int32_t qlb = static_cast<int32_t>(qlb64);
-      const int64_t tol64 = (static_cast<int64_t>(total) * a.eps_num) /
-                            (static_cast<int64_t>(R) * a.eps_den);
+      const int64_t tol64 = static_cast<int64_t>(
+          (enum_ >> 32) == 0 && (eden >> 32) == 0 ? static_cast<uint32_t>(enum_) / static_cast<uint32_t>(eden)
+                                                  : enum_ / eden);
       const int32_t tol = static_cast<int32_t>(tol64 < 1 ? 1 : tol64);
       L.scal[kTotal] = static_cast<int32_t>(total);
       L.scal[kQmax] = static_cast<int32_t>(qmax);
@@ -910,8 +866,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     rec[a.off[ULTRAEP_PLAN_RANK_BEFORE] + r] = L.H[r];
   }
   __syncthreads();
-  // pload -> phys_off, instance counts -> inst_ptr
-  block_exclusive_scan2<kPlanThreads>(L.pload, P, L.iptr, E, L.part);
+  // pload -> phys_off, instance counts -> inst_ptr: one wave each, so the
+  // two scans run side by side and need no barrier but the one after them
+  if (wave == 0) wave_exclusive_scan(L.pload, P);
+  if (wave == 1) wave_exclusive_scan(L.iptr, E);
+  __syncthreads();
 
   // instances of e in ascending physical id = ascending rank inside e's
   // domain.  One thread per master or filled slot places its instance: the
@@ -980,6 +939,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     inst_base[i] = 0;
     inst_local[i] = 0;
   }
+  // (unrolled, so the field offsets come in with one batch of scalar loads
+  // instead of a dependent load per field)
+#pragma unroll
   for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
     const int end = f + 1 < ULTRAEP_PLAN_NUM_FIELDS ? a.off[f + 1] : a.rec_words;
     for (int wd = a.off[f] + a.len[f] + tid; wd < end; wd += kPlanThreads) rec[wd] = 0;
