@@ -18,7 +18,8 @@ same input) and cold (a 1 GiB scratch write before each repetition evicts the
 way; every cold figure also comes as mean, median, p99 and max
 (cold_distribution_us).  The balance is timed again at the pages' default
 knobs (locality-aware decomposition with interleave, at least 1024 pairs per
-replica: pages_defaults).  The CPU oracle is timed stage by stage on the host
+replica: pages_defaults) and with the replica-lean planner option
+(replica_lean: its plan quality and the weight_sync of its fewer slots).  The CPU oracle is timed stage by stage on the host
 on the same workload (cpu_baseline).  Workloads of several layers or
 microbatches also report each instance's max/mean before and after
 (load_trace; --load-trace writes every rank and expert load).  Prints ONE
@@ -495,6 +496,32 @@ def main():
         pdef["dispatch_traffic"] = dispatch_traffic(buf_p.phys_idx[0].cpu().numpy(), w)
         del buf_p
 
+    # ---- replica-lean planning (an option: the greedy without its chain
+    # step), at the pages' minimum of 1024 pairs per replica: the balance
+    # timed cold, its plan quality, and below the weight_sync of its slots
+    lean = None
+    buf_l = None
+    if not args.no_pages_defaults:
+        ctx_l = U.ultraep_create(w.E, w.R, w.S, w.D, threshold=thr, min_tokens=1024, replica_lean=True)
+        buf_l = U.Buffers(ctx_l, L, w.T, w.k, dev)
+
+        def balance_l(i):
+            U.ultraep_balance(ctx_l, d_idx[i], w.T, w.k, buf_l.workspace, buf_l.plans, buf_l.phys_idx,
+                              buf_l.pos, topk_w=d_w[i], inv=buf_l.inv, w_perm=buf_l.w_perm, L=L)
+
+        plans_l = []
+        for i in range(n_inst):
+            balance_l(i)
+            host = buf_l.plans.cpu().numpy()
+            plans_l.append([ctx_l.decode_plan(host[l]) for l in range(L)])
+        l_cold = timed(lambda r: balance_l(r % n_inst), n_inst if args.config == 4 else args.cold_reps, True)
+        balance_l(0)
+        torch.cuda.synchronize()
+        lean = {"replica_lean": True, "min_tokens_per_replica": 1024, "reroute_mode": 0,
+                "balance_reroute_us_per_layer": float(np.mean(l_cold)) * 1e3 / L,
+                "cold_distribution_us": dist_us(l_cold, L)}
+        lean.update(quality(ctx_l, [p[l] for p in plans_l for l in range(L)], w))
+
     # ---- combine and its backward (after the experts; not part of the step):
     # the tokens of the permuted rank against the whole layout of the first
     # layer, expert outputs and output gradients drawn on the GPU
@@ -570,6 +597,18 @@ def main():
         t_rank = timed(lambda r: ws(slots[0], slots[1], None), args.cold_reps, True)
         t_all = timed(lambda r: ws(0, nslot, None), args.cold_reps, True)
         t_rel = timed(lambda r: ws(0, nslot, relay), args.cold_reps, True)
+        if lean is not None:
+            # every filled slot of the lean plan (fewer replicas: fewer copies)
+            def ws_lean(r):
+                for q in range(2):
+                    U.ultraep_weight_sync(ctx_l, buf_l.plans[0], ptrs[q], reps_w[q], numels[q], 0, nslot)
+            ws_lean(0)
+            t_lean = timed(ws_lean, args.cold_reps, True)
+            lean_e = [int(e) for e in plans_l[0][0]["slot_expert"] if e >= 0]
+            lean_b = sum(n * 2 * (len(lean_e) + len(set(lean_e))) for n in numels)
+            lean["weight_sync_all_slots_us"] = float(np.mean(t_lean)) * 1e3
+            lean["weight_sync_all_slots_bytes"] = lean_b
+            lean["weight_sync_all_slots_GBps"] = gbps_fn(lean_b, float(np.mean(t_lean)))
         rel = relay.cpu().numpy()
         b_rank, b_all = ws_bytes(slots[0], slots[1]), ws_bytes(0, nslot)
         wsync = {"expert_weights": f"fc1 2x{w.H}x{w.ffn} + fc2 {w.H}x{w.ffn} bf16 per expert",
@@ -585,7 +624,7 @@ def main():
         wsync["all_slots_frac_of_peak"] = wsync["all_slots_GBps"] / HBM_PEAK_GBPS
         wsync["rank_slots_frac_of_peak"] = wsync["rank_slots_GBps"] / HBM_PEAK_GBPS
         del mast, ptrs, reps_w, relay
-    del scratch
+    del scratch, buf_l
 
     # ---- algorithmic bytes
     row_bytes = 2 * 2 * w.H + 4                            # read row, write row, read inv
@@ -661,6 +700,8 @@ def main():
         result["stale_plan_imbalance_median_max"] = [float(np.median(stale)), float(np.max(stale))]
     if pdef is not None:
         result["pages_defaults"] = pdef
+    if lean is not None:
+        result["replica_lean"] = lean
     # per-(layer, microbatch) loads before and after balancing (the pages'
     # load profiler records the same per microbatch: [README] "Load profiler
     # and viewer"): max/mean per instance in the line, every rank and expert

@@ -94,6 +94,17 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 
 __device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(m); }
 
+// Inclusive scan across the wave's lanes (cross-lane shuffles).
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
 // 16-byte vectors as native clang vectors (the nontemporal builtins take
 // these, not HIP's struct vector types).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

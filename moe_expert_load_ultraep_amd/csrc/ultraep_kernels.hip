@@ -70,17 +70,6 @@ __device__ __forceinline__ void load_tile_ids(const int32_t* __restrict__ src, i
   }
 }
 
-// Inclusive scan across the wave's lanes (cross-lane shuffles).
-__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
 // Exclusive scan of a[0, n) by the calling wave alone (a[n] receives the
 // total): each lane sums a contiguous run, the lanes scan their sums, and
 // each lane writes its run's prefixes.  For the short arrays of a tile's
