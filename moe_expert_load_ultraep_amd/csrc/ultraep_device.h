@@ -84,6 +84,20 @@ __device__ __forceinline__ void wave_max3_bcast(uint32_t& a, uint32_t& b, uint32
   c = readlane(c, 63);
 }
 
+// Two independent wave maxima, interleaved as wave_max3_bcast.
+__device__ __forceinline__ void wave_max2_bcast(uint32_t& a, uint32_t& b) {
+#define ULTRAEP_MAX2(F) a = max(a, F(a)); b = max(b, F(b))
+  ULTRAEP_MAX2(dpp<0xB1>);
+  ULTRAEP_MAX2(dpp<0x4E>);
+  ULTRAEP_MAX2(dpp<0x141>);
+  ULTRAEP_MAX2(dpp<0x140>);
+  ULTRAEP_MAX2((dpp_rows<0x142, 0xA>));
+  ULTRAEP_MAX2((dpp_rows<0x143, 0xC>));
+#undef ULTRAEP_MAX2
+  a = readlane(a, 63);
+  b = readlane(b, 63);
+}
+
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
   x += dpp<0xB1>(x);
   x += dpp<0x4E>(x);
@@ -94,15 +108,20 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 
 __device__ __forceinline__ int lowest_lane(uint64_t m) { return __builtin_ctzll(m); }
 
-// Inclusive scan across the wave's lanes (cross-lane shuffles).
+// Inclusive scan across the wave's lanes, all in DPP (no LDS round trip):
+// inside each 16-lane row by row shifts of 1, 2, 4 and 8 lanes (a lane
+// whose source lies before its row adds 0), then the row totals are carried
+// by row broadcasts (lane 15 into row 1 and lane 47 into row 3, then lane 31
+// into rows 2 and 3).  Every lane must be active.
 __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
+  uint32_t v = static_cast<uint32_t>(x);
+  v += dpp<0x111>(v);               // row_shr:1
+  v += dpp<0x112>(v);               // row_shr:2
+  v += dpp<0x114>(v);               // row_shr:4
+  v += dpp<0x118>(v);               // row_shr:8
+  v += dpp_rows<0x142, 0xA>(v);     // row_bcast:15 -> rows 1, 3
+  v += dpp_rows<0x143, 0xC>(v);     // row_bcast:31 -> rows 2, 3
+  return static_cast<int32_t>(v);
 }
 
 // 16-byte vectors as native clang vectors (the nontemporal builtins take

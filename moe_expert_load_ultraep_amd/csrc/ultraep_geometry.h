@@ -147,6 +147,12 @@ __host__ __device__ inline int32_t local_row(int32_t t0, int u, int32_t t1) {
   return t0 + u < t1 - 1 ? t0 + u : t1 - 1;
 }
 
+// The planner loads the first batch of every local take early: thread tid
+// for slot tid (rank tid / S) and for master tid (rank tid / M), before it
+// knows which experts those instances hold.  A rank without tiles (a layer
+// of no tokens) has no rows, and then nothing is loaded.
+__host__ __device__ inline bool local_prefetch(int32_t tpr) { return tpr > 0; }
+
 // Grid quotas per probe round: enough (quota, domain) items for one probe
 // wave per SIMD.  More probe waves than SIMDs only share issue slots: the
 // probes of a round run in lock step, and the first one usually succeeds.

@@ -452,84 +452,84 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
     qk[j] = pa[j] > 0 ? (static_cast<uint32_t>(pa[j]) << TB) | (tie0 - j) : 0u;
   int32_t spare = act ? max(0, Q - Hr) : 0;
   int32_t nh = act ? 0 : S;  // filled slots; inactive lanes look full
-  int32_t he[SMAX], hq[SMAX];
+  // hosted replicas, newest first, each as the queue index (lane * MMAX + j
+  // inside the domain) of its expert's master, which names the expert
+  int32_t ht[SMAX], hq[SMAX];
 #pragma unroll
   for (int s = 0; s < SMAX; ++s) {
-    he[s] = -1;
+    ht[s] = -1;
     hq[s] = 0;
   }
-
-  // the queue's pop key: the largest piece, ties to the lowest expert id
-  auto queue_key = [&]() {
-    uint32_t mk = 0;
-#pragma unroll
-    for (int j = 0; j < MMAX; ++j) mk = max(mk, qk[j]);
-    return mk;
-  };
+  const uint32_t rl = static_cast<uint32_t>(63 - lane);
 
   // One reduction stage per step: the receiver key, the donor key and the
   // queue's key after the pop are reduced together.  The next pop key is
   // then known without another reduction: a fit leaves the queue as the pop
   // left it; a chain grows the donor's piece (its key grows by the pairs
   // added, the tie bits stay) and may re-queue the rest of the popped piece
-  // under its own tie bits; a fill re-queues the rest.
+  // under its own tie bits; a fill re-queues the rest.  Keys are unique, so
+  // the popped entry is the one whose key equals the pop key.
   //
   // The three outcomes share one update.  The receiver (lane kl) takes
   // r_amt pairs: the whole piece on a fit, else its whole spare (0 when no
   // rank has spare); the donor (lane dl, chains only) takes x more; the
   // rest goes back to the owner's queue entry.  Receiver and donor are
   // different ranks (a rank with spare queued nothing), so each lane places
-  // at most one instance per step, and the step has no branch but the exit
-  // and the rare failure.
-  uint32_t km = wave_max_bcast(queue_key());
-  const int max_steps = D * S + 1;
-  for (int step = 0; step <= max_steps; ++step) {
-    if (km == 0) {
-      if (act) {
+  // at most one replica per step, and the step has no branch but the exit
+  // and the rare failure.  A rank that queues a piece has no spare, so the
+  // popped piece's own rank is never a receiver; it is kept out of the
+  // donors explicitly.
+  uint32_t mk = 0;
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-          if (s < S) {
-            res_e[lane * S + s] = he[s];
-            res_q[lane * S + s] = hq[s];
-          }
-      }
-      return true;
-    }
+  for (int j = 0; j < MMAX; ++j) mk = max(mk, qk[j]);
+  uint32_t km = wave_max_bcast(mk);
+  int guard = D * S + 1;  // every step fills a slot
+  while (km != 0) {
+    if (--guard < 0) return false;
     const uint32_t own_tie = km & TMASK;
-    const uint32_t t = TMASK - own_tie;
-    const int owner = static_cast<int>(t / MMAX), jsel = static_cast<int>(t % MMAX);
-    const int32_t e = (d * D + owner) * M + jsel;
+    const int32_t t = static_cast<int32_t>(TMASK - own_tie);
     const int32_t amt = static_cast<int32_t>(km >> TB);
-    const bool mine = lane == owner;
     bool hosts = false;
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) hosts |= (he[s] == e);
-    const bool elig = !mine && nh < S && !hosts;
+    for (int s = 0; s < SMAX; ++s) hosts |= ht[s] == t;
+    const bool elig = !hosts && nh < S;
     const uint32_t core = spare >= amt ? (kFitBit | (kFitBit - 1 - static_cast<uint32_t>(spare)))
                                        : static_cast<uint32_t>(spare);
     // receivers need a spare of at least the minimum (a whole piece is never
     // below it), donors room for the minimum more
-    const uint32_t key = (elig && (MIN ? spare >= mt : spare > 0))
-                             ? (core << 6) | static_cast<uint32_t>(63 - lane) : 0u;
+    const uint32_t key = (elig && (MIN ? spare >= mt : spare > 0)) ? (core << 6) | rl : 0u;
+    const bool delig = !LEAN && elig && lane != t / MMAX;
     uint32_t dk = 0, qn = 0;
+    bool popped[MMAX];
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
-      // the popped piece is out of the queue for this step
-      const uint32_t kj = (mine && j == jsel) ? 0u : qk[j];
+      popped[j] = qk[j] == km;
+      const uint32_t kj = popped[j] ? 0u : qk[j];
       qn = max(qn, kj);
-      dk = max(dk, (!LEAN && elig && (MIN ? room[j] >= mt : room[j] > 0)) ? kj : 0u);
+      if constexpr (!LEAN) dk = max(dk, (delig && (MIN ? room[j] >= mt : room[j] > 0)) ? kj : 0u);
     }
     uint32_t kmax = key, dmax = dk, knext = qn;
-    wave_max3_bcast(kmax, dmax, knext);
+    if constexpr (LEAN)
+      wave_max2_bcast(kmax, knext);
+    else
+      wave_max3_bcast(kmax, dmax, knext);
     const bool fit = (kmax & (kFitBit << 6)) != 0;
-    int32_t r_amt, x;
-    const int kl = 63 - static_cast<int>(kmax & 63);
-    const uint32_t dt = TMASK - (dmax & TMASK);
-    const int dl = static_cast<int>(dt / MMAX) & 63, djs = static_cast<int>(dt % MMAX);
-    int32_t myroom = 0;
+    // the receiver's lane, none (64) when no rank has spare
+    const int kl = kmax != 0 ? 63 - static_cast<int>(kmax & 63) : 64;
+    int32_t r_amt, x = 0;
+    int dl = 0, djs = 0;
+    if constexpr (!LEAN) {
+      const uint32_t dt = TMASK - (dmax & TMASK);
+      dl = static_cast<int>(dt / MMAX) & 63;
+      djs = static_cast<int>(dt % MMAX);
+    }
+    int32_t droom = 0;
+    if constexpr (!LEAN) {
+      int32_t myroom = room[0];
 #pragma unroll
-    for (int j = 0; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
-    const int32_t droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
+      for (int j = 1; j < MMAX; ++j) myroom = j == djs ? room[j] : myroom;
+      droom = static_cast<int32_t>(readlane(static_cast<uint32_t>(myroom), dl));
+    }
     if constexpr (MIN) {
       // without a fit the roomiest receiver takes its spare, but leaves at
       // least the minimum queued and takes nothing below it; the donor's
@@ -548,32 +548,51 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
       // the receiver takes the whole piece on a fit, else its whole spare
       if (!fit && kmax == 0 && dmax == 0) return false;
       r_amt = fit ? amt : static_cast<int32_t>(kmax >> 6);
-      x = (!fit && dmax > 0) ? min(amt - r_amt, droom) : 0;
+      if constexpr (!LEAN) x = (!fit && dmax > 0) ? min(amt - r_amt, droom) : 0;
     }
     const int32_t left = amt - r_amt - x;
-    const bool rcv = lane == kl, don = lane == dl;
-    const int32_t give = (rcv ? r_amt : 0) + (don ? x : 0);
+    const bool rcv = lane == kl, don = !LEAN && lane == dl;
+    // (the receiver, when there is one, is never the donor; dl names some
+    // lane even when no donor is taken, x then being 0)
+    const int32_t give = rcv ? r_amt : (don ? x : 0);
     const bool put = give > 0;
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) {
-      const bool here = put && s == nh;
-      he[s] = here ? e : he[s];
-      hq[s] = here ? give : hq[s];
+    for (int s = SMAX - 1; s > 0; --s) {
+      ht[s] = put ? ht[s - 1] : ht[s];
+      hq[s] = put ? hq[s - 1] : hq[s];
     }
+    ht[0] = put ? t : ht[0];
+    hq[0] = put ? give : hq[0];
     nh += put ? 1 : 0;
     spare -= rcv ? r_amt : 0;
     const uint32_t requeue = left > 0 ? (static_cast<uint32_t>(left) << TB) | own_tie : 0u;
+    const uint32_t xs = static_cast<uint32_t>(x) << TB;
 #pragma unroll
     for (int j = 0; j < MMAX; ++j) {
-      const int32_t add = (don && j == djs) ? x : 0;
-      qk[j] = (mine && j == jsel) ? requeue : qk[j] + (static_cast<uint32_t>(add) << TB);
-      room[j] -= add;
+      const bool dj = don && j == djs;
+      qk[j] = popped[j] ? requeue : qk[j] + (dj ? xs : 0u);
+      room[j] -= dj ? x : 0;
     }
     // a fit leaves dmax at most knext (the donor's piece is still queued)
-    km = max(knext, dmax + (static_cast<uint32_t>(x) << TB));
-    km = max(km, requeue);
+    km = __builtin_amdgcn_readfirstlane(static_cast<int>(max(max(knext, dmax + xs), requeue)));
   }
-  return false;
+  // hosted lists in arrival order (slot s holds the s-th replica placed)
+  if (act) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s < S) {
+        int32_t tt = -1, qq = 0;
+#pragma unroll
+        for (int p = 0; p < SMAX; ++p)
+          if (p == nh - 1 - s) {
+            tt = ht[p];
+            qq = hq[p];
+          }
+        res_e[lane * S + s] = tt >= 0 ? (d * D + tt / MMAX) * M + tt % MMAX : -1;
+        res_q[lane * S + s] = tt >= 0 ? qq : 0;
+      }
+  }
+  return true;
 }
 
 // Tile ordinal bases for the experts of tile-base workgroup `role` (see
@@ -759,6 +778,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
       L.scal[kReplicas] = 0;
       L.scal[kCmax] = static_cast<int32_t>(cmax);
     }
+  } else {
+    // meanwhile the other waves write what is already final (the counts and
+    // the padding between the record's fields: fixed values, so a record is
+    // a pure function of its inputs) and set up the master quotas, so these
+    // stores are long done when the kernel ends
+    const int t1 = tid - 64, n1 = kPlanThreads - 64;
+    for (int e = t1; e < E; e += n1) {
+      rec[a.off[ULTRAEP_PLAN_COUNTS] + e] = L.c[e];
+      L.mq[e] = L.c[e];
+      L.rmask[e] = 0;
+    }
+    // (unrolled, so the field offsets come in with one batch of scalar
+    // loads instead of a dependent load per field)
+#pragma unroll
+    for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
+      const int end = f + 1 < ULTRAEP_PLAN_NUM_FIELDS ? a.off[f + 1] : a.rec_words;
+      for (int wd = a.off[f] + a.len[f] + t1; wd < end; wd += n1) rec[wd] = 0;
+    }
   }
   __syncthreads();
   const int32_t qlb = L.scal[kQlb], tol = L.scal[kTol], K = L.scal[kK], qmax = L.scal[kQmax];
@@ -807,35 +844,51 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     __syncthreads();
   }
 
-  // -- phase 3: the plan record.
-  for (int s = tid; s < R * S; s += kPlanThreads) {
+  // -- phase 3: the plan record.  One thread per slot (there are at most
+  // kPlanThreads) takes its hosted expert and quota from the winning probe,
+  // records them, and takes the quota off the master's (L.mq starts as the
+  // counts) and marks the slot's rank in the expert's mask.
+  // The same thread later places the slot's instance and that of master
+  // tid, whose local takes need the counts of the expert in its rank's
+  // tiles: the first kLocalBatch of those are loaded here, and their latency
+  // passes while the offsets are built.
+  static_assert(ULTRAEP_MAX_TOTAL_SLOTS <= kPlanThreads && ULTRAEP_MAX_EXPERTS <= kPlanThreads,
+                "one thread per slot and per master");
+  int32_t slot_e = -1, slot_q = 0;
+  int32_t xs[kLocalBatch], xm[kLocalBatch];
+  {
+    const int s = tid;
     int32_t e = -1, q = 0;
-    if (!no_moves) {
+    if (s < R * S && !no_moves) {
       const int r = s / S, j = s % S, d = r / D, lr = r % D;
       const int item = (winner - wg0) * a.ndom + d;
       e = L.res[static_cast<size_t>(item) * D * S + lr * S + j];
       q = L.res[static_cast<size_t>(a.items + item) * D * S + lr * S + j];
     }
-    L.slotE[s] = e;
-    L.slotQ[s] = e >= 0 ? q : 0;
-  }
-  for (int e = tid; e < E; e += kPlanThreads) {
-    L.mq[e] = L.c[e];
-    L.rmask[e] = 0;
-  }
-  __syncthreads();
-  for (int s = tid; s < R * S; s += kPlanThreads) {
-    const int32_t e = L.slotE[s];
-    if (e >= 0) {
-      atomicSub(&L.mq[e], L.slotQ[s]);
-      atomicOr(&L.rmask[e], 1ull << ((s / S) % D));
+    q = e >= 0 ? q : 0;
+    slot_e = e;
+    slot_q = q;
+    {
+      const bool pf = local_prefetch(a.tpr);
+      const int rs = S > 0 ? s / S : 0, rm = tid / M;
+#pragma unroll
+      for (int u = 0; u < kLocalBatch; ++u) {
+        xs[u] = pf && e >= 0 ? H[static_cast<int64_t>(local_row(rs * a.tpr, u, (rs + 1) * a.tpr)) * hs + e] : 0;
+        xm[u] = pf && tid < E ? H[static_cast<int64_t>(local_row(rm * a.tpr, u, (rm + 1) * a.tpr)) * hs + tid] : 0;
+      }
     }
-  }
-  if (wave == 0) {
-    uint32_t filled = 0;
-    for (int s0 = 0; s0 < R * S; s0 += 64)
-      filled += __builtin_popcountll(ballot(s0 + lane < R * S && L.slotE[s0 + lane] >= 0));
-    if (lane == 0) L.scal[kReplicas] = static_cast<int32_t>(filled);
+    if (s < R * S) {
+      L.slotE[s] = e;
+      L.slotQ[s] = q;
+      rec[a.off[ULTRAEP_PLAN_SLOT_EXPERT] + s] = e;
+      rec[a.off[ULTRAEP_PLAN_SLOT_QUOTA] + s] = q;
+      if (e >= 0) {
+        atomicSub(&L.mq[e], q);
+        atomicOr(&L.rmask[e], 1ull << ((s / S) % D));
+      }
+    }
+    const uint32_t filled = __builtin_popcountll(ballot(e >= 0));
+    if (lane == 0 && filled) atomicAdd(&L.scal[kReplicas], static_cast<int32_t>(filled));
   }
   __syncthreads();
   // physical loads (recorded as they are written: the scan below turns them
@@ -846,7 +899,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     L.pload[p] = q;
     rec[a.off[ULTRAEP_PLAN_PHYS_LOAD] + p] = q;
   }
-  for (int e = tid; e < E; e += kPlanThreads) L.iptr[e] = 1 + __builtin_popcountll(L.rmask[e]);
+  for (int e = tid; e < E; e += kPlanThreads) {
+    L.iptr[e] = 1 + __builtin_popcountll(L.rmask[e]);
+    rec[a.off[ULTRAEP_PLAN_MASTER_QUOTA] + e] = L.mq[e];
+  }
   for (int r = tid; r < R; r += kPlanThreads) {
     int32_t s = 0;
     for (int j = 0; j < M; ++j) s += L.mq[r * M + j];
@@ -871,21 +927,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
   int32_t* inst_end = rec + a.off[ULTRAEP_PLAN_INST_END];
   int32_t* inst_base = rec + a.off[ULTRAEP_PLAN_INST_BASE];
   int32_t* inst_local = rec + a.off[ULTRAEP_PLAN_INST_LOCAL];
-  for (int x = tid; x < E + R * S; x += kPlanThreads) {
-    int e, r, p;
-    int32_t q;
-    if (x < E) {
-      e = x;
-      r = e / M;
-      p = r * (M + S) + e % M;
-      q = L.mq[e];
-    } else {
-      e = L.slotE[x - E];
-      if (e < 0) continue;
-      r = (x - E) / S;
-      p = r * (M + S) + M + (x - E) % S;
-      q = L.slotQ[x - E];
-    }
+  for (int e = tid; e <= E; e += kPlanThreads) rec[a.off[ULTRAEP_PLAN_INST_PTR] + e] = L.iptr[e];
+  for (int p = tid; p <= P; p += kPlanThreads) rec[a.off[ULTRAEP_PLAN_PHYS_OFF] + p] = L.pload[p];
+  // unused instance entries get fixed values
+  for (int i = L.iptr[E] + tid; i < a.n_inst; i += kPlanThreads) {
+    inst_phys[i] = -1;
+    inst_end[i] = 0;
+    inst_base[i] = 0;
+    inst_local[i] = 0;
+  }
+  // thread tid places master tid and the instance of slot tid
+  auto place = [&](int e, int r, int p, int32_t q, const int32_t (&x0)[kLocalBatch]) {
     const int home = e / M;
     const uint64_t in_domain = D == 64 ? ~0ull : ((1ull << D) - 1);
     const uint64_t m = (L.rmask[e] | (1ull << (home % D))) & in_domain;
@@ -894,17 +946,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     L.iq[i] = q;
     L.iex[i] = e;
     inst_phys[i] = p;
-    // pairs of e from rank r's tiles, eight loads in flight at a time
+    // pairs of e from rank r's tiles: the first batch came in early, the
+    // rest (ranks of more than kLocalBatch tiles) eight loads at a time
+    const int t0 = r * a.tpr, t1 = t0 + a.tpr;
     int32_t own = 0;
-    const int t1 = (r + 1) * a.tpr;
-    for (int t0 = r * a.tpr; t0 < t1; t0 += kLocalBatch) {
+#pragma unroll
+    for (int u = 0; u < kLocalBatch; ++u) own += t0 + u < t1 ? x0[u] : 0;
+    for (int tb = t0 + kLocalBatch; tb < t1; tb += kLocalBatch) {
       int32_t x[kLocalBatch];
 #pragma unroll
-      for (int u = 0; u < kLocalBatch; ++u) x[u] = H[static_cast<int64_t>(local_row(t0, u, t1)) * hs + e];
+      for (int u = 0; u < kLocalBatch; ++u) x[u] = H[static_cast<int64_t>(local_row(tb, u, t1)) * hs + e];
 #pragma unroll
-      for (int u = 0; u < kLocalBatch; ++u) own += t0 + u < t1 ? x[u] : 0;
+      for (int u = 0; u < kLocalBatch; ++u) own += tb + u < t1 ? x[u] : 0;
     }
     inst_local[i] = min(q, own);
+  };
+  if (tid < E) {
+    const int r = tid / M;
+    place(tid, r, r * (M + S) + tid % M, L.mq[tid], xm);
+  }
+  if (tid < R * S && slot_e >= 0) {
+    const int r = tid / S;
+    place(slot_e, r, r * (M + S) + M + tid % S, slot_q, xs);
   }
   __syncthreads();
   // quota ends and first rows: the instances' quotas are scanned once across
@@ -919,31 +982,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
     const int32_t end = L.iq[i + 1] - L.iq[L.iptr[e]];
     inst_end[i] = end;
     inst_base[i] = L.pload[L.instp[i]] - (end - q);
-  }
-  // unused instance entries and the padding between fields get fixed values,
-  // so a record is a pure function of its inputs
-  for (int i = L.iptr[E] + tid; i < a.n_inst; i += kPlanThreads) {
-    inst_phys[i] = -1;
-    inst_end[i] = 0;
-    inst_base[i] = 0;
-    inst_local[i] = 0;
-  }
-  // (unrolled, so the field offsets come in with one batch of scalar loads
-  // instead of a dependent load per field)
-#pragma unroll
-  for (int f = 0; f < ULTRAEP_PLAN_NUM_FIELDS; ++f) {
-    const int end = f + 1 < ULTRAEP_PLAN_NUM_FIELDS ? a.off[f + 1] : a.rec_words;
-    for (int wd = a.off[f] + a.len[f] + tid; wd < end; wd += kPlanThreads) rec[wd] = 0;
-  }
-  for (int e = tid; e < E; e += kPlanThreads) {
-    rec[a.off[ULTRAEP_PLAN_COUNTS] + e] = L.c[e];
-    rec[a.off[ULTRAEP_PLAN_MASTER_QUOTA] + e] = L.mq[e];
-  }
-  for (int e = tid; e <= E; e += kPlanThreads) rec[a.off[ULTRAEP_PLAN_INST_PTR] + e] = L.iptr[e];
-  for (int p = tid; p <= P; p += kPlanThreads) rec[a.off[ULTRAEP_PLAN_PHYS_OFF] + p] = L.pload[p];
-  for (int s = tid; s < R * S; s += kPlanThreads) {
-    rec[a.off[ULTRAEP_PLAN_SLOT_EXPERT] + s] = L.slotE[s];
-    rec[a.off[ULTRAEP_PLAN_SLOT_QUOTA] + s] = L.slotQ[s];
   }
   if (tid < kHeaderWords) {
     int32_t v = 0;
@@ -1104,14 +1142,18 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
   // with the layout, the packed values wait out the steps up to pass 2 in
   // the staging words (pass 1 is done with its lane masks), so they hold no
   // registers meanwhile; the registers take the pairs' weights instead (one
-  // coalesced load per chunk), which arrive while the runs are set up
+  // coalesced load per chunk), which arrive while the runs are set up.  The
+  // weights come through one buffer resource over the tile (one offset
+  // register for all chunks; loads past the tile read 0 and are not used).
   float wl[LAYOUT ? T::kChunks : 1];
   if (LAYOUT) {
 #pragma unroll
     for (int c = 0; c < T::kChunks; ++c) reinterpret_cast<uint32_t*>(S.wst)[c * NT + threadIdx.x] = v[c];
+    const __amdgpu_buffer_rsrc_t r_w = row_rsrc(w + first, static_cast<uint32_t>(n_here) * 4u);
 #pragma unroll
     for (int c = 0; c < T::kChunks; ++c)
-      wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
+      wl[c] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(r_w, (base + c * 64 + lane) * 4, 0, kNonTemporal));
   }
   for (int e = threadIdx.x; e < E; e += NT) {
     const int32_t b0 = S.tcnt[e];

@@ -15,7 +15,9 @@
 //   plant (optional) replaces one index function by a plausible mistake, to
 //   show that the walk catches it: "sum-row" (the histogram sum's batch
 //   without its clamp to the last row), "scan-row" (the same in the tile-base
-//   scan), "scan-ew" (experts per tile-base workgroup not capped at E).
+//   scan), "scan-ew" (experts per tile-base workgroup not capped at E),
+//   "local-first" (the planner's early first batch of the local takes loaded
+//   also for ranks without tiles).
 // Exit status: 0 every index in bounds, 1 a violation (printed), 2 usage or
 // a shape the library refuses.
 #include <cstdio>
@@ -44,6 +46,7 @@ int32_t sum_row_x(int32_t tb, int u, int32_t nch, int32_t ntiles) {
 int32_t scan_row_x(int32_t tb, int u, int32_t ntiles) {
   return plant == "scan-row" ? tb + u : scan_row(tb, u, ntiles);
 }
+bool local_prefetch_x(int32_t tpr) { return plant == "local-first" ? true : local_prefetch(tpr); }
 PlanGrid plan_grid_x(int32_t E, int32_t ntiles) {
   if (plant != "scan-ew") return plan_grid(E, ntiles);
   PlanGrid g;
@@ -205,6 +208,22 @@ int main(int argc, char** argv) {
           if (hbase + static_cast<int64_t>(row + 1) * hs > hist_entries) fail("local take entry", r, row);
         }
     }
+    // the early first batch of the local takes: thread tid loads rank
+    // tid / S's rows for slot tid and rank tid / M's for master tid (any
+    // expert column: the experts are not known yet)
+    if (local_prefetch_x(tpr))
+      for (int tid = 0; tid < kPlanThreads; ++tid)
+        for (int which = 0; which < 2; ++which) {
+          if (which == 0 ? (tid >= R * S) : (tid >= E)) continue;
+          const int32_t r = which == 0 ? tid / S : tid / (E / R);
+          for (int u = 0; u < kLocalBatch; ++u) {
+            const int32_t row = local_row(r * tpr, u, (r + 1) * tpr);
+            if (row < r * tpr || row >= (r + 1) * tpr || row < 0 || row >= ntiles)
+              fail("local take first batch row", tid, r, row);
+            else if (hbase + static_cast<int64_t>(row + 1) * hs > hist_entries)
+              fail("local take first batch entry", tid, r, row);
+          }
+        }
     // the plan record: every field the planner writes, at the extents its
     // loops use, inside the record of its layer
     const int64_t want[ULTRAEP_PLAN_NUM_FIELDS] = {ULTRAEP_HDR_WORDS, E, E, R * S, R * S, P, P + 1,

@@ -5,9 +5,9 @@ and reroute launches with the kernels' own index functions
 (csrc/ultraep_geometry.h) and checks each global index against the buffer
 the library sizes for it.  It runs here over the edge shapes of the GPU
 parity tests and the eight workloads, one and several layers per call, and
-must reject three planted index mistakes of the kind that once faulted the
+must reject four planted index mistakes of the kinds that once faulted the
 plan launch on the GPU (a batch of histogram loads without its clamp to the
-last tile row).
+last tile row; the early local-take loads made for a layer without tokens).
 """
 import os
 import shutil
@@ -71,7 +71,8 @@ def test_deep_workload_all_layers(checker):
     assert rc == 0, out
 
 
-@pytest.mark.parametrize("plant", ["sum-row", "scan-row", "scan-ew"])
-def test_planted_index_mistakes_are_caught(checker, plant):
-    rc, out = run(checker, 8, 4, 1, 4, 8, 256, 2, plant)
+@pytest.mark.parametrize("plant,T", [("sum-row", 256), ("scan-row", 256), ("scan-ew", 256),
+                                     ("local-first", 0)])
+def test_planted_index_mistakes_are_caught(checker, plant, T):
+    rc, out = run(checker, 8, 4, 1, 4, 8, T, 2, plant)
     assert rc == 1 and "out of bounds" in out, out
