@@ -49,25 +49,24 @@ struct Tiling {
 };
 
 // Expert ids of one wave's stretch of a tile: chunk c, lane l holds pair
-// base + 64c + l.  Every load is issued unconditionally (indices past the
-// tile are clamped to its last pair and masked afterwards) so all C loads
-// are in flight together instead of one round trip per chunk.  Ids outside
-// [0, E) and padding become E.
+// base + 64c + l.  Every load is issued unconditionally through one buffer
+// resource over the tile (one offset register for all chunks; loads past the
+// tile read 0 and are masked afterwards), so all C loads are in flight
+// together instead of one round trip per chunk.  Ids outside [0, E) and
+// padding become E.
 template <int C>
 __device__ __forceinline__ void load_tile_ids(const int32_t* __restrict__ src, int base,
                                               int n_here, int lane, int32_t E,
                                               uint32_t (&v)[C]) {
-  const int last = n_here - 1;
-  int32_t raw[C];
+  const __amdgpu_buffer_rsrc_t r = row_rsrc(src, static_cast<uint32_t>(n_here) * 4u);
+  uint32_t raw[C];
 #pragma unroll
   for (int c = 0; c < C; ++c)
-    raw[c] = __builtin_nontemporal_load(src + min(base + c * 64 + lane, last));
+    raw[c] = __builtin_amdgcn_raw_buffer_load_b32(r, (base + c * 64 + lane) * 4, 0, kNonTemporal);
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const uint32_t x = static_cast<uint32_t>(raw[c]);
-    v[c] = (base + c * 64 + lane < n_here && x < static_cast<uint32_t>(E)) ? x
-                                                                           : static_cast<uint32_t>(E);
-  }
+  for (int c = 0; c < C; ++c)
+    v[c] = (base + c * 64 + lane < n_here && raw[c] < static_cast<uint32_t>(E)) ? raw[c]
+                                                                                 : static_cast<uint32_t>(E);
 }
 
 // Exclusive scan of a[0, n) by the calling wave alone (a[n] receives the
@@ -1774,12 +1773,16 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c) v[c] = S_.park[c * NT + threadIdx.x];
   // each pair's routing weight, one coalesced load per chunk, issued here
-  // so that they are in flight behind the LDS work of pass 2
+  // so that they are in flight behind the LDS work of pass 2 (through one
+  // buffer resource over the tile: one offset register for all chunks;
+  // loads past the tile read 0 and are not used)
   float wl[LAYOUT ? T::kChunks : 1];
   if (LAYOUT && !gather_w) {
+    const __amdgpu_buffer_rsrc_t r_w = row_rsrc(w + first, static_cast<uint32_t>(n_here) * 4u);
 #pragma unroll
     for (int c = 0; c < T::kChunks; ++c)
-      wl[c] = __builtin_nontemporal_load(w + first + min(base + c * 64 + lane, n_here - 1));
+      wl[c] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(r_w, (base + c * 64 + lane) * 4, 0, kNonTemporal));
   }
   __syncthreads();
 
