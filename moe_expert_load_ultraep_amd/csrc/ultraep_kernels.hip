@@ -21,13 +21,16 @@ namespace ultraep {
 namespace {
 
 // Lanes of the wave holding the same value v: every lane ORs its lane bit
-// into an LDS word owned by its value, then reads the word back.  LDS
-// operations of one wave complete in program order, so the read sees all of
-// this instruction's ORs; the caller clears the word (one lane per group)
-// before the next use.  Every lane must be active.
+// into an LDS word owned by its value, then reads the word back.  Each half
+// of the wave ORs into its own 32-bit half of the 64-bit word (half the
+// bytes of a 64-bit OR, and equal values of the two halves do not collide);
+// the word read back holds lanes 0-31 in its low half.  LDS operations of
+// one wave complete in program order, so the read sees all of this
+// instruction's ORs; the caller clears the word (one lane per group) before
+// the next use.  Every lane must be active.
 __device__ __forceinline__ uint64_t match_peers_lds(unsigned long long* words, uint32_t v,
                                                     int lane) {
-  atomicOr(&words[v], 1ull << lane);
+  atomicOr(reinterpret_cast<uint32_t*>(words) + 2 * v + (lane >> 5), 1u << (lane & 31));
   return __atomic_load_n(&words[v], __ATOMIC_RELAXED);
 }
 
