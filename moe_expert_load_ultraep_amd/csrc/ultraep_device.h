@@ -124,6 +124,42 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t x) {
   return static_cast<int32_t>(v);
 }
 
+// Aligned segments of N lanes (N a power of two, at most 16, so a segment
+// never crosses a 16-lane row), for work that N lanes share: an inclusive
+// scan (row shifts, each added only where the source lane is in the
+// segment), and the segment's sum and minimum in every lane (the quad swaps
+// and half-row and row mirrors of wave_max).  Every lane of a segment must
+// be active together.
+template <int N>
+__device__ __forceinline__ int32_t segment_inclusive_scan(int32_t x, int sub) {
+  static_assert(N >= 1 && N <= 16 && (N & (N - 1)) == 0, "segments of 1, 2, 4, 8 or 16 lanes");
+  uint32_t v = static_cast<uint32_t>(x), y;
+  if constexpr (N > 1) { y = dpp<0x111>(v); v += sub >= 1 ? y : 0u; }
+  if constexpr (N > 2) { y = dpp<0x112>(v); v += sub >= 2 ? y : 0u; }
+  if constexpr (N > 4) { y = dpp<0x114>(v); v += sub >= 4 ? y : 0u; }
+  if constexpr (N > 8) { y = dpp<0x118>(v); v += sub >= 8 ? y : 0u; }
+  return static_cast<int32_t>(v);
+}
+
+template <int N>
+__device__ __forceinline__ int32_t segment_sum(int32_t x) {
+  uint32_t v = static_cast<uint32_t>(x);
+  if constexpr (N > 1) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (N > 2) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (N > 4) v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (N > 8) v += dpp<0x140>(v);  // row_mirror
+  return static_cast<int32_t>(v);
+}
+
+template <int N>
+__device__ __forceinline__ int32_t segment_min(int32_t x) {
+  if constexpr (N > 1) x = min(x, static_cast<int32_t>(dpp<0xB1>(static_cast<uint32_t>(x))));
+  if constexpr (N > 2) x = min(x, static_cast<int32_t>(dpp<0x4E>(static_cast<uint32_t>(x))));
+  if constexpr (N > 4) x = min(x, static_cast<int32_t>(dpp<0x141>(static_cast<uint32_t>(x))));
+  if constexpr (N > 8) x = min(x, static_cast<int32_t>(dpp<0x140>(static_cast<uint32_t>(x))));
+  return x;
+}
+
 // 16-byte vectors as native clang vectors (the nontemporal builtins take
 // these, not HIP's struct vector types).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -1457,6 +1457,188 @@ __device__ inline void interleave_round(const LocalLds& S_, int i0, int i1, int 
 
 // Two 16-wave workgroups per CU need at most 64 VGPRs per lane (8 waves per
 // SIMD).
+// Lanes that share one expert's record set-up in the locality reroute: the
+// largest power of two, at most 16, with every expert's lanes in one pass
+// of the workgroup (at least one lane; more experts then take more passes).
+__host__ __device__ inline int records_lanes(int E, int threads) {
+  int g = 1;
+  while (2 * g <= 16 && static_cast<int64_t>(E) * 2 * g <= threads) g *= 2;
+  return g;
+}
+
+// Per expert, G lanes together: the tile's runs and the packed record of
+// pass 2.  Record words 0-3: local take, pool offset (contiguous: u = t +
+// it; interleave: the place x counted from the tile's first pool pair = t +
+// it), then contiguous: first instance and end of e's instances;
+// interleave: the bound on x inside the phase, and phase entry base | phase
+// instances << 16.  Words 4-6: local instance's physical expert and first
+// row, and (interleave) u - x.  The loops over e's instances take G
+// instances at a time; a first match is the lowest set bit of the
+// segment's ballot, and a count of earlier instances the set bits below
+// the lane, so the G lanes agree on every value without a reduction.  The
+// tile's later interleave phases (rare) are set up by the segment's first
+// lane alone.
+template <bool INTERLEAVE, bool LAYOUT, int NT, int G>
+__device__ __forceinline__ void local_records(const LocalLds& S_, int32_t* er, int E, int n_inst) {
+  constexpr int EPI = NT / G;
+  const int lane = lane_id();
+  const int sub = lane & (G - 1), seg = lane & ~(G - 1);
+  const uint32_t segmask = (1u << G) - 1, below = (1u << sub) - 1;
+  auto bits = [&](bool pred) { return static_cast<uint32_t>(ballot(pred) >> seg) & segmask; };
+  for (int e0 = 0; e0 < E; e0 += EPI) {
+    const int e = e0 + static_cast<int>(threadIdx.x) / G;
+    if (e >= E) continue;  // whole segments
+    const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
+    int32_t* rec = er + e * kErWords;
+    const int32_t t0 = S_.cntw[e], t1 = t0 + rec[kErCount];
+    const int32_t pbase = rec[kErPool];
+    const int L = rec[kErLoc];
+    const int32_t aL = L >= 0 ? S_.ia[L] : 0;
+    const int32_t u0 = pbase + max(t0, aL) - aL, u1 = pbase + max(t1, aL) - aL;
+    if (LAYOUT && sub == 0) {
+      S_.roff[n_inst + e] = L >= 0 ? max(0, min(t1, aL) - t0) : 0;
+      S_.ro0[n_inst + e] = L >= 0 ? S_.irow[L] + t0 : 0;
+    }
+    int32_t w2, w3, w6 = 0, w7 = -1;
+    if (!INTERLEAVE) {
+      // the first instance whose pool range ends past u0 (the pool ends
+      // grow with the instance), else the last
+      int k = i1 - 1;
+      for (int g0 = i0; g0 < i1 - 1; g0 += G) {
+        const int kk = g0 + sub;
+        const uint32_t hit = bits(kk < i1 - 1 && u0 < S_.ipool[kk] + S_.irho[kk]);
+        if (hit) {
+          k = g0 + __builtin_ctz(hit);
+          break;
+        }
+      }
+      w2 = k;
+      w3 = i1;
+      for (int i = i0 + sub; i < i1; i += G) {
+        const int32_t a = S_.ia[i], r = S_.irho[i], pl0 = S_.ipool[i];
+        if (LAYOUT) {
+          const int32_t a0 = min(max(u0 - pl0, 0), r);
+          const int32_t a1 = min(max(u1 - pl0, 0), r);
+          S_.roff[i] = a1 - a0;
+          S_.ro0[i] = S_.irow[i] + a + a0;
+        }
+        i32x4 ent;
+        ent.x = S_.iphys[i];
+        ent.y = S_.irow[i] + a - pl0;  // row = this + u
+        ent.z = pl0 + r;                // end of the instance's pool range
+        ent.w = 0;
+        *reinterpret_cast<i32x4*>(S_.pi + 4 * i) = ent;
+      }
+    } else {
+      // the first level whose F exceeds u0 (F grows with the level)
+      int j = i1;
+      for (int g0 = i0; g0 < i1; g0 += G) {
+        const int jj = g0 + sub;
+        const uint32_t hit = bits(jj < i1 && S_.fv[jj] > u0);
+        if (hit) {
+          j = g0 + __builtin_ctz(hit);
+          break;
+        }
+      }
+      const int32_t lam0 = j > i0 ? S_.lev[j - 1] : 0;
+      const int32_t f0 = j > i0 ? S_.fv[j - 1] : 0;
+      // the tile's first pool pair of e is round lam0 + q0, place r0 of the
+      // phase; a later pool pair u of the tile is x = u - u0 + r0 places
+      // further (x < kTile + 64, small enough for a float quotient)
+      int n = 0, q0 = 0, r0 = 0;
+      if (j < i1) {
+        const int32_t a = max(S_.act[j], 1);
+        q0 = (u0 - f0) / a;
+        r0 = (u0 - f0) - q0 * a;
+        for (int g0 = i0; g0 < i1; g0 += G) {
+          const int i = g0 + sub;
+          const bool take = i < i1 && S_.irho[i] > lam0;
+          const uint32_t b = bits(take);
+          if (take) {
+            i32x2 ent;
+            ent.x = S_.iphys[i] | (i << 16);
+            ent.y = S_.irow[i] + S_.ia[i] + lam0 + q0;  // row = this + x / a
+            *reinterpret_cast<i32x2*>(S_.al + 2 * (i0 + n + __builtin_popcount(b & below))) = ent;
+          }
+          n += __builtin_popcount(b);
+        }
+      }
+      w2 = j < i1 ? S_.fv[j] - u0 + r0 : 0;  // x below this: in the phase
+      w3 = i0 | (n << 16);
+      w6 = u0 - r0;                           // u = x + this
+      // the later phases the tile's pool pairs of e reach (up to the first
+      // whose end is at or past u1): a header {x bound, x at the phase
+      // start, instances | first entry << 8, rounds before the phase} and
+      // the phase's instances in order, from the tile's pool
+      if (sub == 0 && j < i1 && S_.fv[j] < u1) {
+        int jl = j + 1;
+        while (jl < i1 - 1 && S_.fv[jl] < u1) ++jl;
+        const int nh = jl - j;
+        int ne = 0;
+        for (int jj = j + 1; jj <= jl; ++jj) ne += S_.act[jj];
+        const int hb = atomicAdd(&S_.pcnt[0], nh);
+        const int eb = atomicAdd(&S_.pcnt[1], ne);
+        if (hb + nh <= kPhaseHeaders && eb + ne <= kPhaseEntries) {
+          int ep = eb;
+          for (int jj = j + 1; jj <= jl; ++jj) {
+            const int32_t lamp = S_.lev[jj - 1];
+            i32x4 h;
+            h.x = S_.fv[jj] - w6;
+            h.y = S_.fv[jj - 1] - w6;
+            h.z = S_.act[jj] | (ep << 8);
+            h.w = lamp;
+            *reinterpret_cast<i32x4*>(S_.phdr + 4 * (hb + jj - j - 1)) = h;
+            for (int i = i0; i < i1; ++i) {
+              if (S_.irho[i] > lamp) {
+                i32x2 ent;
+                ent.x = S_.iphys[i] | (i << 16);
+                ent.y = S_.irow[i] + S_.ia[i];
+                *reinterpret_cast<i32x2*>(S_.pent + 2 * ep) = ent;
+                ++ep;
+              }
+            }
+          }
+          w7 = hb | (nh << 16);
+        }
+      }
+      if (LAYOUT) {
+        int32_t tau0, s0, tau1, s1;
+        interleave_round(S_, i0, i1, j, u0, &tau0, &s0);
+        interleave_round(S_, i0, i1, j, u1, &tau1, &s1);
+        int32_t p0 = 0, p1 = 0;  // instances before i still taking in round tau0 / tau1
+        for (int g0 = i0; g0 < i1; g0 += G) {
+          const int i = g0 + sub;
+          const bool on = i < i1;
+          const int32_t r = on ? S_.irho[i] : 0;
+          const uint32_t b0 = bits(on && r > tau0), b1 = bits(on && r > tau1);
+          if (on) {
+            const int32_t c0 = p0 + __builtin_popcount(b0 & below), c1 = p1 + __builtin_popcount(b1 & below);
+            const int32_t a0 = min(r, tau0) + (r > tau0 && c0 < s0 ? 1 : 0);
+            const int32_t a1 = min(r, tau1) + (r > tau1 && c1 < s1 ? 1 : 0);
+            S_.roff[i] = a1 - a0;
+            S_.ro0[i] = S_.irow[i] + S_.ia[i] + a0;
+          }
+          p0 += __builtin_popcount(b0);
+          p1 += __builtin_popcount(b1);
+        }
+      }
+    }
+    if (sub == 0) {
+      i32x4 lo, hi;
+      lo.x = aL;
+      lo.y = pbase - aL - w6;  // u (contiguous) or x (interleave) = t + this
+      lo.z = w2;
+      lo.w = w3;
+      hi.x = L >= 0 ? S_.iphys[L] : -1;
+      hi.y = L >= 0 ? S_.irow[L] : 0;
+      hi.z = w6;
+      hi.w = w7;
+      *reinterpret_cast<i32x4*>(rec) = lo;
+      *reinterpret_cast<i32x4*>(rec + 4) = hi;
+    }
+  }
+}
+
 template <bool INTERLEAVE, bool LAYOUT, int W, bool GATHER = false>
 __global__ __launch_bounds__(TileShape<W>::kThreads)
 __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
@@ -1631,134 +1813,14 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
   }
   __syncthreads();
 
-  // per expert (one thread owns e, its record and its instances' entries):
-  // the tile's runs and the packed record of pass 2.  Record words 0-3:
-  // local take, pool offset (contiguous: u = t + it; interleave: the place x
-  // counted from the tile's first pool pair = t + it), then contiguous: first
-  // instance and end of e's instances; interleave: the bound on x inside the
-  // phase, and phase entry base | phase instances << 16.  Words 4-6: local
-  // instance's physical expert and first row, and (interleave) u - x.
-  for (int e = threadIdx.x; e < E; e += NT) {
-    const int i0 = S_.iptr[e], i1 = S_.iptr[e + 1];
-    int32_t* rec = er + e * kErWords;
-    const int32_t t0 = S_.cntw[e], t1 = t0 + rec[kErCount];
-    const int32_t pbase = rec[kErPool];
-    const int L = rec[kErLoc];
-    const int32_t aL = L >= 0 ? S_.ia[L] : 0;
-    const int32_t u0 = pbase + max(t0, aL) - aL, u1 = pbase + max(t1, aL) - aL;
-    if (LAYOUT) {
-      S_.roff[n_inst + e] = L >= 0 ? max(0, min(t1, aL) - t0) : 0;
-      S_.ro0[n_inst + e] = L >= 0 ? S_.irow[L] + t0 : 0;
-    }
-    int32_t w2, w3, w6 = 0, w7 = -1;
-    if (!INTERLEAVE) {
-      int k = i0;
-      while (k < i1 - 1 && u0 >= S_.ipool[k] + S_.irho[k]) ++k;
-      w2 = k;
-      w3 = i1;
-      for (int i = i0; i < i1; ++i) {
-        const int32_t a = S_.ia[i], r = S_.irho[i], pl0 = S_.ipool[i];
-        if (LAYOUT) {
-          const int32_t a0 = min(max(u0 - pl0, 0), r);
-          const int32_t a1 = min(max(u1 - pl0, 0), r);
-          S_.roff[i] = a1 - a0;
-          S_.ro0[i] = S_.irow[i] + a + a0;
-        }
-        i32x4 ent;
-        ent.x = S_.iphys[i];
-        ent.y = S_.irow[i] + a - pl0;  // row = this + u
-        ent.z = pl0 + r;                // end of the instance's pool range
-        ent.w = 0;
-        *reinterpret_cast<i32x4*>(S_.pi + 4 * i) = ent;
-      }
-    } else {
-      int j = i0;
-      while (j < i1 && S_.fv[j] <= u0) ++j;
-      const int32_t lam0 = j > i0 ? S_.lev[j - 1] : 0;
-      const int32_t f0 = j > i0 ? S_.fv[j - 1] : 0;
-      // the tile's first pool pair of e is round lam0 + q0, place r0 of the
-      // phase; a later pool pair u of the tile is x = u - u0 + r0 places
-      // further (x < kTile + 64, small enough for a float quotient)
-      int n = 0, q0 = 0, r0 = 0;
-      if (j < i1) {
-        const int32_t a = max(S_.act[j], 1);
-        q0 = (u0 - f0) / a;
-        r0 = (u0 - f0) - q0 * a;
-        for (int i = i0; i < i1; ++i) {
-          if (S_.irho[i] > lam0) {
-            i32x2 ent;
-            ent.x = S_.iphys[i] | (i << 16);
-            ent.y = S_.irow[i] + S_.ia[i] + lam0 + q0;  // row = this + x / a
-            *reinterpret_cast<i32x2*>(S_.al + 2 * (i0 + n)) = ent;
-            ++n;
-          }
-        }
-      }
-      w2 = j < i1 ? S_.fv[j] - u0 + r0 : 0;  // x below this: in the phase
-      w3 = i0 | (n << 16);
-      w6 = u0 - r0;                           // u = x + this
-      // the later phases the tile's pool pairs of e reach (up to the first
-      // whose end is at or past u1): a header {x bound, x at the phase
-      // start, instances | first entry << 8, rounds before the phase} and
-      // the phase's instances in order, from the tile's pool
-      if (j < i1 && S_.fv[j] < u1) {
-        int jl = j + 1;
-        while (jl < i1 - 1 && S_.fv[jl] < u1) ++jl;
-        const int nh = jl - j;
-        int ne = 0;
-        for (int jj = j + 1; jj <= jl; ++jj) ne += S_.act[jj];
-        const int hb = atomicAdd(&S_.pcnt[0], nh);
-        const int eb = atomicAdd(&S_.pcnt[1], ne);
-        if (hb + nh <= kPhaseHeaders && eb + ne <= kPhaseEntries) {
-          int ep = eb;
-          for (int jj = j + 1; jj <= jl; ++jj) {
-            const int32_t lamp = S_.lev[jj - 1];
-            i32x4 h;
-            h.x = S_.fv[jj] - w6;
-            h.y = S_.fv[jj - 1] - w6;
-            h.z = S_.act[jj] | (ep << 8);
-            h.w = lamp;
-            *reinterpret_cast<i32x4*>(S_.phdr + 4 * (hb + jj - j - 1)) = h;
-            for (int i = i0; i < i1; ++i) {
-              if (S_.irho[i] > lamp) {
-                i32x2 ent;
-                ent.x = S_.iphys[i] | (i << 16);
-                ent.y = S_.irow[i] + S_.ia[i];
-                *reinterpret_cast<i32x2*>(S_.pent + 2 * ep) = ent;
-                ++ep;
-              }
-            }
-          }
-          w7 = hb | (nh << 16);
-        }
-      }
-      if (LAYOUT) {
-        int32_t tau0, s0, tau1, s1;
-        interleave_round(S_, i0, i1, j, u0, &tau0, &s0);
-        interleave_round(S_, i0, i1, j, u1, &tau1, &s1);
-        int32_t p0 = 0, p1 = 0;  // instances before i still taking in round tau0 / tau1
-        for (int i = i0; i < i1; ++i) {
-          const int32_t r = S_.irho[i];
-          const int32_t a0 = min(r, tau0) + (r > tau0 && p0 < s0 ? 1 : 0);
-          const int32_t a1 = min(r, tau1) + (r > tau1 && p1 < s1 ? 1 : 0);
-          p0 += r > tau0 ? 1 : 0;
-          p1 += r > tau1 ? 1 : 0;
-          S_.roff[i] = a1 - a0;
-          S_.ro0[i] = S_.irow[i] + S_.ia[i] + a0;
-        }
-      }
-    }
-    i32x4 lo, hi;
-    lo.x = aL;
-    lo.y = pbase - aL - w6;  // u (contiguous) or x (interleave) = t + this
-    lo.z = w2;
-    lo.w = w3;
-    hi.x = L >= 0 ? S_.iphys[L] : -1;
-    hi.y = L >= 0 ? S_.irow[L] : 0;
-    hi.z = w6;
-    hi.w = w7;
-    *reinterpret_cast<i32x4*>(rec) = lo;
-    *reinterpret_cast<i32x4*>(rec + 4) = hi;
+  // per expert: the tile's runs and the packed record of pass 2, several
+  // lanes per expert (local_records)
+  switch (records_lanes(E, NT)) {
+    case 16: local_records<INTERLEAVE, LAYOUT, NT, 16>(S_, er, E, n_inst); break;
+    case 8: local_records<INTERLEAVE, LAYOUT, NT, 8>(S_, er, E, n_inst); break;
+    case 4: local_records<INTERLEAVE, LAYOUT, NT, 4>(S_, er, E, n_inst); break;
+    case 2: local_records<INTERLEAVE, LAYOUT, NT, 2>(S_, er, E, n_inst); break;
+    default: local_records<INTERLEAVE, LAYOUT, NT, 1>(S_, er, E, n_inst); break;
   }
   if (LAYOUT) {
     // instance entries beyond the plan's used ones are empty runs
