@@ -538,14 +538,21 @@ __device__ bool greedy_probe_packed(int32_t Q, int d, const PlanParams& a, const
       // part is cut so that what stays queued is 0 or at least the minimum
       // (bitwise logic: short-circuit tests let the compiler sink the donor
       // and queue reductions behind the receiver's)
-      r_amt = fit ? amt : min(static_cast<int32_t>(kmax >> 6), amt - mt);
-      r_amt = (!fit & (r_amt < mt)) ? 0 : r_amt;
-      const bool chain = !fit & (dmax > 0);
-      const int32_t rest = amt - r_amt;
-      x = min(rest, droom);
-      x = ((rest - x > 0) & (rest - x < mt)) ? rest - mt : x;
-      x = chain ? x : 0;
-      if ((!fit & (r_amt == 0) & (dmax == 0)) | (chain & (x < mt))) return false;
+      if (fit) {
+        r_amt = amt;
+      } else {
+        r_amt = min(static_cast<int32_t>(kmax >> 6), amt - mt);
+        r_amt = r_amt >= mt ? r_amt : 0;
+        const int32_t rest = amt - r_amt;
+        if (dmax > 0) {
+          // the donor takes the rest when it has room for all of it, else
+          // at most rest - mt (what stays queued is at least the minimum)
+          x = droom >= rest ? rest : min(droom, rest - mt);
+          if (x < mt) return false;
+        } else if (r_amt == 0) {
+          return false;
+        }
+      }
     } else {
       // the receiver takes the whole piece on a fit, else its whole spare
       if (!fit && kmax == 0 && dmax == 0) return false;
