@@ -674,15 +674,19 @@ __device__ void sum_hist_rows(const uint16_t* __restrict__ H, int hs, int ntiles
         x[u][0] = reinterpret_cast<const uint32_t*>(H)[row * (hs / 2) + q];
       }
     }
+    // rows past the last are masked to zero, not skipped: a load whose
+    // value is used only under a condition may be sunk into that branch and
+    // issued after the others have been waited for
 #pragma unroll
-    for (int u = 0; u < B; ++u)
-      if (tb + u * nch < ntiles) {
+    for (int u = 0; u < B; ++u) {
+      const uint32_t keep = tb + u * nch < ntiles ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-        for (int w = 0; w < W; ++w) {
-          sum[2 * w] += static_cast<int32_t>(x[u][w] & 0xFFFFu);
-          sum[2 * w + 1] += static_cast<int32_t>(x[u][w] >> 16);
-        }
+      for (int w = 0; w < W; ++w) {
+        const uint32_t v = x[u][w] & keep;
+        sum[2 * w] += static_cast<int32_t>(v & 0xFFFFu);
+        sum[2 * w + 1] += static_cast<int32_t>(v >> 16);
       }
+    }
   }
 #pragma unroll
   for (int i = 0; i < 2 * W; ++i) {
@@ -2153,24 +2157,31 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
   // Whenever this workgroup does e's work, its own slot s0 is the first
   // replica summed (the lowest of e's slots in the range), so the first
   // round of s0's gradient and of e's master is loaded before the list below
-  // is known: the data loads then wait on one dependent load (the master
-  // pointer), not on the chain slot -> instance range -> instances.
+  // is known: the gradient loads wait only on the slot's expert (an empty
+  // slot loads nothing), the master's on one more dependent load (its
+  // pointer), and neither on the chain slot -> instance range -> instances.
   const int64_t n4 = numel / 4;
   const f32x4* r4 = reinterpret_cast<const f32x4*>(reps);
-  float* m = masters[e];
-  const bool vec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(reps) & 15) == 0) &&
-                   ((reinterpret_cast<uintptr_t>(m) & 15) == 0);
+  const bool rvec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(reps) & 15) == 0);
   const int64_t span = static_cast<int64_t>(kFoldVecs) * kFoldThreads;
   const int64_t i00 = static_cast<int64_t>(blockIdx.x) * span + threadIdx.x;
   f32x4 g0[kFoldVecs], a0[kFoldVecs];
-  if (vec && m != nullptr) {
+  if (rvec) {
     const f32x4* rq = r4 + static_cast<int64_t>(s0 - slot_begin) * n4;
+#pragma unroll
+    for (int u = 0; u < kFoldVecs; ++u) {
+      const int64_t i = i00 + static_cast<int64_t>(u) * kFoldThreads;
+      g0[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float* m = masters[e];
+  const bool vec = rvec && ((reinterpret_cast<uintptr_t>(m) & 15) == 0);
+  if (vec && m != nullptr) {
     const f32x4* m4 = reinterpret_cast<const f32x4*>(m);
 #pragma unroll
     for (int u = 0; u < kFoldVecs; ++u) {
       const int64_t i = i00 + static_cast<int64_t>(u) * kFoldThreads;
       a0[u] = i < n4 ? __builtin_nontemporal_load(m4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
-      g0[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   if (threadIdx.x < 64) {
@@ -2208,10 +2219,19 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
     // each thread takes kFoldVecs 16-byte vectors a block-width apart, and
     // every load of a replica round is issued before any add or store (the
     // masters and the replica gradients are distinct buffers)
+    // (rounds step by a workgroup-uniform base b0, so each round's stores
+    // go through one buffer resource over its vectors: those past the end
+    // are dropped.  A workgroup's last round is written through at device
+    // scope, so little is left dirty in the L2s for the write-back at the
+    // kernel's end; earlier rounds stay plain non-temporal, the faster form
+    // for long streams.)
     f32x4* m4 = reinterpret_cast<f32x4*>(m);
-    for (int64_t i0 = i00; i0 < n4; i0 += static_cast<int64_t>(gridDim.x) * span) {
+    const int64_t b00 = i00 - threadIdx.x;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * span;
+    for (int64_t b0 = b00; b0 < n4; b0 += step) {
+      const int64_t i0 = b0 + threadIdx.x;
       f32x4 acc[kFoldVecs];
-      if (i0 == i00) {
+      if (b0 == b00) {
 #pragma unroll
         for (int u = 0; u < kFoldVecs; ++u) acc[u] = a0[u];
       } else {
@@ -2223,7 +2243,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
       }
       for (int q = 0; q < n; ++q) {
         f32x4 g[kFoldVecs];
-        if (q == 0 && i0 == i00) {
+        if (q == 0 && b0 == b00) {
           // s_list[0] is s0: its first round is already loaded
 #pragma unroll
           for (int u = 0; u < kFoldVecs; ++u) g[u] = g0[u];
@@ -2243,10 +2263,18 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
           acc[u].w += g[u].w;
         }
       }
+      const __amdgpu_buffer_rsrc_t dst =
+          row_rsrc(m4 + b0, static_cast<uint32_t>((n4 - b0 < span ? n4 - b0 : span) * 16));
+      if (b0 + step >= n4) {
 #pragma unroll
-      for (int u = 0; u < kFoldVecs; ++u) {
-        const int64_t i = i0 + static_cast<int64_t>(u) * kFoldThreads;
-        if (i < n4) __builtin_nontemporal_store(acc[u], m4 + i);
+        for (int u = 0; u < kFoldVecs; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[u]), dst,
+                                                 (threadIdx.x + u * kFoldThreads) * 16, 0, kStreamStore);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kFoldVecs; ++u)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[u]), dst,
+                                                 (threadIdx.x + u * kFoldThreads) * 16, 0, kNonTemporal);
       }
     }
   } else {
