@@ -208,9 +208,9 @@ constexpr int kBufferWord3 = 0x00020000;  // raw buffer, 32-bit data format (gfx
 constexpr int kNonTemporal = 2;           // cache policy bit: non-temporal
 // Non-temporal stores written through at device scope (the sc1 bit): the
 // L2s keep no dirty lines of them for the write-back at the kernel's end.
-// Used for the last stores of a streaming kernel; as the form of every
-// store of a long copy, or of 4-byte scatters, it measured slower than
-// plain non-temporal stores.
+// Used where a streaming kernel's workgroups each store once, at its end;
+// as the form of every store of a long copy, or of 4-byte scatters, it
+// measured slower than plain non-temporal global stores.
 constexpr int kStreamStore = kNonTemporal | 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uint32_t bytes) {
