@@ -2083,7 +2083,7 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
 // permute: bf16 rows into the layout order
 // ------------------------------------------------------------------------
 // One wave per output row: the row's source token is one uniform load, and
-// the row moves in steps of 64 lanes x 4 x 16 bytes.  Every row is addressed
+// the row moves in steps of 64 lanes x 2 x 16 bytes.  Every row is addressed
 // through its own buffer resource whose size is the row's byte length, or 0
 // for a row that must be zero-filled: loads past the size return zeros and
 // stores past it are dropped, so ragged row tails and invalid rows need no

@@ -366,10 +366,13 @@ def test_permute_random_bits_and_capacity():
         assert np.array_equal(out.cpu().numpy().view(np.uint16), want[:cap])
 
 
-@pytest.mark.parametrize("cfg_id,numel", [(3, None), (2, 4097 * 3 + 1), (5, None)])
+@pytest.mark.parametrize("cfg_id,numel", [(3, None), (2, 4097 * 3 + 1), (5, None), (2, None),
+                                           (2, 4 * (1024 * 37 + 5))])
 def test_fold_full_size(cfg_id, numel):
-    """One rank's slots folded at full size (vector path), and an odd numel
-    (scalar path)."""
+    """One rank's slots folded at full size (vector path: several rounds per
+    workgroup at workloads 3 and 5, one round at workload 2), an odd numel
+    (scalar path), and a one-round grid whose last workgroup covers only 5
+    vectors (the ragged end of the one-round store form)."""
     w = W.CONFIGS[cfg_id]
     idx, _ = routing_cached(cfg_id, 0, 0)
     c, dropped = O.count(idx, w.E)
