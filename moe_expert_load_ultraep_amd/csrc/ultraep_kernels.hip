@@ -107,10 +107,16 @@ __device__ void wave_exclusive_scan(int32_t* a, int n) {
 // valid id to an LDS counter.  The order of the additions does not matter
 // here, so a plain LDS atomic per pair is the cheapest form: equal ids in one
 // wave instruction only serialise inside the LDS, they cost no VALU work.
+// Lanes 8q..8q+7 add into copy q of the counters (kCountCopies copies, rows
+// of E + 1 words so the copies of one expert fall in different banks): with
+// top-8 routing those lanes hold one token's 8 distinct experts, so a hot
+// expert's atomics in one instruction hit 8 different words instead of one.
+// The copies are summed when the row is written.
 // A tile holds at most kTile pairs, so its counts are stored as 16-bit
 // values, rows of hist_stride(E) entries: the planner reads every row, and
 // half the bytes is half its wait.
 using CountTile = TileShape<16>;
+constexpr int kCountCopies = 8;
 
 __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
     const int32_t* __restrict__ idx, int32_t N, int32_t TK, int32_t tpr, int32_t E, int32_t ntiles,
@@ -120,20 +126,26 @@ __global__ __launch_bounds__(CountTile::kThreads) void count_kernel(
   const int64_t blk = blockIdx.x;
   const int32_t layer = static_cast<int32_t>(blk / ntiles);
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
-  for (int i = threadIdx.x; i < E; i += T::kThreads) s_cnt[i] = 0;
+  for (int i = threadIdx.x; i < kCountCopies * (E + 1); i += T::kThreads) s_cnt[i] = 0;
   const TileSpan sp = tile_span(layer, tile, N, TK, tpr);
   const int32_t* src = idx + sp.first;
   const int n_here = sp.n;
   uint32_t v[T::kChunks];
   load_tile_ids(src, (threadIdx.x >> 6) * T::kWavePairs, n_here, lane_id(), E, v);
   __syncthreads();
+  int32_t* mine = s_cnt + (lane_id() / (64 / kCountCopies)) * (E + 1);
 #pragma unroll
   for (int c = 0; c < T::kChunks; ++c)
-    if (v[c] < static_cast<uint32_t>(E)) atomicAdd(&s_cnt[v[c]], 1);
+    if (v[c] < static_cast<uint32_t>(E)) atomicAdd(&mine[v[c]], 1);
   __syncthreads();
   uint16_t* dst = hist + (static_cast<int64_t>(layer) * ntiles + tile) * hist_stride(E);
-  for (int i = threadIdx.x; i < hist_stride(E); i += T::kThreads)
-    dst[i] = static_cast<uint16_t>(i < E ? s_cnt[i] : 0);
+  for (int i = threadIdx.x; i < hist_stride(E); i += T::kThreads) {
+    int32_t n = 0;
+    if (i < E)
+#pragma unroll
+      for (int q = 0; q < kCountCopies; ++q) n += s_cnt[q * (E + 1) + i];
+    dst[i] = static_cast<uint16_t>(n);
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -747,15 +759,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const uint16_t* __re
       cmax = max(cmax, wave_max(e0 + lane < E ? static_cast<uint32_t>(L.c[e0 + lane]) : 0u));
     // domain loads by LDS atomics (L.dom starts at zero): one instruction
     // per 64 ranks instead of a serial sum per domain
+    // (when a domain spans whole waves of ranks, its load is the wave sums
+    // of its ranks, added by one lane, instead of 64 atomics on one word)
+    const bool wide = D % 64 == 0;
     for (int r0 = 0; r0 < R; r0 += 64) {
       const int r = r0 + lane;
       int32_t h = 0;
       if (r < R) {
         for (int j = 0; j < M; ++j) h += L.c[r * M + j];
         L.H[r] = h;
-        atomicAdd(&L.dom[r / D], h);
+        if (!wide) atomicAdd(&L.dom[r / D], h);
       }
-      total += wave_sum(static_cast<uint32_t>(h));
+      const uint32_t hsum = wave_sum(static_cast<uint32_t>(h));
+      if (wide && lane == 0) L.dom[r0 / D] += static_cast<int32_t>(hsum);
+      total += hsum;
       qmax = max(qmax, wave_max(static_cast<uint32_t>(h)));
     }
     for (int d0 = 0; d0 < a.ndom; d0 += 64) {
@@ -2144,22 +2161,40 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 constexpr int kFoldThreads = 256;
 constexpr int kFoldMaxReps = 64;
 constexpr int kFoldVecs = 4;  // 16-byte vectors in flight per lane and stream
+constexpr int kFoldScan = 4;  // 64-slot chunks of the range wave 0 loads at once
+constexpr int kFoldPtrs = (ULTRAEP_MAX_EXPERTS + kFoldThreads - 1) / kFoldThreads;
 
 __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
-    const int32_t* __restrict__ slot_expert, const int32_t* __restrict__ inst_ptr,
-    const int32_t* __restrict__ inst_phys, int32_t M, int32_t S, float* const* __restrict__ masters,
+    const int32_t* __restrict__ slot_expert, int32_t E, float* const* __restrict__ masters,
     const float* __restrict__ reps, int64_t numel, int32_t slot_begin, int32_t slot_end) {
   __shared__ int32_t s_list[kFoldMaxReps];
   __shared__ int32_t s_n;
+  __shared__ float* s_mptr[ULTRAEP_MAX_EXPERTS];
   const int32_t s0 = slot_begin + static_cast<int32_t>(blockIdx.y);
+  const int32_t nsl = slot_end - slot_begin;
+  // The loads that wait on nothing go out first and together: this slot's
+  // expert, the experts of the range's first slots (wave 0) and every master
+  // pointer.  e's replicas in the range are the slots whose expert is e, in
+  // ascending slot id (the order the fold sums them), so the list is one
+  // ballot away and the master's address one LDS read, where a walk of e's
+  // instances had cost two more dependent loads and the pointer one.
   const int32_t e = slot_expert[s0];
-  if (e < 0) return;
+  int32_t se[kFoldScan];
+  if (threadIdx.x < 64) {
+#pragma unroll
+    for (int c = 0; c < kFoldScan; ++c)
+      se[c] = c * 64 < nsl ? slot_expert[slot_begin + min(c * 64 + static_cast<int32_t>(threadIdx.x), nsl - 1)] : -1;
+  }
+  float* mp[kFoldPtrs];
+#pragma unroll
+  for (int c = 0; c < kFoldPtrs; ++c)
+    mp[c] = c * kFoldThreads < E ? masters[min(c * kFoldThreads + static_cast<int32_t>(threadIdx.x), E - 1)]
+                                 : nullptr;
+  if (e < 0 || e >= E) return;
   // Whenever this workgroup does e's work, its own slot s0 is the first
   // replica summed (the lowest of e's slots in the range), so the first
-  // round of s0's gradient and of e's master is loaded before the list below
-  // is known: the gradient loads wait only on the slot's expert (an empty
-  // slot loads nothing), the master's on one more dependent load (its
-  // pointer), and neither on the chain slot -> instance range -> instances.
+  // round of s0's gradient is loaded before the list is known: those loads
+  // wait only on the slot's expert (an empty slot loads nothing).
   const int64_t n4 = numel / 4;
   const f32x4* r4 = reinterpret_cast<const f32x4*>(reps);
   const bool rvec = (numel % 4 == 0) && ((reinterpret_cast<uintptr_t>(reps) & 15) == 0);
@@ -2174,7 +2209,39 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
       g0[u] = i < n4 ? __builtin_nontemporal_load(rq + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  float* m = masters[e];
+#pragma unroll
+  for (int c = 0; c < kFoldPtrs; ++c) {
+    const int32_t x = c * kFoldThreads + static_cast<int32_t>(threadIdx.x);
+    if (x < E) s_mptr[x] = mp[c];
+  }
+  if (threadIdx.x < 64) {
+    // the range's slots of expert e, kept in order; the workgroups of the
+    // lowest of them do e's work
+    const int lane = threadIdx.x;
+    int n = 0;
+    bool first = true;
+    for (int32_t b = 0; b < nsl; b += kFoldScan * 64) {
+      if (b > 0) {
+#pragma unroll
+        for (int c = 0; c < kFoldScan; ++c)
+          se[c] = b + c * 64 < nsl ? slot_expert[slot_begin + min(b + c * 64 + lane, nsl - 1)] : -1;
+      }
+#pragma unroll
+      for (int c = 0; c < kFoldScan; ++c) {
+        const int32_t i = b + c * 64 + lane;
+        const int32_t s = (i < nsl && se[c] == e) ? i : -1;
+        const uint64_t mk = ballot(s >= 0);
+        if (n == 0 && mk != 0)
+          first = static_cast<int32_t>(readlane(static_cast<uint32_t>(s), lowest_lane(mk))) == s0 - slot_begin;
+        const int at = n + count_below(mk);
+        if (s >= 0 && at < kFoldMaxReps) s_list[at] = s;
+        n += __builtin_popcountll(mk);
+      }
+    }
+    if (lane == 0) s_n = first ? n : 0;
+  }
+  __syncthreads();
+  float* m = s_mptr[e];
   const bool vec = rvec && ((reinterpret_cast<uintptr_t>(m) & 15) == 0);
   if (vec && m != nullptr) {
     const f32x4* m4 = reinterpret_cast<const f32x4*>(m);
@@ -2184,33 +2251,6 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(
       a0[u] = i < n4 ? __builtin_nontemporal_load(m4 + i) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  if (threadIdx.x < 64) {
-    // e's instances are in ascending physical id, i.e. ascending slot id for
-    // its replicas: wave 0 reads them 64 at a time and keeps, in order, those
-    // in the range; the workgroups of the lowest of them do e's work
-    const int lane = threadIdx.x;
-    const int32_t i0 = inst_ptr[e], i1 = inst_ptr[e + 1];
-    int n = 0;
-    bool first = true;
-    for (int32_t b = i0; b < i1; b += 64) {
-      const int32_t i = b + lane;
-      int32_t s = -1;
-      if (i < i1) {
-        const int32_t p = inst_phys[i];
-        const int32_t j = p % (M + S);
-        const int32_t q = (p / (M + S)) * S + (j - M);
-        s = (j >= M && q >= slot_begin && q < slot_end) ? q : -1;
-      }
-      const uint64_t mk = ballot(s >= 0);
-      if (n == 0 && mk != 0)
-        first = static_cast<int32_t>(readlane(static_cast<uint32_t>(s), lowest_lane(mk))) == s0;
-      const int at = n + count_below(mk);
-      if (s >= 0 && at < kFoldMaxReps) s_list[at] = s - slot_begin;
-      n += __builtin_popcountll(mk);
-    }
-    if (lane == 0) s_n = first ? n : 0;
-  }
-  __syncthreads();
   const int n = min(s_n, kFoldMaxReps);
   if (n == 0 || m == nullptr) return;
 
@@ -2461,7 +2501,8 @@ hipError_t launch_balance(const Shape& sh, int32_t L, const int32_t* idx, const 
   int32_t* tbase = ws + static_cast<int64_t>(L) * ntiles * sh.E;
   if (blocks > 0) {
     hipLaunchKernelGGL(count_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(CountTile::kThreads),
-                       sizeof(int32_t) * sh.E, st, idx, N, TK, tl.tpr, sh.E, ntiles, hist);
+                       sizeof(int32_t) * kCountCopies * (sh.E + 1), st, idx, N, TK, tl.tpr, sh.E, ntiles,
+                       hist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2548,9 +2589,8 @@ hipError_t launch_fold(const Shape& sh, const int32_t* plan, float* const* maste
   const int64_t want = (numel + per_block - 1) / per_block;
   const uint32_t bx = static_cast<uint32_t>(want < 2048 ? want : 2048);
   hipLaunchKernelGGL(fold_kernel, dim3(bx, static_cast<uint32_t>(nslots)), dim3(kFoldThreads), 0, st,
-                     plan + sh.lay.off[ULTRAEP_PLAN_SLOT_EXPERT], plan + sh.lay.off[ULTRAEP_PLAN_INST_PTR],
-                     plan + sh.lay.off[ULTRAEP_PLAN_INST_PHYS], sh.M, sh.S, masters, reps, numel,
-                     slot_begin, slot_end);
+                     plan + sh.lay.off[ULTRAEP_PLAN_SLOT_EXPERT], sh.E, masters, reps, numel, slot_begin,
+                     slot_end);
   return hipGetLastError();
 }
 
