@@ -47,6 +47,21 @@ __host__ __device__ inline TileSpan tile_span(int64_t layer, int32_t tile, int32
   return {layer * N + tile0, tile0, rest < kTile ? rest : kTile};
 }
 
+// Workgroups of one launch are handed to the 8 XCDs in turn (workgroup g to
+// XCD g % 8), and each XCD has its own L2.  The reroute kernels take their
+// (layer, tile) from xcd_block, which gives the workgroups of one XCD
+// consecutive tiles: neighbouring tiles write the two ends of the same
+// layout runs, so the lines they share meet in one L2 instead of going to
+// HBM twice as partial lines.  A bijection on [0, n): the first 8*(n/8)
+// blocks are regrouped, the n % 8 last ones keep their index.
+constexpr int kXcds = 8;
+
+__host__ __device__ inline int64_t xcd_block(int64_t g, int64_t n) {
+  const int64_t per = n / kXcds;
+  if (g >= per * kXcds) return g;
+  return (g % kXcds) * per + g / kXcds;
+}
+
 // ---- the plan launch -------------------------------------------------------
 // Per layer, one planner workgroup (role 0) and scan_wgs tile-base workgroups
 // (roles 1..scan_wgs), each of the latter covering scan_ew experts: enough

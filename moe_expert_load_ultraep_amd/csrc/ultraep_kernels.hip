@@ -1126,7 +1126,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_kernel(
       S.sn = reinterpret_cast<uint16_t*>(q);
     }
   }
-  const int64_t blk = blockIdx.x;
+  const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
   const int32_t layer = static_cast<int32_t>(blk / ntiles);
   const int32_t tile = static_cast<int32_t>(blk % ntiles);
   const int32_t* plan = plans + static_cast<int64_t>(layer) * rec_words;
@@ -1719,7 +1719,7 @@ __attribute__((amdgpu_waves_per_eu(W == 16 ? 8 : 1))) void reroute_local_kernel(
       S_.ro0 = q; q += n_inst + E;
     }
   }
-  const int64_t blkid = blockIdx.x;
+  const int64_t blkid = xcd_block(blockIdx.x, gridDim.x);
   const int32_t layer = static_cast<int32_t>(blkid / ntiles);
   const int32_t tile = static_cast<int32_t>(blkid % ntiles);
   const int32_t src_rank = tile / tpr;

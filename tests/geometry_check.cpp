@@ -17,7 +17,8 @@
 //   without its clamp to the last row), "scan-row" (the same in the tile-base
 //   scan), "scan-ew" (experts per tile-base workgroup not capped at E),
 //   "local-first" (the planner's early first batch of the local takes loaded
-//   also for ranks without tiles).
+//   also for ranks without tiles), "xcd-tail" (the reroute's XCD block order
+//   applied also to the blocks past the last whole group of eight).
 // Exit status: 0 every index in bounds, 1 a violation (printed), 2 usage or
 // a shape the library refuses.
 #include <cstdio>
@@ -47,6 +48,9 @@ int32_t scan_row_x(int32_t tb, int u, int32_t ntiles) {
   return plant == "scan-row" ? tb + u : scan_row(tb, u, ntiles);
 }
 bool local_prefetch_x(int32_t tpr) { return plant == "local-first" ? true : local_prefetch(tpr); }
+int64_t xcd_block_x(int64_t g, int64_t n) {
+  return plant == "xcd-tail" ? (g % kXcds) * (n / kXcds) + g / kXcds : xcd_block(g, n);
+}
 PlanGrid plan_grid_x(int32_t E, int32_t ntiles) {
   if (plant != "scan-ew") return plan_grid(E, ntiles);
   PlanGrid g;
@@ -242,14 +246,28 @@ int main(int argc, char** argv) {
         break;
       }
 
-  // ---- reroute: one workgroup per (layer, tile), as count ----
-  for (int64_t blk = 0; blk < static_cast<int64_t>(L) * ntiles; ++blk) {
+  // ---- reroute: one workgroup per (layer, tile), as count, in the XCD
+  // order: every (layer, tile) taken by exactly one workgroup ----
+  const int64_t nrb = static_cast<int64_t>(L) * ntiles;
+  std::vector<int> taken(static_cast<size_t>(nrb), 0);
+  for (int64_t g = 0; g < nrb; ++g) {
+    const int64_t blk = xcd_block_x(g, nrb);
+    if (blk < 0 || blk >= nrb) {
+      fail("reroute block order", g, blk);
+      continue;
+    }
+    ++taken[static_cast<size_t>(blk)];
     const int32_t layer = static_cast<int32_t>(blk / ntiles), tile = static_cast<int32_t>(blk % ntiles);
     const TileSpan sp = tile_span(layer, tile, N, TK, tpr);
     if (sp.first + sp.n > pairs) fail("reroute pairs", blk, sp.first);
     const int64_t b = tbase_at + (static_cast<int64_t>(layer) * ntiles + tile) * E;
     if (b < tbase_at || b + E > ws_words) fail("reroute tile bases", blk, b);
   }
+  for (int64_t i = 0; i < nrb; ++i)
+    if (taken[static_cast<size_t>(i)] != 1) {
+      fail("reroute tile not taken once", i, taken[static_cast<size_t>(i)]);
+      break;
+    }
 
   ultraep_destroy(ctx);
   if (fails) {

@@ -5,9 +5,11 @@ and reroute launches with the kernels' own index functions
 (csrc/ultraep_geometry.h) and checks each global index against the buffer
 the library sizes for it.  It runs here over the edge shapes of the GPU
 parity tests and the eight workloads, one and several layers per call, and
-must reject four planted index mistakes of the kinds that once faulted the
-plan launch on the GPU (a batch of histogram loads without its clamp to the
-last tile row; the early local-take loads made for a layer without tokens).
+must reject planted index mistakes of the kinds that once faulted the plan
+launch on the GPU (a batch of histogram loads without its clamp to the last
+tile row; the early local-take loads made for a layer without tokens), and a
+reroute block order that is not a bijection when the grid is not a multiple
+of eight workgroups.
 """
 import os
 import shutil
@@ -76,3 +78,11 @@ def test_deep_workload_all_layers(checker):
 def test_planted_index_mistakes_are_caught(checker, plant, T):
     rc, out = run(checker, 8, 4, 1, 4, 8, T, 2, plant)
     assert rc == 1 and "out of bounds" in out, out
+
+
+def test_planted_block_order_mistake_is_caught(checker):
+    # 3 layers of 4 tiles: 12 reroute workgroups, 4 past the last group of 8
+    rc, out = run(checker, 8, 4, 1, 4, 3, 256, 2, "xcd-tail")
+    assert rc == 1 and "reroute" in out, out
+    rc, out = run(checker, 8, 4, 1, 4, 3, 256, 2)
+    assert rc == 0, out
