@@ -2099,21 +2099,25 @@ __global__ __launch_bounds__(256) void layout_kernel(const int32_t* __restrict__
 // ------------------------------------------------------------------------
 // permute: bf16 rows into the layout order
 // ------------------------------------------------------------------------
-// One wave per output row: the row's source token is one uniform load, and
-// the row moves in steps of 64 lanes x 2 x 16 bytes.  Every row is addressed
-// through its own buffer resource whose size is the row's byte length, or 0
-// for a row that must be zero-filled: loads past the size return zeros and
-// stores past it are dropped, so ragged row tails and invalid rows need no
-// per-lane branches.  Loads and stores are non-temporal (each row is streamed
-// once).  Launch-shape sweeps on a full-size segment (H = 4096) put one row
-// per wave with 2 vectors per lane in flight ahead of 4 or 8, of several
-// rows per wave, and of persistent waves (with the tokens of 64 rows in one
-// load, and with the next row's loads issued before the current row's
-// stores): many small independent streams keep more of HBM's channels busy
-// than a few deep ones.  Rows of 4096, 5120 and 7168 elements are whole
-// multiples of the 128 vectors one round moves.
+// One wave per 1 KiB chunk of an output row (64 lanes x one 16-byte vector):
+// the row's source token is one uniform load, and the chunk moves with one
+// load and one store per lane.  Every row is addressed through its own
+// buffer resource whose size is the row's byte length, or 0 for a row that
+// must be zero-filled: loads past the size return zeros and stores past it
+// are dropped, so ragged row tails and invalid rows need no per-lane
+// branches.  Loads and stores are non-temporal (each row is streamed once).
+// Launch-shape sweeps on a full-size segment (H = 4096, 66,191 rows) put the
+// 1 KiB chunk per wave first: 170 us of kernel time against 173 us for 2 KiB
+// chunks (two rounds of one vector), 179 us for 2 KiB in one round, 183 us
+// for 4 KiB, 185 us for the whole row per wave (four rounds of two vectors),
+// 195 us for the whole row in one round, and 252 us for 512-byte chunks of
+// 8-byte vectors.  A row's chunks are neighbouring waves, so the row's
+// source bytes are requested together; many small independent streams keep
+// more of HBM's channels busy than a few deep ones.
 constexpr int kPermThreads = 256;
-constexpr int kPermUnroll = 2;
+constexpr int kPermChunk = 64;  // 16-byte vectors per wave
+
+__host__ __device__ inline int32_t perm_chunks(int32_t H8) { return (H8 + kPermChunk - 1) / kPermChunk; }
 
 __device__ __forceinline__ int32_t perm_token(int32_t n, int32_t k, int64_t hidden_rows) {
   const int32_t t = n >= 0 ? n / k : -1;
@@ -2129,24 +2133,20 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   const int lane = lane_id();
   const uint32_t rowb = static_cast<uint32_t>(H8) * 16u;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kPermThreads / 64);
+  const int32_t nch = perm_chunks(H8);
   // wave-uniform values go through readfirstlane so the buffer resources
   // built from them live in scalar registers
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  for (int64_t row = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + wv; row < rows;
-       row += nwaves) {
+  for (int64_t item = static_cast<int64_t>(blockIdx.x) * (kPermThreads / 64) + wv; item < rows * nch;
+       item += nwaves) {
+    const int64_t row = item / nch;
+    const int32_t c0 = static_cast<int32_t>(item - row * nch) * kPermChunk;
     const int32_t t = __builtin_amdgcn_readfirstlane(perm_token(inv[seg0 + row], k, hidden_rows));
     const __amdgpu_buffer_rsrc_t src =
         row_rsrc(hidden + static_cast<int64_t>(t < 0 ? 0 : t) * H8, t < 0 ? 0u : rowb);
     const __amdgpu_buffer_rsrc_t dst = row_rsrc(out + row * H8, rowb);
-    for (int c0 = 0; c0 < H8; c0 += 64 * kPermUnroll) {
-      u32x4 x[kPermUnroll];
-#pragma unroll
-      for (int u = 0; u < kPermUnroll; ++u)
-        x[u] = __builtin_amdgcn_raw_buffer_load_b128(src, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
-#pragma unroll
-      for (int u = 0; u < kPermUnroll; ++u)
-        __builtin_amdgcn_raw_buffer_store_b128(x[u], dst, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
-    }
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(src, (c0 + lane) * 16, 0, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(x, dst, (c0 + lane) * 16, 0, kNonTemporal);
   }
 }
 
@@ -2571,7 +2571,7 @@ hipError_t launch_permute(const Shape& sh, const int32_t* plan, const int32_t* i
                           const uint16_t* hidden, int64_t hidden_rows, int32_t H, int32_t p_begin,
                           int32_t p_end, uint16_t* out, int64_t cap, hipStream_t st) {
   if (cap <= 0 || p_begin == p_end) return hipSuccess;
-  const int64_t want = (cap + 3) / 4;  // one row per wave
+  const int64_t want = (cap * perm_chunks(H / 8) + kPermThreads / 64 - 1) / (kPermThreads / 64);  // one chunk per wave
   const uint32_t blocks = static_cast<uint32_t>(want < (1 << 20) ? want : (1 << 20));
   hipLaunchKernelGGL(permute_kernel, dim3(blocks), dim3(kPermThreads), 0, st,
                      plan + sh.lay.off[ULTRAEP_PLAN_PHYS_OFF], inv, k,
