@@ -92,12 +92,16 @@ KERNEL_SOURCE = os.path.join(ROOT, "moe_expert_load_ultraep_amd", "csrc", "ultra
 
 
 def permute_source_sha256():
-    """Hash of the permute kernel's source (its comment block, constants,
-    helpers and body), so recorded counters go stale only when it changes."""
+    """Hash of the permute kernel's source (its constants, helpers and body,
+    not its comment block), so recorded counters go stale only when the
+    code changes; None when the kernel cannot be found."""
     import hashlib
     text = open(KERNEL_SOURCE).read()
-    start = text.index("// One wave per output row")
-    end = text.index("\n}\n", text.index("void permute_kernel(", start)) + 3
+    try:
+        start = text.index("constexpr int kPermThreads")
+        end = text.index("\n}\n", text.index("void permute_kernel(", start)) + 3
+    except ValueError:
+        return None
     return hashlib.sha256(text[start:end].encode()).hexdigest()
 
 

@@ -24,9 +24,17 @@ constexpr int kRowsInFlight = 4;    // rows of one token loaded together
 constexpr int kChunksInFlight = 2;  // 16-byte column chunks per lane per row
 
 // y[t] = sum_j w[g, j] * rows[pos[g*k + j]] for g = g0 + t (w = 1 when not
-// WEIGHTED).  Column chunks are the outer loop so each chunk's fp32
-// accumulators stay in registers while the k rows stream through; the rows
-// of a token are summed in ascending j.
+// WEIGHTED).  One wave per (token, 1 KiB column chunk: 64 lanes x one 16-byte
+// vector): the chunk of up to kCombRows rows is loaded at once and summed in
+// ascending j into fp32 accumulators, eight per lane.  A token's chunks are
+// neighbouring waves, so its rows are requested together; many short
+// independent streams keep more HBM channels busy than one wave walking a
+// token's columns.
+constexpr int kCombChunk = 64;  // 16-byte vectors per wave
+constexpr int kCombRows = 8;    // rows of one token loaded together
+
+__host__ __device__ inline int32_t comb_chunks(int32_t H8) { return (H8 + kCombChunk - 1) / kCombChunk; }
+
 template <bool WEIGHTED>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ w, int32_t k,
@@ -36,7 +44,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   const uint32_t rowb = static_cast<uint32_t>(H8) * 16u;
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kCombWaves;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kCombWaves + wv; t < ntok; t += nwaves) {
+  const int32_t nch = comb_chunks(H8);
+  for (int64_t item = static_cast<int64_t>(blockIdx.x) * kCombWaves + wv; item < ntok * nch;
+       item += nwaves) {
+    const int64_t t = item / nch;
+    const int32_t c0 = static_cast<int32_t>(item - t * nch) * kCombChunk;
     const int64_t n0 = (g0 + t) * k;
     // lane j < k holds pair j's layout row (-1 when dropped) and weight
     int32_t pj = -1;
@@ -46,50 +58,38 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
       pj = (p >= 0 && p < layout_rows) ? p : -1;
       if (WEIGHTED) wj = w[n0 + lane];
     }
-    const __amdgpu_buffer_rsrc_t dst = row_rsrc(out + t * H8, rowb);
-    for (int c0 = 0; c0 < H8; c0 += 64 * kChunksInFlight) {
-      float acc[kChunksInFlight][8];
+    float acc[8];
 #pragma unroll
-      for (int u = 0; u < kChunksInFlight; ++u)
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += kCombRows) {
+      u32x4 x[kCombRows];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
-      for (int j0 = 0; j0 < k; j0 += kRowsInFlight) {
-        u32x4 x[kRowsInFlight][kChunksInFlight];
+      for (int r = 0; r < kCombRows; ++r) {
+        const int j = j0 + r;
+        const int32_t p = static_cast<int32_t>(readlane(static_cast<uint32_t>(pj), j < k ? j : 0));
+        const bool live = j < k && p >= 0;
+        const __amdgpu_buffer_rsrc_t src =
+            row_rsrc(rows + static_cast<int64_t>(live ? p : 0) * H8, live ? rowb : 0u);
+        x[r] = __builtin_amdgcn_raw_buffer_load_b128(src, (c0 + lane) * 16, 0, kNonTemporal);
+      }
 #pragma unroll
-        for (int r = 0; r < kRowsInFlight; ++r) {
-          const int j = j0 + r;
-          const int32_t p = static_cast<int32_t>(readlane(static_cast<uint32_t>(pj), j < k ? j : 0));
-          const bool live = j < k && p >= 0;
-          const __amdgpu_buffer_rsrc_t src =
-              row_rsrc(rows + static_cast<int64_t>(live ? p : 0) * H8, live ? rowb : 0u);
+      for (int r = 0; r < kCombRows; ++r) {
+        const int j = j0 + r;
+        const float wt = WEIGHTED ? readlane_f(wj, j < k ? j : 0) : 1.f;
+        if (j < k) {
 #pragma unroll
-          for (int u = 0; u < kChunksInFlight; ++u)
-            x[r][u] = __builtin_amdgcn_raw_buffer_load_b128(src, (c0 + u * 64 + lane) * 16, 0,
-                                                             kNonTemporal);
-        }
-#pragma unroll
-        for (int r = 0; r < kRowsInFlight; ++r) {
-          const int j = j0 + r;
-          const float wt = WEIGHTED ? readlane_f(wj, j < k ? j : 0) : 1.f;
-          if (j < k) {
-#pragma unroll
-            for (int u = 0; u < kChunksInFlight; ++u)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                acc[u][2 * q] += wt * bf16_lo(x[r][u][q]);
-                acc[u][2 * q + 1] += wt * bf16_hi(x[r][u][q]);
-              }
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += wt * bf16_lo(x[r][q]);
+            acc[2 * q + 1] += wt * bf16_hi(x[r][q]);
           }
         }
       }
-#pragma unroll
-      for (int u = 0; u < kChunksInFlight; ++u) {
-        u32x4 y;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = pack_bf16(acc[u][2 * q], acc[u][2 * q + 1]);
-        __builtin_amdgcn_raw_buffer_store_b128(y, dst, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
-      }
     }
+    u32x4 y;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) y[q] = pack_bf16(acc[2 * q], acc[2 * q + 1]);
+    const __amdgpu_buffer_rsrc_t dst = row_rsrc(out + t * H8, rowb);
+    __builtin_amdgcn_raw_buffer_store_b128(y, dst, (c0 + lane) * 16, 0, kNonTemporal);
   }
 }
 
@@ -170,8 +170,8 @@ __global__ __launch_bounds__(kCombThreads) void combine_backward_kernel(
   }
 }
 
-uint32_t comb_blocks(int64_t ntok) {
-  const int64_t want = (ntok + kCombWaves - 1) / kCombWaves;
+uint32_t comb_blocks(int64_t items) {
+  const int64_t want = (items + kCombWaves - 1) / kCombWaves;
   return static_cast<uint32_t>(want < (1 << 20) ? want : (1 << 20));
 }
 
@@ -185,10 +185,10 @@ hipError_t launch_combine(const int32_t* pos, const float* w, int32_t k, const u
   const auto* r = reinterpret_cast<const u32x4*>(rows);
   auto* o = reinterpret_cast<u32x4*>(out);
   if (w != nullptr)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(comb_blocks(ntok)), dim3(kCombThreads), 0, st, pos,
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(comb_blocks(ntok * comb_chunks(H / 8))), dim3(kCombThreads), 0, st, pos,
                        w, k, r, layout_rows, H / 8, g0, ntok, o);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(comb_blocks(ntok)), dim3(kCombThreads), 0, st,
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(comb_blocks(ntok * comb_chunks(H / 8))), dim3(kCombThreads), 0, st,
                        pos, w, k, r, layout_rows, H / 8, g0, ntok, o);
   return hipGetLastError();
 }
