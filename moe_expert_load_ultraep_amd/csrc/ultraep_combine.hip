@@ -20,8 +20,6 @@ namespace {
 
 constexpr int kCombThreads = 256;
 constexpr int kCombWaves = kCombThreads / 64;
-constexpr int kRowsInFlight = 4;    // rows of one token loaded together
-constexpr int kChunksInFlight = 2;  // 16-byte column chunks per lane per row
 
 // y[t] = sum_j w[g, j] * rows[pos[g*k + j]] for g = g0 + t (w = 1 when not
 // WEIGHTED).  One wave per (token, 1 KiB column chunk: 64 lanes x one 16-byte
@@ -95,11 +93,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 
 // For each pair n = g*k + j of the tokens: grad_rows[pos[n]] = w[n] * dy[t]
 // (bf16) and grad_w[t*k + j] = <dy[t], rows[pos[n]]> (fp32: each lane sums
-// its columns in order, then the wave sums the lanes in a fixed order).  The
-// rows of a token go in groups of kRowsInFlight: one pass over the columns
-// loads the gradient chunk once for the group's rows, and the group's dot
-// products are reduced together at its end.  The gradient row is re-read per
-// group from L2; expert-output rows are read once, gradient rows written once.
+// its columns in order, then the wave sums the lanes in a fixed order).  One
+// wave per pair: a token's k pairs are neighbouring waves, so its gradient
+// row is read from HBM once and then from L2 (default cache policy), while
+// the expert-output rows are read once and the gradient rows written once
+// (non-temporal).
+constexpr int kChunksInFlight = 2;  // 16-byte column chunks per lane per round
+
 __global__ __launch_bounds__(kCombThreads) void combine_backward_kernel(
     const int32_t* __restrict__ pos, const float* __restrict__ w, int32_t k,
     const u32x4* __restrict__ rows, int64_t layout_rows, int32_t H8, const u32x4* __restrict__ dy,
@@ -108,65 +108,42 @@ __global__ __launch_bounds__(kCombThreads) void combine_backward_kernel(
   const uint32_t rowb = static_cast<uint32_t>(H8) * 16u;
   const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * kCombWaves;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kCombWaves + wv; t < ntok; t += nwaves) {
-    const int64_t n0 = (g0 + t) * k;
-    int32_t pj = -1;
-    float wj = 0.f;
-    if (lane < k) {
-      const int32_t p = pos[n0 + lane];
-      pj = (p >= 0 && p < layout_rows) ? p : -1;
-      wj = w[n0 + lane];
-    }
+  for (int64_t item = static_cast<int64_t>(blockIdx.x) * kCombWaves + wv; item < ntok * k;
+       item += nwaves) {
+    const int64_t t = item / k;
+    const int32_t j = static_cast<int32_t>(item - t * k);
+    const int64_t n = (g0 + t) * k + j;
+    const int32_t p = __builtin_amdgcn_readfirstlane(pos[n]);
+    const bool live = p >= 0 && p < layout_rows;
+    const float wt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int32_t, w[n])));
+    const int64_t row = live ? p : 0;
     const __amdgpu_buffer_rsrc_t gsrc = row_rsrc(dy + t * H8, rowb);
-    for (int j0 = 0; j0 < k; j0 += kRowsInFlight) {
-      __amdgpu_buffer_rsrc_t xsrc[kRowsInFlight], gdst[kRowsInFlight];
-      float wt[kRowsInFlight], dot[kRowsInFlight];
+    const __amdgpu_buffer_rsrc_t xsrc = row_rsrc(rows + row * H8, live ? rowb : 0u);
+    const __amdgpu_buffer_rsrc_t gdst = row_rsrc(grad_rows + row * H8, live ? rowb : 0u);
+    float dot = 0.f;
+    for (int c0 = 0; c0 < H8; c0 += 64 * kChunksInFlight) {
+      u32x4 g[kChunksInFlight], x[kChunksInFlight];
 #pragma unroll
-      for (int r = 0; r < kRowsInFlight; ++r) {
-        const int j = j0 + r;
-        const int32_t p = static_cast<int32_t>(readlane(static_cast<uint32_t>(pj), j < k ? j : 0));
-        const bool live = j < k && p >= 0;
-        const int64_t row = live ? p : 0;
-        xsrc[r] = row_rsrc(rows + row * H8, live ? rowb : 0u);
-        gdst[r] = row_rsrc(grad_rows + row * H8, live ? rowb : 0u);
-        wt[r] = readlane_f(wj, j < k ? j : 0);
-        dot[r] = 0.f;
-      }
-      for (int c0 = 0; c0 < H8; c0 += 64 * kChunksInFlight) {
-        u32x4 g[kChunksInFlight], x[kRowsInFlight][kChunksInFlight];
+      for (int u = 0; u < kChunksInFlight; ++u)
+        g[u] = __builtin_amdgcn_raw_buffer_load_b128(gsrc, (c0 + u * 64 + lane) * 16, 0, 0);
 #pragma unroll
-        for (int u = 0; u < kChunksInFlight; ++u)
-          g[u] = __builtin_amdgcn_raw_buffer_load_b128(gsrc, (c0 + u * 64 + lane) * 16, 0, 0);
+      for (int u = 0; u < kChunksInFlight; ++u)
+        x[u] = __builtin_amdgcn_raw_buffer_load_b128(xsrc, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
 #pragma unroll
-        for (int r = 0; r < kRowsInFlight; ++r)
+      for (int u = 0; u < kChunksInFlight; ++u) {
+        u32x4 d;
 #pragma unroll
-          for (int u = 0; u < kChunksInFlight; ++u)
-            x[r][u] = __builtin_amdgcn_raw_buffer_load_b128(xsrc[r], (c0 + u * 64 + lane) * 16, 0,
-                                                            kNonTemporal);
-#pragma unroll
-        for (int r = 0; r < kRowsInFlight; ++r)
-#pragma unroll
-          for (int u = 0; u < kChunksInFlight; ++u) {
-            u32x4 d;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float glo = bf16_lo(g[u][q]), ghi = bf16_hi(g[u][q]);
-              dot[r] += glo * bf16_lo(x[r][u][q]);
-              dot[r] += ghi * bf16_hi(x[r][u][q]);
-              d[q] = pack_bf16(wt[r] * glo, wt[r] * ghi);
-            }
-            __builtin_amdgcn_raw_buffer_store_b128(d, gdst[r], (c0 + u * 64 + lane) * 16, 0,
-                                                   kNonTemporal);
-          }
-      }
-#pragma unroll
-      for (int r = 0; r < kRowsInFlight; ++r) {
-        const int j = j0 + r;
-        const float sum = wave_sum_f32(dot[r]);
-        const int32_t p = static_cast<int32_t>(readlane(static_cast<uint32_t>(pj), j < k ? j : 0));
-        if (lane == 0 && j < k) grad_w[t * k + j] = p >= 0 ? sum : 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const float glo = bf16_lo(g[u][q]), ghi = bf16_hi(g[u][q]);
+          dot += glo * bf16_lo(x[u][q]);
+          dot += ghi * bf16_hi(x[u][q]);
+          d[q] = pack_bf16(wt * glo, wt * ghi);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(d, gdst, (c0 + u * 64 + lane) * 16, 0, kNonTemporal);
       }
     }
+    const float sum = wave_sum_f32(dot);
+    if (lane == 0) grad_w[t * k + j] = live ? sum : 0.f;
   }
 }
 
@@ -199,7 +176,7 @@ hipError_t launch_combine_backward(const int32_t* pos, const float* w, int32_t k
                                    uint16_t* grad_rows, float* grad_w, hipStream_t st) {
   const int64_t ntok = g1 - g0;
   if (ntok <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_backward_kernel, dim3(comb_blocks(ntok)), dim3(kCombThreads), 0, st, pos,
+  hipLaunchKernelGGL(combine_backward_kernel, dim3(comb_blocks(ntok * k)), dim3(kCombThreads), 0, st, pos,
                      w, k, reinterpret_cast<const u32x4*>(rows), layout_rows, H / 8,
                      reinterpret_cast<const u32x4*>(grad_out), g0, ntok,
                      reinterpret_cast<u32x4*>(grad_rows), grad_w);
