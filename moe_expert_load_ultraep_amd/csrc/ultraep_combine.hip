@@ -4,10 +4,11 @@
 // weighted by its routing probabilities; in the backward pass reroute gathers
 // the gradients of the physical replicas back to the logical experts).
 //
-// All three are HBM-streaming gathers over the dispatch layout: one wave per
-// token, every row of the token addressed through its own buffer resource
-// (size 0 for a dropped pair, so it reads as zeros and its stores vanish),
-// 16-byte accesses, fp32 arithmetic, bf16 results rounded to nearest even.
+// All three are HBM-streaming gathers over the dispatch layout: the combine
+// runs one wave per (token, 1 KiB column chunk), its backward one wave per
+// pair; every row is addressed through its own buffer resource (size 0 for a
+// dropped pair, so it reads as zeros and its stores vanish), with 16-byte
+// accesses, fp32 arithmetic and bf16 results rounded to nearest even.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
