@@ -90,13 +90,13 @@ def run_case(rng, T, k, H, nrows, g0, g1, drop=0.0, weighted=True):
 
 
 @pytest.mark.parametrize("T,k,H,nrows,g0,g1,drop,weighted", [
-    (300, 8, 4096, 2600, 0, 300, 0.0, True),      # several chunk rounds, full range
+    (300, 8, 4096, 2600, 0, 300, 0.0, True),      # eight 1 KiB column chunks a token, full range
     (300, 8, 4096, 2600, 0, 300, 0.0, False),     # unweighted: backward of the dispatch
-    (257, 6, 136, 1600, 13, 250, 0.05, True),     # ragged H (17 chunks), sub-range, dropped pairs
-    (64, 1, 8, 64, 0, 64, 0.0, True),             # k = 1, one chunk per row
-    (40, 64, 64, 2600, 0, 40, 0.02, True),        # k = 64 (16 groups of rows)
+    (257, 6, 136, 1600, 13, 250, 0.05, True),     # ragged H (one partial chunk), sub-range, dropped pairs
+    (64, 1, 8, 64, 0, 64, 0.0, True),             # k = 1, one 16-byte vector per row
+    (40, 64, 64, 2600, 0, 40, 0.02, True),        # k = 64 (eight groups of eight rows)
     (50, 3, 7168, 200, 7, 7, 0.0, True),          # empty range
-    (700, 2, 1000, 1400, 100, 700, 0.0, True),    # H % 512 != 0
+    (700, 2, 1000, 1400, 100, 700, 0.0, True),    # H / 8 % 64 != 0: a partial second chunk
 ])
 def test_combine_cases(T, k, H, nrows, g0, g1, drop, weighted):
     say(f"combine T={T} k={k} H={H} rows={nrows} range=[{g0},{g1}) drop={drop} weighted={weighted}")
