@@ -56,6 +56,7 @@ SHAPES = [
     (256, 64, 2, 64, 4096, 8),       # 61 layers
     (160, 40, 3, 8, 16384, 8),       # topology
     (256, 64, 2, 64, 8192, 8),       # the pages' table shape
+    (24, 6, 2, 3, 2000, 8),          # the GPU block-order test: 12 tiles a layer, ragged
 ]
 
 

@@ -26,6 +26,30 @@ def _ctx(w, **kw):
     return U.ultraep_create(w.E, w.R, w.S, w.D, **kw)
 
 
+# ---------------------------------------------------------- block order ---
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_reroute_block_order_tail_several_layers(mode):
+    """The reroute kernels take their (layer, tile) from the workgroup index
+    in XCD order, and the grid's last (workgroups mod 8) keep their index.
+    Three layers of 12 tiles each (six ranks of two tiles, the second one
+    ragged) make 36 workgroups, 4 past the last group of eight: every layer
+    is compared in full, in each reroute mode, with the layout fused."""
+    E, R, S, D, T, k, L = 24, 6, 2, 3, 2000, 8, 3
+    rng = np.random.default_rng(7100 + mode)
+    idx, wt = [], []
+    for _ in range(L):
+        p = rng.dirichlet(np.full(E, 0.4))
+        keys = np.log(np.maximum(p, 1e-12))[None, :] + rng.gumbel(size=(R * T, E))
+        idx.append(np.argsort(-keys, axis=1)[:, :k].astype(np.int32))
+        wt.append(rng.random((R * T, k), dtype=np.float32))
+    idx, wt = np.stack(idx), np.stack(wt)
+    say(f"block order: E={E} R={R} S={S} D={D} T={T} k={k} L={L} mode={mode}")
+    ctx = U.ultraep_create(E, R, S, D, reroute_mode=mode)
+    got = run_balance(ctx, idx, wt, T, k)
+    for l in range(L):
+        assert_layer_equal(ctx, got, l, idx[l], wt[l], E, R, S, D)
+
+
 # ------------------------------------------------------------------ tiny ---
 def test_tiny_full_path_eight_layers():
     """Tiny workload: 8 independent layers balanced in one batched call,
